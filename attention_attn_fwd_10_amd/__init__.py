@@ -1,0 +1,208 @@
+"""Python binding of the MI355X fused attention forward library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libattn_fwd.so``.  torch supplies device memory and the stream.
+The entry points mirror the C ABI in ``include/attn.h``:
+
+* ``fwd``            -> ``attn_fwd``            (bf16 / fp16, optional causal mask)
+* ``fp8_quantize``   -> ``attn_fp8_quantize``   (rotation + e4m3 block quantisation)
+* ``fwd_fp8``        -> ``attn_fwd_fp8``        (e4m3 forward with per-block scales)
+* ``fwd_varlen``     -> ``attn_fwd_varlen``     (packed sequences, optional paged KV)
+
+Tensors use the [batch, seq, heads, head_dim] layout (varlen: [tokens, heads,
+head_dim]).  If the library has not been built, importing this package fails:
+there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["fwd", "fp8_quantize", "fwd_fp8", "fwd_varlen", "lib_path", "AttnError",
+           "ATTN_BF16", "ATTN_FP16"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libattn_fwd.so")
+
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
+ATTN_BF16, ATTN_FP16 = 0, 1
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with `python -m attention_attn_fwd_10_amd.build` "
+            "(there is no fallback path)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    I64P = ctypes.POINTER(ctypes.c_int64)
+    lib.attn_fwd.argtypes = [I, P, I64P, P, I64P, P, I64P, P, I64P, P, I, I, I, I, I, F, I, P]
+    lib.attn_fwd.restype = I
+    lib.attn_fp8_quantize.argtypes = [P, I64P, P, P, I, I, I, I, I, P, P]
+    lib.attn_fp8_quantize.restype = I
+    lib.attn_fwd_fp8.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, I, F, I, P]
+    lib.attn_fwd_fp8.restype = I
+    lib.attn_fwd_varlen.argtypes = [I, P, P, P, P, P, P, I, I, P, P, I, I, I, I, I, I, F, I, P]
+    lib.attn_fwd_varlen.restype = I
+    lib.attn_status_string.argtypes = [I]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        msg = _lib.attn_last_error().decode() or _lib.attn_status_string(status).decode()
+        raise AttnError(status, msg)
+
+
+def _strides(t):
+    """[B, S, H, D] element strides as the C ABI's {batch, seq, head} triple."""
+    if t.stride(3) != 1:
+        raise ValueError("head_dim must be the contiguous dimension")
+    arr = (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+    return arr
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dtype_code(dt):
+    import torch
+    if dt == torch.bfloat16:
+        return ATTN_BF16
+    if dt == torch.float16:
+        return ATTN_FP16
+    raise TypeError(f"unsupported dtype {dt}: bf16 or fp16 expected")
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must live on the GPU")
+
+
+def fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None, return_lse=True, stream=None):
+    """Fused attention forward.  q [B, Sq, H, D], k/v [B, Sk, H, D] (bf16 or
+    fp16, head_dim contiguous).  Returns (o [B, Sq, H, D], lse [B, H, Sq] fp32)."""
+    import torch
+    _require_cuda(q, k, v, out, lse)
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    if k.shape != (B, Sk, H, D) or v.shape != (B, Sk, H, D):
+        raise ValueError("k and v must be [B, Sk, H, D] matching q")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share a dtype")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format) if not q.is_contiguous() \
+            else torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (B, H, Sq)):
+        raise ValueError("lse must be contiguous float32 [B, H, Sq]")
+    _check(_lib.attn_fwd(_dtype_code(q.dtype), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+                         _ptr(out), _strides(out), _ptr(lse), B, H, Sq, Sk, D, scale, int(bool(causal)),
+                         _stream(stream)))
+    return out, lse
+
+
+def fp8_quantize(x, block_rows=128, signs=None, out=None, scales=None, stream=None):
+    """Quantise a bf16 [B, S, H, D] tensor to e4m3 (uint8 codes) with one scale
+    per (b, h, 128-row block) or per tensor (block_rows=0), optionally after the
+    random-sign Hadamard rotation given by ``signs`` (int8 [D] of +-1)."""
+    import torch
+    _require_cuda(x, signs, out, scales)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("fp8_quantize expects bf16 input")
+    B, S, H, D = x.shape
+    if out is None:
+        out = torch.empty((B, S, H, D), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        shape = (B, H, (S + 127) // 128) if block_rows else (1,)
+        scales = torch.empty(shape, dtype=torch.float32, device=x.device)
+    if signs is not None and (signs.dtype != torch.int8 or signs.numel() != D):
+        raise ValueError("signs must be int8 [D]")
+    _check(_lib.attn_fp8_quantize(_ptr(x), _strides(x), _ptr(out), _ptr(scales), B, H, S, D, int(block_rows),
+                                  _ptr(signs), _stream(stream)))
+    return out, scales
+
+
+def fwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, block_rows=128, softmax_scale=None, causal=False,
+            out=None, lse=None, stream=None):
+    """8-bit fused forward on e4m3 codes (uint8 [B, S, H, D], contiguous) and
+    their scales.  Returns (o bf16 [B, Sq, H, D], lse fp32 [B, H, Sq])."""
+    import torch
+    _require_cuda(q8, q_scale, k8, k_scale, v8, v_scale, out, lse)
+    B, Sq, H, D = q8.shape
+    Sk = k8.shape[1]
+    for t in (q8, k8, v8):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("q8, k8, v8 must be contiguous uint8 e4m3 codes")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, Sq, H, D), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q8.device)
+    _check(_lib.attn_fwd_fp8(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v8), _ptr(v_scale),
+                             int(block_rows), _ptr(out), _ptr(lse), B, H, Sq, Sk, D, scale, int(bool(causal)),
+                             _stream(stream)))
+    return out, lse
+
+
+def fwd_varlen(q, cu_seqlens_q, k, v, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale=None,
+               causal=False, block_table=None, page_size=0, out=None, lse=None, stream=None):
+    """Packed variable-length forward.  q [total_q, H, D]; cu_seqlens int32
+    [B+1] on the device.  Without a block table k, v are packed [total_k, H, D];
+    with one they are paged caches [num_pages, page_size, H, D].  Returns
+    (o [total_q, H, D], lse fp32 [H, total_q])."""
+    import torch
+    _require_cuda(q, cu_seqlens_q, k, v, cu_seqlens_k, block_table, out, lse)
+    total_q, H, D = q.shape
+    B = cu_seqlens_q.numel() - 1
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("varlen tensors must be contiguous")
+    for t in (cu_seqlens_q, cu_seqlens_k):
+        if t.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+    max_pages = 0
+    if block_table is not None:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
+            raise ValueError("block_table must be contiguous int32 [B, max_pages]")
+        max_pages = block_table.shape[1]
+        if k.shape[1] != page_size:
+            raise ValueError("paged k/v must be [num_pages, page_size, H, D]")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    _check(_lib.attn_fwd_varlen(_dtype_code(q.dtype), _ptr(q), _ptr(cu_seqlens_q), _ptr(k), _ptr(v),
+                                _ptr(cu_seqlens_k), _ptr(block_table), max_pages, int(page_size), _ptr(out),
+                                _ptr(lse), B, H, D, total_q, int(max_seqlen_q), int(max_seqlen_k), scale,
+                                int(bool(causal)), _stream(stream)))
+    return out, lse

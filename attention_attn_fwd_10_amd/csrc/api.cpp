@@ -1,0 +1,241 @@
+// C ABI of the attention forward library: host-side argument validation and
+// dispatch to the kernel instantiations.  Nothing here touches the device
+// before every argument has been checked, so an error return means that no
+// work was queued and nothing was written.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/attn.h"
+#include "common.hpp"
+
+namespace attn {
+template <int D, int DT, bool CAUSAL, int MODE>
+hipError_t launch_fwd16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fp8_quantize(const QuantArgs& a, int D, hipStream_t s);
+hipError_t launch_fwd_fp8(const Fp8Args& a, int D, bool causal, hipStream_t s);
+}  // namespace attn
+
+namespace {
+
+thread_local std::string g_last_error;
+
+attn_status_t fail(attn_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+attn_status_t fail(attn_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+attn_status_t ok() {
+  g_last_error.clear();
+  return ATTN_OK;
+}
+
+attn_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+attn_status_t check_strides(const char* name, const int64_t* s) {
+  if (s == nullptr) return fail(ATTN_ERR_INVALID, "%s_strides is NULL", name);
+  for (int i = 0; i < 3; ++i) {
+    if (s[i] < 0) return fail(ATTN_ERR_INVALID, "%s_strides[%d] = %lld is negative", name, i, (long long)s[i]);
+    if (s[i] % 8 != 0)
+      return fail(ATTN_ERR_INVALID, "%s_strides[%d] = %lld is not a multiple of 8 elements", name, i,
+                  (long long)s[i]);
+  }
+  return ATTN_OK;
+}
+
+attn_status_t check_scale(float scale) {
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(ATTN_ERR_INVALID, "softmax_scale must be finite and > 0 (got %g)", (double)scale);
+  return ATTN_OK;
+}
+
+attn_status_t check_head_dim(int D) {
+  if (D <= 0) return fail(ATTN_ERR_INVALID, "head_dim %d must be positive", D);
+  if (D != 64 && D != 128 && D != 256)
+    return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d is not one of 64, 128, 256", D);
+  return ATTN_OK;
+}
+
+template <int D, int DT>
+hipError_t dispatch_causal_mode(const attn::FwdArgs& a, bool causal, int mode, hipStream_t s) {
+  using namespace attn;
+  if (mode == kDense)
+    return causal ? launch_fwd16<D, DT, true, kDense>(a, s) : launch_fwd16<D, DT, false, kDense>(a, s);
+  if (mode == kVarlen)
+    return causal ? launch_fwd16<D, DT, true, kVarlen>(a, s) : launch_fwd16<D, DT, false, kVarlen>(a, s);
+  return causal ? launch_fwd16<D, DT, true, kPaged>(a, s) : launch_fwd16<D, DT, false, kPaged>(a, s);
+}
+
+hipError_t dispatch_fwd16(const attn::FwdArgs& a, int D, int dtype, bool causal, int mode, hipStream_t s) {
+  if (dtype == ATTN_BF16) {
+    if (D == 64) return dispatch_causal_mode<64, attn::kBF16>(a, causal, mode, s);
+    if (D == 128) return dispatch_causal_mode<128, attn::kBF16>(a, causal, mode, s);
+    return dispatch_causal_mode<256, attn::kBF16>(a, causal, mode, s);
+  }
+  if (D == 64) return dispatch_causal_mode<64, attn::kFP16>(a, causal, mode, s);
+  if (D == 128) return dispatch_causal_mode<128, attn::kFP16>(a, causal, mode, s);
+  return dispatch_causal_mode<256, attn::kFP16>(a, causal, mode, s);
+}
+
+constexpr int kBR = 128;  // query rows per workgroup of every forward kernel
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID: return "ATTN_ERR_INVALID";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+    default: return "ATTN_STATUS_UNKNOWN";
+  }
+}
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+attn_status_t attn_fwd(int dtype, const void* q, const int64_t q_strides[3], const void* k,
+                       const int64_t k_strides[3], const void* v, const int64_t v_strides[3], void* o,
+                       const int64_t o_strides[3], float* lse, int B, int H, int Sq, int Sk, int D,
+                       float softmax_scale, int causal, void* stream) {
+  attn_status_t st;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return fail(ATTN_ERR_INVALID, "dtype %d is not bf16/fp16", dtype);
+  if (B < 0 || H < 0 || Sq < 0 || Sk < 0) return fail(ATTN_ERR_INVALID, "negative size (B=%d H=%d Sq=%d Sk=%d)", B, H, Sq, Sk);
+  if ((st = check_head_dim(D)) != ATTN_OK) return st;
+  if ((st = check_scale(softmax_scale)) != ATTN_OK) return st;
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID, "causal must be 0 or 1 (got %d)", causal);
+  if ((st = check_strides("q", q_strides)) != ATTN_OK) return st;
+  if ((st = check_strides("k", k_strides)) != ATTN_OK) return st;
+  if ((st = check_strides("v", v_strides)) != ATTN_OK) return st;
+  if ((st = check_strides("o", o_strides)) != ATTN_OK) return st;
+  if (B == 0 || H == 0 || Sq == 0) return ok();
+  if (q == nullptr || o == nullptr) return fail(ATTN_ERR_INVALID, "q or o is NULL");
+  if (Sk > 0 && (k == nullptr || v == nullptr)) return fail(ATTN_ERR_INVALID, "k or v is NULL");
+  if (!aligned16(q) || !aligned16(o) || !aligned16(k) || !aligned16(v) || !aligned16(lse))
+    return fail(ATTN_ERR_INVALID, "q, k, v, o and lse must be 16-byte aligned");
+  const int64_t n_qblk = (Sq + kBR - 1) / kBR;
+  if ((int64_t)B * H * n_qblk > INT32_MAX) return fail(ATTN_ERR_INVALID, "problem too large for one launch");
+
+  attn::FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.q_sb = q_strides[0]; a.q_ss = q_strides[1]; a.q_sh = q_strides[2];
+  a.k_sb = k_strides[0]; a.k_ss = k_strides[1]; a.k_sh = k_strides[2];
+  a.v_sb = v_strides[0]; a.v_ss = v_strides[1]; a.v_sh = v_strides[2];
+  a.o_sb = o_strides[0]; a.o_ss = o_strides[1]; a.o_sh = o_strides[2];
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk;
+  a.scale_log2 = softmax_scale * attn::kLog2e;
+  a.n_qblk = (int)n_qblk;
+  return hip_status(dispatch_fwd16(a, D, dtype, causal != 0, attn::kDense, (hipStream_t)stream), "attn_fwd launch");
+}
+
+attn_status_t attn_fwd_varlen(int dtype, const void* q, const int32_t* cu_seqlens_q, const void* k, const void* v,
+                              const int32_t* cu_seqlens_k, const int32_t* block_table, int max_pages_per_seq,
+                              int page_size, void* o, float* lse, int B, int H, int D, int total_q,
+                              int max_seqlen_q, int max_seqlen_k, float softmax_scale, int causal, void* stream) {
+  attn_status_t st;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return fail(ATTN_ERR_INVALID, "dtype %d is not bf16/fp16", dtype);
+  if (B < 0 || H < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(ATTN_ERR_INVALID, "negative size");
+  if ((st = check_head_dim(D)) != ATTN_OK) return st;
+  if ((st = check_scale(softmax_scale)) != ATTN_OK) return st;
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID, "causal must be 0 or 1 (got %d)", causal);
+  int page_shift = 0;
+  if (block_table != nullptr) {
+    if (page_size < 16 || (page_size & (page_size - 1)) != 0)
+      return fail(ATTN_ERR_INVALID, "page_size %d must be a power of two >= 16", page_size);
+    if (max_pages_per_seq < 1) return fail(ATTN_ERR_INVALID, "max_pages_per_seq must be >= 1");
+    if ((int64_t)max_pages_per_seq * page_size < max_seqlen_k)
+      return fail(ATTN_ERR_INVALID, "max_pages_per_seq * page_size < max_seqlen_k");
+    while ((1 << page_shift) < page_size) ++page_shift;
+  }
+  if (B == 0 || H == 0 || total_q == 0 || max_seqlen_q == 0) return ok();
+  if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return fail(ATTN_ERR_INVALID, "cu_seqlens is NULL");
+  if (q == nullptr || o == nullptr) return fail(ATTN_ERR_INVALID, "q or o is NULL");
+  if (max_seqlen_k > 0 && (k == nullptr || v == nullptr)) return fail(ATTN_ERR_INVALID, "k or v is NULL");
+  if (!aligned16(q) || !aligned16(o) || !aligned16(k) || !aligned16(v) || !aligned16(lse))
+    return fail(ATTN_ERR_INVALID, "q, k, v, o and lse must be 16-byte aligned");
+  const int64_t n_qblk = (max_seqlen_q + kBR - 1) / kBR;
+  if ((int64_t)B * H * n_qblk > INT32_MAX) return fail(ATTN_ERR_INVALID, "problem too large for one launch");
+
+  attn::FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  const int64_t tok = (int64_t)H * D;  // packed [tokens, H, D]
+  a.q_ss = tok; a.q_sh = D;
+  a.k_ss = tok; a.k_sh = D;
+  a.v_ss = tok; a.v_sh = D;
+  a.o_ss = tok; a.o_sh = D;
+  a.B = B; a.H = H; a.Sq = max_seqlen_q; a.Sk = max_seqlen_k;
+  a.scale_log2 = softmax_scale * attn::kLog2e;
+  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+  a.block_table = block_table; a.max_pages = max_pages_per_seq; a.page_shift = page_shift;
+  a.n_qblk = (int)n_qblk;
+  a.total_q = total_q;
+  const int mode = block_table != nullptr ? attn::kPaged : attn::kVarlen;
+  return hip_status(dispatch_fwd16(a, D, dtype, causal != 0, mode, (hipStream_t)stream), "attn_fwd_varlen launch");
+}
+
+attn_status_t attn_fp8_quantize(const void* x, const int64_t x_strides[3], uint8_t* x8, float* scales, int B, int H,
+                                int S, int D, int block_rows, const int8_t* signs, void* stream) {
+  attn_status_t st;
+  if (B < 0 || H < 0 || S < 0) return fail(ATTN_ERR_INVALID, "negative size");
+  if ((st = check_head_dim(D)) != ATTN_OK) return st;
+  if (block_rows != 0 && block_rows != 128) return fail(ATTN_ERR_INVALID, "block_rows must be 128 or 0 (got %d)", block_rows);
+  if ((st = check_strides("x", x_strides)) != ATTN_OK) return st;
+  if (B == 0 || H == 0 || S == 0) return ok();
+  if (x == nullptr || x8 == nullptr || scales == nullptr) return fail(ATTN_ERR_INVALID, "x, x8 or scales is NULL");
+  if (!aligned16(x) || !aligned16(x8)) return fail(ATTN_ERR_INVALID, "x and x8 must be 16-byte aligned");
+  if ((int64_t)B * H * ((S + 127) / 128) > INT32_MAX) return fail(ATTN_ERR_INVALID, "problem too large");
+  attn::QuantArgs a{};
+  a.x = (const uint16_t*)x;
+  a.x_sb = x_strides[0]; a.x_ss = x_strides[1]; a.x_sh = x_strides[2];
+  a.x8 = x8; a.scales = scales; a.signs = signs;
+  a.B = B; a.H = H; a.S = S; a.block_rows = block_rows;
+  return hip_status(attn::launch_fp8_quantize(a, D, (hipStream_t)stream), "attn_fp8_quantize launch");
+}
+
+attn_status_t attn_fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
+                           const uint8_t* v8, const float* v_scale, int block_rows, void* o, float* lse, int B,
+                           int H, int Sq, int Sk, int D, float softmax_scale, int causal, void* stream) {
+  attn_status_t st;
+  if (B < 0 || H < 0 || Sq < 0 || Sk < 0) return fail(ATTN_ERR_INVALID, "negative size");
+  if (D <= 0) return fail(ATTN_ERR_INVALID, "head_dim %d must be positive", D);
+  if (D != 128) return fail(ATTN_ERR_UNSUPPORTED, "the 8-bit path supports head_dim 128 only (got %d)", D);
+  if ((st = check_scale(softmax_scale)) != ATTN_OK) return st;
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID, "causal must be 0 or 1 (got %d)", causal);
+  if (block_rows != 0 && block_rows != 128) return fail(ATTN_ERR_INVALID, "block_rows must be 128 or 0 (got %d)", block_rows);
+  if (B == 0 || H == 0 || Sq == 0) return ok();
+  if (q8 == nullptr || q_scale == nullptr || o == nullptr) return fail(ATTN_ERR_INVALID, "q8, q_scale or o is NULL");
+  if (Sk > 0 && (k8 == nullptr || v8 == nullptr || k_scale == nullptr || v_scale == nullptr))
+    return fail(ATTN_ERR_INVALID, "k8, v8 or their scales are NULL");
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) || !aligned16(lse))
+    return fail(ATTN_ERR_INVALID, "q8, k8, v8, o and lse must be 16-byte aligned");
+  const int64_t n_qblk = (Sq + kBR - 1) / kBR;
+  if ((int64_t)B * H * n_qblk > INT32_MAX) return fail(ATTN_ERR_INVALID, "problem too large for one launch");
+  attn::Fp8Args a{};
+  a.q = q8; a.k = k8; a.v = v8; a.qs = q_scale; a.ks = k_scale; a.vs = v_scale;
+  a.o = o; a.lse = lse;
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk;
+  a.block_rows = block_rows;
+  a.scale_log2 = softmax_scale * attn::kLog2e;
+  a.n_qblk = (int)n_qblk;
+  return hip_status(attn::launch_fwd_fp8(a, D, causal != 0, (hipStream_t)stream), "attn_fwd_fp8 launch");
+}
+
+}  // extern "C"

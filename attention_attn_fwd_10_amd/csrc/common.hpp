@@ -1,0 +1,132 @@
+// Device helpers shared by the gfx950 attention kernels: vector types, MFMA
+// wrappers, conversions, the work-item remap and launch-side argument structs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// dtype tags
+constexpr int kBF16 = 0;
+constexpr int kFP16 = 1;
+
+// ---------------------------------------------------------------------------
+// MFMA: D(32x32, fp32) += A(32x16) * B(16x32); A/B hold 8 16-bit values/lane.
+// Lane l supplies row (l % 32) of A / column (l % 32) of B and the k-slice
+// selected by l / 32; the same (lane, element) -> k map applies to A and B.
+// The accumulator: lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4 and
+// column l % 32.
+// ---------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (DT == kBF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+// 8-bit: D(32x32) += A(32x64) * B(64x32), 32 e4m3 values per lane (both operands e4m3).
+__device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  // format selectors 0 = e4m3 for A and B; scale exponents 127 = x1.0
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// two floats -> packed 16-bit pair (round to nearest even), low half = a
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (DT == kBF16) {
+    __bf16 x = (__bf16)a, y = (__bf16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  } else {
+    _Float16 x = (_Float16)a, y = (_Float16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Swap bits 2 and 3 of a row index inside a 32-row MFMA tile.  Storing key k
+// (or head-dim row d) at LDS row swz(k) and reading row m = lane % 32 makes
+// accumulator register r of lane half hh correspond to index
+// 16*(r/8) + 8*hh + r%8, i.e. runs of 8 consecutive keys (or d) per lane.
+__device__ __forceinline__ int swz23(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs.  Map the hardware
+// block id to a logical tile id so that consecutive logical tiles (the q-blocks
+// of one head) run on the same XCD and share its L2.
+__device__ __forceinline__ int xcd_remap(int p, int n) {
+  constexpr int kXcd = 8;
+  const int per = n / kXcd, rem = n % kXcd;
+  const int xcd = p % kXcd, slot = p / kXcd;
+  return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
+// ---------------------------------------------------------------------------
+// launch-side argument blocks (plain data, passed by value)
+// ---------------------------------------------------------------------------
+enum KvMode { kDense = 0, kVarlen = 1, kPaged = 2 };
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int B, H, Sq, Sk;          // dense sizes; varlen: B = #sequences, Sq/Sk = max lengths
+  float scale_log2;          // softmax_scale * log2(e)
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* block_table;
+  int max_pages;
+  int page_shift;            // log2(page_size)
+  int n_qblk;                // query blocks per (b, h)
+  int total_q;               // varlen: rows of the packed q (LSE row length)
+};
+
+struct Fp8Args {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const float* qs;
+  const float* ks;
+  const float* vs;
+  void* o;
+  float* lse;
+  int B, H, Sq, Sk;
+  int block_rows;            // 128 or 0 (per-tensor)
+  float scale_log2;
+  int n_qblk;
+};
+
+struct QuantArgs {
+  const uint16_t* x;
+  int64_t x_sb, x_ss, x_sh;
+  uint8_t* x8;
+  float* scales;
+  const int8_t* signs;
+  int B, H, S;
+  int block_rows;
+};
+
+}  // namespace attn

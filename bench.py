@@ -1,0 +1,196 @@
+#!/usr/bin/env python3
+"""Throughput of the fused attention forward on one MI355X.
+
+One step = one pass of the hot path over one batch of synthetic input: a single
+``attn_fwd`` launch (bf16, non-causal) on the FlashAttention-3 ablation shape
+(batch 4, seq 8448, 16 heads, head_dim 128).  Inputs are seeded N(0,1) bf16,
+resident in HBM before the timed region.  The line also carries the 8-bit path
+(quantised inputs, attention kernel alone) on batch 4 / 16 heads / seq 8192 /
+d128 when that path is available, the roofline position of the timed kernel and
+the float64 CPU oracle timed on a bounded sample of the same workload.
+
+Prints ONE JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--causal", action="store_true", help="time the causal variant instead")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-fp8", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--sweep", action="store_true", help="also time the 16384-token seq sweep (extra output)")
+    return p.parse_args()
+
+
+def time_launches(fn, steps, warmup):
+    """Average duration of ``fn`` (one launch on torch's current stream) with HIP
+    events bracketing exactly ``steps`` launches."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms
+
+
+def cpu_baseline(w, q, k, v, target_s):
+    """The float64 oracle (three-pass definition) on whole heads of the same
+    workload until about ``target_s`` seconds of CPU work have run."""
+    from oracle import attention as OA
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    flops_head = 4.0 * w.seq_q * w.seq_k * w.head_dim / (2 if w.causal else 1)
+    t0 = time.perf_counter()
+    n = 0
+    pairs = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    while n < len(pairs):
+        b, h = pairs[n]
+        OA.naive_head(q[b, :, h], k[b, :, h], v[b, :, h], w.scale, w.causal)
+        n += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": n * flops_head / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} of {len(pairs)} (batch, head) pairs of {w.name}, all rows, float64 numpy "
+                      f"three-pass, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import attention_attn_fwd_10_amd as A
+    import workloads as W
+
+    w = W.WORKLOADS["ablation"]
+    if args.causal:
+        w = W.Workload(w.name + "_causal", w.batch, w.heads, w.seq_q, w.seq_k, w.head_dim, True, w.seed)
+    qs, ks = w.shapes()
+    qh, kh, vh = W.qkv_normal(w.seed, qs, ks)
+    dev = "cuda"
+    q = torch.from_numpy(qh).to(torch.bfloat16).to(dev)
+    k = torch.from_numpy(kh).to(torch.bfloat16).to(dev)
+    v = torch.from_numpy(vh).to(torch.bfloat16).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.heads, w.seq_q), dtype=torch.float32, device=dev)
+    print(f"[bench] inputs ready: {w.name}", file=sys.stderr, flush=True)
+
+    ms = time_launches(lambda: A.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse), args.steps, args.warmup)
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    algo_bytes = 2 * (2 * w.batch * w.seq_q * w.heads * w.head_dim + 2 * w.batch * w.seq_k * w.heads * w.head_dim) \
+        + 4 * w.batch * w.heads * w.seq_q
+    print(f"[bench] bf16 fwd {ms:.3f} ms  {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    result = {
+        "metric": "attn fwd TFLOPs/s at d128 seq 8k (bf16, fp8) + % of MI355X MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) rounded to bf16, device-resident",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_q": w.seq_q, "seq_k": w.seq_k,
+                   "head_dim": w.head_dim, "causal": w.causal, "flops_per_step": w.flops,
+                   "flop_convention": "4*B*H*Sq*Sk*D, halved for causal"},
+        "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "fwd16_kernel<128, bf16, non-causal, dense>",
+                     "algorithmic_bytes": algo_bytes},
+    }
+
+    if not args.no_fp8:
+        result["fp8"] = bench_fp8(A, W, args)
+
+    if args.sweep:
+        result["sweep"] = bench_sweep(A, W, args)
+
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, qh, kh, vh, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def bench_fp8(A, W, args):
+    import torch
+    w = W.WORKLOADS["fp8"]
+    qs, _ = w.shapes()
+    qh, kh, vh = W.qkv_outlier(w.seed, qs)
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in (qh, kh, vh))
+    signs = torch.from_numpy(W.random_signs(4, w.head_dim)).cuda()
+    try:
+        q8, qsc = A.fp8_quantize(q, 128, signs)
+        k8, ksc = A.fp8_quantize(k, 128, signs)
+        v8, vsc = A.fp8_quantize(v, 128, None)
+        o = torch.empty((w.batch, w.seq_q, w.heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((w.batch, w.heads, w.seq_q), dtype=torch.float32, device="cuda")
+        ms = time_launches(lambda: A.fwd_fp8(q8, qsc, k8, ksc, v8, vsc, 128, w.scale, False, out=o, lse=lse),
+                           args.steps, args.warmup)
+        ms_q = time_launches(lambda: A.fp8_quantize(q, 128, signs, out=q8, scales=qsc), args.steps, 2)
+    except A.AttnError as e:
+        return {"available": False, "reason": str(e)}
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    q_bytes = 2 * q.numel() + q.numel() + 4 * qsc.numel()
+    print(f"[bench] fp8 fwd {ms:.3f} ms  {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    return {"available": True, "workload": w.name, "ms": round(ms, 4), "tflops": round(tflops, 2),
+            "pct_of_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2), "peak": PEAK_FP8_TFLOPS,
+            "quantize_ms_per_tensor": round(ms_q, 4),
+            "quantize_gbs": round(q_bytes / (ms_q * 1e-3) / 1e9, 1),
+            "end_to_end_ms": round(ms + 3 * ms_q, 4)}
+
+
+def bench_sweep(A, W, args):
+    import torch
+    out = []
+    for w in W.seq_sweep_points():
+        qs, ks = w.shapes()
+        g = torch.Generator(device="cuda").manual_seed(w.seed)
+        q, k, v = (torch.randn(qs, generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+        ms = time_launches(lambda: A.fwd(q, k, v, w.scale, w.causal), max(3, args.steps // 4), 2)
+        tf = w.flops / (ms * 1e-3) / 1e12
+        byts = 4 * q.numel() * 2 + 4 * w.batch * w.heads * w.seq_q
+        out.append({"workload": w.name, "ms": round(ms, 4), "tflops": round(tf, 1),
+                    "gbs": round(byts / (ms * 1e-3) / 1e9, 1)})
+        print(f"[bench] {w.name}: {ms:.3f} ms {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    return out
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+/*
+ * attn.h — C ABI of the fused scaled-dot-product attention forward pass on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (the "Fused attention kernel" page, Overview and
+ * Implementation sketch): for every batch b, head h and query row i,
+ *
+ *     s_ij   = softmax_scale * <q_i, k_j>            for keys j in A_i
+ *     O_i    = sum_j exp(s_ij) v_j / sum_j exp(s_ij)
+ *     LSE_i  = ln sum_j exp(s_ij)
+ *
+ * one key block at a time with a running row maximum and row sum, so that the
+ * score and probability matrices never reach device memory.  A_i is every key
+ * of the sequence, intersected with {j <= i + Lk - Lq} when causal (masking is
+ * aligned to the bottom-right corner; identical to j <= i when Lq == Lk).  A
+ * row whose A_i is empty gets O_i = 0 and LSE_i = -inf.
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *    library allocates nothing, keeps no per-call state and is safe to call
+ *    from several host threads.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls are asynchronous on that stream; nothing inside the library
+ *    synchronises.  The caller keeps every buffer alive until the stream has
+ *    run the work.
+ *  - Element strides are given in ELEMENTS, as int64 triples
+ *    {batch, seq, head}; the head_dim stride is always 1.
+ *  - Arguments are validated on the host before anything is launched: on any
+ *    error nothing is written.  Sizes of zero (batch, heads or sequence) are a
+ *    no-op returning ATTN_OK.  Device-resident index arrays (cu_seqlens,
+ *    block tables) are trusted: they must satisfy the stated invariants.
+ *  - Accumulation is float32; O is rounded to nearest-even into its storage
+ *    type; LSE is float32 in natural-log units.
+ */
+#ifndef ATTN_FWD_MI355X_H
+#define ATTN_FWD_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID = 1,      /* a null pointer, a negative size, a bad stride, a non-finite scale ... */
+    ATTN_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement (e.g. head_dim 96) */
+    ATTN_ERR_HIP = 3           /* the HIP runtime refused a launch */
+} attn_status_t;
+
+typedef enum {
+    ATTN_BF16 = 0,
+    ATTN_FP16 = 1
+} attn_dtype_t;
+
+/*
+ * attn_fwd — 16-bit fused forward.
+ * ("Fused attention kernel" page: Overview, Implementation sketch; the
+ * FlashAttention-3 summary page: FP16 forward.)
+ *
+ * q: [B, Sq, H, D], k and v: [B, Sk, H, D], o: [B, Sq, H, D], all of `dtype`,
+ * addressed as base + b*s[0] + i*s[1] + h*s[2] + d with s the stride triple.
+ * lse: float32 [B, H, Sq] contiguous, or NULL to skip it.
+ * D must be 64, 128 or 256 (ATTN_ERR_UNSUPPORTED otherwise); strides must be
+ * multiples of 8 elements and pointers 16-byte aligned.
+ * softmax_scale must be finite and > 0 (1/sqrt(D) is the usual choice).
+ * causal: 0 or 1.
+ */
+attn_status_t attn_fwd(int dtype,
+                       const void* q, const int64_t q_strides[3],
+                       const void* k, const int64_t k_strides[3],
+                       const void* v, const int64_t v_strides[3],
+                       void* o, const int64_t o_strides[3],
+                       float* lse,
+                       int B, int H, int Sq, int Sk, int D,
+                       float softmax_scale, int causal, void* stream);
+
+/*
+ * attn_fp8_quantize — the 8-bit prologue for one tensor.
+ * ("Fused attention kernel" page, section "8-bit forward pass": e4m3 format,
+ * block quantisation, incoherent processing with a random-sign Hadamard
+ * rotation.)
+ *
+ * x: bf16 [B, S, H, D] with stride triple x_strides.
+ * signs: NULL, or int8 [D] of +-1 on the device: then every row is first
+ *   rotated, x' = (x * signs) H_D / sqrt(D) with H_D the Sylvester Hadamard
+ *   matrix (computed in float32 as a fast Walsh-Hadamard transform).
+ * block_rows: 128 -> one scale per (b, h, block of 128 consecutive rows),
+ *   scales float32 [B, H, ceil(S/128)];  0 -> one scale for the whole tensor,
+ *   scales float32 [1].
+ * Each scale is amax / 448 in float32 (1 for an all-zero block); each code is
+ * e4m3fn(x' / scale) rounded to nearest-even and saturated to +-448.
+ * x8: uint8 e4m3fn (OCP E4M3FN encoding) [B, S, H, D], contiguous.
+ * Per-tensor mode uses `scales[0]` as its reduction cell; it is overwritten.
+ */
+attn_status_t attn_fp8_quantize(const void* x, const int64_t x_strides[3],
+                                uint8_t* x8, float* scales,
+                                int B, int H, int S, int D,
+                                int block_rows, const int8_t* signs, void* stream);
+
+/*
+ * attn_fwd_fp8 — 8-bit fused forward on quantised inputs.
+ * ("Fused attention kernel" page, section "8-bit forward pass": both GEMMs in
+ * e4m3, V tiles transposed on chip rather than in a global pass, per-block
+ * scales.)
+ *
+ * q8: e4m3 [B, Sq, H, D] and k8, v8: e4m3 [B, Sk, H, D], contiguous, as
+ * written by attn_fp8_quantize (with the same `signs` for q and k, none for v).
+ * q_scale, k_scale, v_scale: float32, [B, H, ceil(S/128)] when block_rows is
+ * 128, [1] when block_rows is 0.  The attention probabilities are also
+ * rounded to e4m3 for the second GEMM.
+ * o: bf16 [B, Sq, H, D] contiguous; lse: float32 [B, H, Sq] or NULL.
+ * D must be 128.
+ */
+attn_status_t attn_fwd_fp8(const uint8_t* q8, const float* q_scale,
+                           const uint8_t* k8, const float* k_scale,
+                           const uint8_t* v8, const float* v_scale,
+                           int block_rows,
+                           void* o, float* lse,
+                           int B, int H, int Sq, int Sk, int D,
+                           float softmax_scale, int causal, void* stream);
+
+/*
+ * attn_fwd_varlen — packed variable-length batch, optionally with a paged KV
+ * cache.  (The StreamHPC case study lists Paged Attention and Varlen Attention
+ * among the features of its fused kernel.)
+ *
+ * q, o: [total_q, H, D] contiguous of `dtype`; cu_seqlens_q: int32 [B+1]
+ * prefix sums, cu_seqlens_q[0] = 0, non-decreasing; sequence b owns query rows
+ * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and has Lk[b] = cu_seqlens_k[b+1] -
+ * cu_seqlens_k[b] keys.
+ * block_table == NULL: k, v are packed [total_k, H, D] contiguous, sequence b
+ *   owning rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1.
+ * block_table != NULL: k, v are paged caches [num_pages, page_size, H, D]
+ *   contiguous; key t of sequence b lives in page
+ *   block_table[b * max_pages_per_seq + t / page_size] at slot t % page_size.
+ *   page_size must be a power of two >= 16.  Only the entries a sequence needs
+ *   are read, and slots past Lk[b] in its last page are never read.
+ * lse: float32 [H, total_q] or NULL, total_q = cu_seqlens_q[B] (the caller
+ * states it; it is the row count of q and o).  max_seqlen_q / max_seqlen_k
+ * bound every sequence's lengths.
+ */
+attn_status_t attn_fwd_varlen(int dtype,
+                              const void* q, const int32_t* cu_seqlens_q,
+                              const void* k, const void* v,
+                              const int32_t* cu_seqlens_k,
+                              const int32_t* block_table, int max_pages_per_seq, int page_size,
+                              void* o, float* lse,
+                              int B, int H, int D, int total_q, int max_seqlen_q, int max_seqlen_k,
+                              float softmax_scale, int causal, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* attn_status_string(int status);
+
+/* Message describing the last error returned on the calling host thread. */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_MI355X_H */

@@ -1,0 +1,57 @@
+"""Shared helpers of the GPU parity tests: host arrays -> device tensors and the
+error measures with the tolerances of the 16-bit path."""
+from __future__ import annotations
+
+import numpy as np
+
+# 16-bit path: max |O - O_ref| <= 1e-2, RMSE(O) <= 2e-3, max |LSE - LSE_ref| <= 1e-3
+MAX_ABS = 1e-2
+RMSE = 2e-3
+LSE_TOL = 1e-3
+
+
+def to_dev(x: np.ndarray, dtype: str = "bf16"):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    t = t.to(torch.bfloat16 if dtype == "bf16" else torch.float16)
+    return t.cuda()
+
+
+def to_host(t) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def errors(o, o_ref, lse=None, lse_ref=None):
+    """Max-abs and RMSE over the entries the reference computed (non-NaN), and
+    the LSE max-abs over finite reference entries (infinite ones must match)."""
+    sel = ~np.isnan(o_ref)
+    d = o[sel] - o_ref[sel]
+    out = {"max_abs": float(np.abs(d).max()) if d.size else 0.0,
+           "rmse": float(np.sqrt(np.mean(d * d))) if d.size else 0.0,
+           "nan_in_out": bool(np.isnan(o[sel]).any())}
+    if lse is not None:
+        lsel = ~np.isnan(lse_ref)
+        fin = np.isfinite(lse_ref) & lsel
+        out["lse_max_abs"] = float(np.abs(lse[fin] - lse_ref[fin]).max()) if fin.any() else 0.0
+        out["lse_inf_match"] = bool(np.array_equal(lse[lsel & ~fin], lse_ref[lsel & ~fin]))
+    return out
+
+
+def assert_close16(o, o_ref, lse=None, lse_ref=None, what=""):
+    e = errors(o, o_ref, lse, lse_ref)
+    assert not e["nan_in_out"], f"{what}: NaN in output {e}"
+    assert e["max_abs"] <= MAX_ABS, f"{what}: {e}"
+    assert e["rmse"] <= RMSE, f"{what}: {e}"
+    if lse is not None:
+        assert e["lse_max_abs"] <= LSE_TOL, f"{what}: {e}"
+        assert e["lse_inf_match"], f"{what}: empty rows must give LSE = -inf {e}"
+    return e
+
+
+def sample_rows(seq: int, seed: int, n_random: int = 64, br: int = 128):
+    """Rows {0, 1, Br-1, Br, S/2, S-1} plus seeded random rows."""
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, br - 1, br, seq // 2, seq - 1]
+    rows = set(r for r in fixed if 0 <= r < seq)
+    rows.update(int(x) for x in rng.integers(0, seq, size=min(n_random, seq)))
+    return np.array(sorted(rows))
