@@ -46,19 +46,53 @@ __device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-// two floats -> packed 16-bit pair (round to nearest even), low half = a
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// two floats -> packed 16-bit pair (round to nearest even), low half = a;
+// one v_cvt_pk_{bf16,f16}_f32 on gfx950
 template <int DT>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const f32x2 v = {a, b};
   if constexpr (DT == kBF16) {
-    __bf16 x = (__bf16)a, y = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
   } else {
-    _Float16 x = (_Float16)a, y = (_Float16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
   }
 }
 
+// LDS transposing read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives, as its element t (t = 0..3), element i % 4 of the 8-byte
+// chunk addressed by lane 4t + i/4 of the same group.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// max / sum of a value with the same lane of the other half-wave (l ^ 32)
+__device__ __forceinline__ float halfwave_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halfwave_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Asynchronous global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's bytes land at lds_wave_base + 16*l; lds_wave_base must be the same
+// for every lane of the wave.  Completion is tracked by vmcnt.
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+// wait until every global load (including LDS DMA) issued by this wave is done
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Swap bits 2 and 3 of a row index inside a 32-row MFMA tile.  Storing key k
 // (or head-dim row d) at LDS row swz(k) and reading row m = lane % 32 makes

@@ -9,18 +9,25 @@
 // How it maps to CDNA4:
 //  * one workgroup = 4 waves = 128 query rows; each wave owns 32 rows and keeps
 //    its Q fragments in registers for the whole key loop;
-//  * K and V tiles of 64 keys go through a two-stage LDS ring: the global loads
-//    of tile j+1 are issued before the matrix work on tile j, and land in the
-//    other LDS stage after it (one barrier per tile);
+//  * K and V tiles of 64 keys go through a two-stage LDS ring filled by
+//    asynchronous global -> LDS copies (global_load_lds_dwordx4): the copies of
+//    tile j+1 are issued before the matrix work on tile j and need no
+//    registers (one barrier per tile);
 //  * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16, so
 //    every lane owns one query column: the row max and row sum are in-lane
-//    reductions plus one exchange between the two half-waves;
-//  * V is written to LDS transposed (head_dim-major) so that the second GEMM,
-//    O^T = V^T P^T, reads its operand with one 16-byte LDS load and takes P^T
-//    straight from the score accumulators (no LDS round trip for P);
+//    reductions plus one half-wave exchange (v_permlane32_swap);
+//  * the second GEMM is O^T = V^T P^T: P^T comes straight from the score
+//    accumulators (no LDS round trip) and V^T is read from the row-major V tile
+//    with the LDS transposing read ds_read_b64_tr_b16, so V is never
+//    transposed in memory;
 //  * exp is evaluated as exp2 with scale*log2(e) folded into one FMA;
-//  * rows past the sequence end and keys past Lk are zero-filled in LDS and
-//    masked, so whatever memory lies there never reaches the result.
+//  * the running max is only moved when a row's new maximum exceeds it by more
+//    than 2^8 (in probability units): between moves the probabilities are
+//    bounded by 256, the result is the same exact identity, and the output
+//    rescale (D/32 x 16 multiplies per lane) is skipped on almost every tile;
+//  * query rows past the sequence end are zero-filled; key rows past Lk are
+//    never read from memory (the copy repeats row Lk-1) and are masked, so
+//    whatever memory lies past the sequence never reaches the result.
 #pragma once
 
 #include "common.hpp"
@@ -31,24 +38,34 @@ template <int D>
 struct Fwd16Cfg {
   static constexpr int BR = 128;                  // query rows per workgroup
   static constexpr int BC = 64;                   // keys per tile
-  static constexpr int KSTR = D + 8;              // LDS row pitch of K tiles (elements)
-  static constexpr int VSTR = BC + 8;             // LDS row pitch of transposed V tiles
-  static constexpr int K_ELEMS = BC * KSTR;
-  static constexpr int V_ELEMS = D * VSTR;
-  static constexpr int NK = BC * D / 8 / 256;     // 16-byte K chunks per thread
-  static constexpr int NVB = (BC / 4) * (D / 8);  // 4-key x 8-dim V blocks per tile
-  static constexpr int NV = (NVB + 255) / 256;    // V blocks per thread
+  static constexpr int CPR = D / 8;               // 16-byte chunks per row
+  // LDS row pitches in 16-byte slots.  K: one pad slot, so the 16 rows read by
+  // 16 consecutive lanes with ds_read_b128 start in 16 different bank groups.
+  // V: the transposing reads fetch 4 rows x 32 bytes per 16 lanes; the pitch
+  // puts those 4 rows in distinct 32-byte bank groups.
+  static constexpr int KSLOTS = CPR + 1;
+  static constexpr int VSLOTS = D == 64 ? 10 : (D == 128 ? 19 : 34);
+  static constexpr int KP = 8 * KSLOTS;           // pitches in elements
+  static constexpr int VP = 8 * VSLOTS;
+  static constexpr int K_ELEMS = BC * KP;
+  static constexpr int V_ELEMS = BC * VP;
+  // a tile is copied by KSLOTS (VSLOTS) wave instructions of 64 x 16 bytes,
+  // dealt round-robin to the 4 waves
+  static constexpr int KI_W = (KSLOTS + 3) / 4;
+  static constexpr int VI_W = (VSLOTS + 3) / 4;
   static constexpr int WAVES_PER_EU = D <= 128 ? 2 : 1;
-  static constexpr int LDS_BYTES = 2 * (2 * K_ELEMS + 2 * V_ELEMS);
 };
+
+// Probabilities may grow to 2^kLazyRescale before the running max is moved.
+constexpr float kLazyRescale = 8.0f;
 
 template <int D, int DT, bool CAUSAL, int MODE>
 __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(FwdArgs a) {
   using C = Fwd16Cfg<D>;
-  constexpr int BR = C::BR, BC = C::BC, KSTR = C::KSTR, VSTR = C::VSTR;
+  constexpr int BR = C::BR, BC = C::BC, KP = C::KP, VP = C::VP, CPR = C::CPR;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::K_ELEMS + 2 * C::V_ELEMS];
   uint16_t* const ks_base = smem;
-  uint16_t* const vt_base = smem + 2 * C::K_ELEMS;
+  uint16_t* const vs_base = smem + 2 * C::K_ELEMS;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
@@ -110,75 +127,91 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
       qf[kk] = qi < Lq ? *(const u32x4*)(qp + 16 * kk) : u32x4{0, 0, 0, 0};
   }
 
-  // ---- K/V tile staging ----------------------------------------------------
-  auto row_off = [&](int key, int64_t base, int64_t ss) -> int64_t {
+  // ---- K/V tiles: asynchronous global -> LDS copies --------------------------
+  // Slot s of a tile (16 bytes) holds LDS row s / SLOTS, column chunk s % SLOTS;
+  // chunks >= CPR are padding and are not copied.  K rows are stored with the
+  // rows of each 32-row group in swz23 order, V rows in natural order.
+  const uint16_t* const kg = (const uint16_t*)a.k + koff;
+  const uint16_t* const vg = (const uint16_t*)a.v + voff;
+  auto k_slot = [&](int ii, int& key_local, int& chunk) {
+    const int s = 64 * (wave + 4 * ii) + lane;
+    const int r = s / C::KSLOTS;
+    chunk = s - r * C::KSLOTS;
+    key_local = (r & ~31) | swz23(r & 31);
+  };
+  auto v_slot = [&](int ii, int& key_local, int& chunk) {
+    const int s = 64 * (wave + 4 * ii) + lane;
+    key_local = s / C::VSLOTS;
+    chunk = s - key_local * C::VSLOTS;
+  };
+  // element offsets of this lane's slots for full tiles of the dense/varlen layouts
+  int k_off[C::KI_W], v_off[C::VI_W];
+  uint32_t k_on = 0, v_on = 0;  // bit ii: this lane copies a real chunk in its ii-th copy
+#pragma unroll
+  for (int ii = 0; ii < C::KI_W; ++ii) {
+    int kl, ch;
+    k_slot(ii, kl, ch);
+    k_off[ii] = kl * (int)a.k_ss + ch * 8;
+    if (wave + 4 * ii < C::KSLOTS && ch < CPR) k_on |= 1u << ii;
+  }
+#pragma unroll
+  for (int ii = 0; ii < C::VI_W; ++ii) {
+    int kl, ch;
+    v_slot(ii, kl, ch);
+    v_off[ii] = kl * (int)a.v_ss + ch * 8;
+    if (wave + 4 * ii < C::VSLOTS && ch < CPR) v_on |= 1u << ii;
+  }
+  auto row_of = [&](int key) -> int64_t {  // element offset of key's row (paged: through the table)
     if constexpr (MODE == kPaged) {
       const int page = a.block_table[(int64_t)b * a.max_pages + (key >> a.page_shift)];
-      const int64_t phys = ((int64_t)page << a.page_shift) | (key & ((1 << a.page_shift) - 1));
-      return base + phys * ss;
+      return (((int64_t)page << a.page_shift) | (key & ((1 << a.page_shift) - 1)));
     } else {
-      return base + (int64_t)key * ss;
+      return key;
     }
   };
-
-  u32x4 kreg[C::NK];
-  u32x4 vreg[C::NV][4];
-  const uint16_t* const kg = (const uint16_t*)a.k;
-  const uint16_t* const vg = (const uint16_t*)a.v;
-
-  auto load_tile = [&](int key0) {
+  auto dma_tile = [&](int key0, int buf) {
+    uint16_t* kb = ks_base + buf * C::K_ELEMS;
+    uint16_t* vb = vs_base + buf * C::V_ELEMS;
+    if (MODE != kPaged && key0 + BC <= Lk) {
+      const uint16_t* k0p = kg + (int64_t)key0 * a.k_ss;
+      const uint16_t* v0p = vg + (int64_t)key0 * a.v_ss;
 #pragma unroll
-    for (int i = 0; i < C::NK; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / (D / 8), col = c % (D / 8);
-      const int key = key0 + row;
-      kreg[i] = key < Lk ? *(const u32x4*)(kg + row_off(key, koff, a.k_ss) + col * 8)
-                         : u32x4{0, 0, 0, 0};
-    }
+      for (int ii = 0; ii < C::KI_W; ++ii)
+        if ((k_on >> ii) & 1u) dma16(k0p + k_off[ii], kb + (wave + 4 * ii) * 512);
 #pragma unroll
-    for (int i = 0; i < C::NV; ++i) {
-      const int blk = tid + 256 * i;
-      if (C::NVB % 256 == 0 || blk < C::NVB) {
-        const int kgp = blk % (BC / 4), dc = blk / (BC / 4);
+      for (int ii = 0; ii < C::VI_W; ++ii)
+        if ((v_on >> ii) & 1u) dma16(v0p + v_off[ii], vb + (wave + 4 * ii) * 512);
+    } else {
+      // partial last tile or paged cache: rows past Lk repeat row Lk-1 (finite
+      // data, masked out of the scores and multiplied by p = 0)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int key = key0 + 4 * kgp + u;
-          vreg[i][u] = key < Lk ? *(const u32x4*)(vg + row_off(key, voff, a.v_ss) + dc * 8)
-                                : u32x4{0, 0, 0, 0};
+      for (int ii = 0; ii < C::KI_W; ++ii) {
+        const int i = wave + 4 * ii;
+        if (i < C::KSLOTS) {
+          int kl, ch;
+          k_slot(ii, kl, ch);
+          if (ch < CPR) dma16(kg + row_of(min(key0 + kl, Lk - 1)) * a.k_ss + ch * 8, kb + i * 512);
+        }
+      }
+#pragma unroll
+      for (int ii = 0; ii < C::VI_W; ++ii) {
+        const int i = wave + 4 * ii;
+        if (i < C::VSLOTS) {
+          int kl, ch;
+          v_slot(ii, kl, ch);
+          if (ch < CPR) dma16(vg + row_of(min(key0 + kl, Lk - 1)) * a.v_ss + ch * 8, vb + i * 512);
         }
       }
     }
   };
 
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = ks_base + buf * C::K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < C::NK; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / (D / 8), col = c % (D / 8);
-      const int lrow = (row & ~31) | swz23(row & 31);
-      *(u32x4*)(ks + lrow * KSTR + col * 8) = kreg[i];
-    }
-    uint16_t* vt = vt_base + buf * C::V_ELEMS;
-#pragma unroll
-    for (int i = 0; i < C::NV; ++i) {
-      const int blk = tid + 256 * i;
-      if (C::NVB % 256 == 0 || blk < C::NVB) {
-        const int kgp = blk % (BC / 4), dc = blk / (BC / 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = 8 * dc + e;
-          const int lrow = (d & ~31) | swz23(d & 31);
-          const int w = e >> 1, sh = (e & 1) * 16;
-          const uint32_t x0 = (vreg[i][0][w] >> sh) & 0xffffu;
-          const uint32_t x1 = (vreg[i][1][w] >> sh) & 0xffffu;
-          const uint32_t x2 = (vreg[i][2][w] >> sh) & 0xffffu;
-          const uint32_t x3 = (vreg[i][3][w] >> sh) & 0xffffu;
-          *(u32x2*)(vt + lrow * VSTR + 4 * kgp) = u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
-        }
-      }
-    }
-  };
+  // V^T operand addressing for ds_read_b64_tr_b16: lane (group g, index j)
+  // points at key 8*(g/2) + j/4 (+4 for the second read) and head-dim column
+  // 16*(g%2) + 4*swap(j%4), so that after the transpose lane l holds
+  // V[key 8*(l/32) + e][d = swz23(l % 32)] for e = 0..7.
+  const int vg_grp = lane >> 4, vg_j = lane & 15;
+  const int vtr_off = (8 * (vg_grp >> 1) + (vg_j >> 2)) * VP + 16 * (vg_grp & 1) +
+                      4 * (((vg_j & 1) << 1) | ((vg_j >> 1) & 1));
 
   // ---- running state ---------------------------------------------------------
   f32x16 oacc[D / 32];
@@ -186,22 +219,33 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-  float m_run = -INFINITY;  // running max of scale*log2(e)*s
+  float m_run = -INFINITY;  // running max of scale*log2(e)*s (moved lazily)
   float l_run = 0.f;        // this half-wave's share of the running sum
   const float c2 = a.scale_log2;
+  const f32x16 zero16 = {};
 
   auto compute = [&](int key0, int buf) {
     if (!wave_active) return;
     if (CAUSAL && key0 > wave_last_key) return;  // tile fully masked for this wave
-    const uint16_t* ks = ks_base + buf * C::K_ELEMS + l32 * KSTR + 8 * hh;
+    // S^T = K Q^T
+    const uint16_t* ks = ks_base + buf * C::K_ELEMS + l32 * KP + 8 * hh;
     f32x16 s[BC / 32];
+    {
+      // all K operands of the tile are read before the first MFMA so that the
+      // LDS latency is paid once; the two score tiles form independent chains
+      constexpr int NKK = D / 16;
+      u32x4 kop[BC / 32][NKK];
 #pragma unroll
-    for (int tt = 0; tt < BC / 32; ++tt) {
+      for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[tt][r] = 0.f;
+        for (int tt = 0; tt < BC / 32; ++tt) kop[tt][kk] = *(const u32x4*)(ks + tt * 32 * KP + 16 * kk);
+      __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the first MFMA
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-        s[tt] = mfma32<DT>(*(const u32x4*)(ks + tt * 32 * KSTR + 16 * kk), qf[kk], s[tt]);
+      for (int tt = 0; tt < BC / 32; ++tt) s[tt] = mfma32<DT>(kop[tt][0], qf[0], zero16);
+#pragma unroll
+      for (int kk = 1; kk < NKK; ++kk)
+#pragma unroll
+        for (int tt = 0; tt < BC / 32; ++tt) s[tt] = mfma32<DT>(kop[tt][kk], qf[kk], s[tt]);
     }
     // register r of tile tt holds key key0 + 32tt + 16(r/8) + 8hh + r%8
     const bool need_mask = (key0 + BC > Lk) || (CAUSAL && key0 + BC - 1 > qw + diag);
@@ -220,11 +264,19 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
     for (int tt = 0; tt < BC / 32; ++tt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    const float nb = -m_use;
+    const float mxs = halfwave_max(mx) * c2;
+    // move the running max only when some row's new max exceeds it by > 2^8
+    if (__builtin_amdgcn_ballot_w64(mxs > m_run + kLazyRescale) != 0) {
+      const float m_new = fmaxf(m_run, mxs);
+      const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      m_run = m_new;
+    }
+    const float nb = m_run == -INFINITY ? 0.f : -m_run;
     float psum = 0.f;
 #pragma unroll
     for (int tt = 0; tt < BC / 32; ++tt)
@@ -234,43 +286,39 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
         s[tt][r] = p;
         psum += p;
       }
-    l_run = alpha * l_run + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-    u32x4 pk[BC / 16];
+    l_run += psum;
+    // O^T += V^T P^T over four 16-key chunks
+    const uint16_t* vs = vs_base + buf * C::V_ELEMS + vtr_off;
 #pragma unroll
     for (int c = 0; c < BC / 16; ++c) {
-      const int tt = c >> 1, r0 = 8 * (c & 1);
-      pk[c] = u32x4{pack2<DT>(s[tt][r0 + 0], s[tt][r0 + 1]), pack2<DT>(s[tt][r0 + 2], s[tt][r0 + 3]),
-                    pack2<DT>(s[tt][r0 + 4], s[tt][r0 + 5]), pack2<DT>(s[tt][r0 + 6], s[tt][r0 + 7])};
+      const int tt = c >> 1, r0p = 8 * (c & 1);
+      const u32x4 pk = {pack2<DT>(s[tt][r0p + 0], s[tt][r0p + 1]), pack2<DT>(s[tt][r0p + 2], s[tt][r0p + 3]),
+                        pack2<DT>(s[tt][r0p + 4], s[tt][r0p + 5]), pack2<DT>(s[tt][r0p + 6], s[tt][r0p + 7])};
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const uint16_t* p = vs + 16 * c * VP + 32 * dt;
+        const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * VP);
+        oacc[dt] = mfma32<DT>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pk, oacc[dt]);
+      }
     }
-    const uint16_t* vt = vt_base + buf * C::V_ELEMS + l32 * VSTR + 8 * hh;
-#pragma unroll
-    for (int c = 0; c < BC / 16; ++c)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        oacc[dt] = mfma32<DT>(*(const u32x4*)(vt + dt * 32 * VSTR + 16 * c), pk[c], oacc[dt]);
   };
 
   // ---- key loop: two-stage LDS ring ------------------------------------------
   if (n_kv > 0) {
-    load_tile(0);
-    store_tile(0);
+    dma_tile(0, 0);
+    wait_vmem();
     __syncthreads();
     for (int j = 0; j < n_kv; ++j) {
       const int buf = j & 1;
-      if (j + 1 < n_kv) load_tile((j + 1) * BC);
+      if (j + 1 < n_kv) dma_tile((j + 1) * BC, buf ^ 1);  // lands while tile j is computed
       compute(j * BC, buf);
-      if (j + 1 < n_kv) store_tile(buf ^ 1);
+      wait_vmem();
       __syncthreads();
     }
   }
 
   // ---- epilogue: o / l, lse = ln2 * (m + log2 l) -----------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = halfwave_sum(l_run);
   if (qi < Lq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* op = (uint16_t*)a.o + ooff + (int64_t)qi * a.o_ss + 8 * hh;
@@ -278,11 +326,11 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int r0 = 8 * half;
+        const int r0p = 8 * half;
         const f32x16& o = oacc[dt];
         *(u32x4*)(op + 32 * dt + 16 * half) =
-            u32x4{pack2<DT>(o[r0 + 0] * inv, o[r0 + 1] * inv), pack2<DT>(o[r0 + 2] * inv, o[r0 + 3] * inv),
-                  pack2<DT>(o[r0 + 4] * inv, o[r0 + 5] * inv), pack2<DT>(o[r0 + 6] * inv, o[r0 + 7] * inv)};
+            u32x4{pack2<DT>(o[r0p + 0] * inv, o[r0p + 1] * inv), pack2<DT>(o[r0p + 2] * inv, o[r0p + 3] * inv),
+                  pack2<DT>(o[r0p + 4] * inv, o[r0p + 5] * inv), pack2<DT>(o[r0p + 6] * inv, o[r0p + 7] * inv)};
       }
     if (hh == 0 && a.lse != nullptr)
       a.lse[lse_base + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;

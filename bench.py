@@ -40,7 +40,22 @@ def parse():
     p.add_argument("--no-fp8", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--sweep", action="store_true", help="also time the 16384-token seq sweep (extra output)")
+    p.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB (calibrates the FETCH_SIZE/WRITE_SIZE counters)")
     return p.parse_args()
+
+
+def copy_reference(mib):
+    """A plain device-to-device copy of known size, run a few times: the HBM
+    byte counters read on it give the scale applied to the kernel's readings."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.arange(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_reference_bytes_read": n * 4, "copy_reference_bytes_written": n * 4}))
 
 
 def time_launches(fn, steps, warmup):
@@ -90,6 +105,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.copy_reference:
+        copy_reference(args.copy_reference)
+        return
     import torch
     import attention_attn_fwd_10_amd as A
     import workloads as W
