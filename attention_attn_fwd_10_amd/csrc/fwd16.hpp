@@ -277,30 +277,30 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
       m_run = m_new;
     }
     const float nb = m_run == -INFINITY ? 0.f : -m_run;
-    float psum = 0.f;
-#pragma unroll
-    for (int tt = 0; tt < BC / 32; ++tt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(s[tt][r], c2, nb));
-        s[tt][r] = p;
-        psum += p;
-      }
-    l_run += psum;
-    // O^T += V^T P^T over four 16-key chunks
     const uint16_t* vs = vs_base + buf * C::V_ELEMS + vtr_off;
+    float psum = 0.f;
+    // O^T += V^T P^T over four 16-key chunks: the exponentials of a chunk, then
+    // its D/32 MFMAs, so the matrix work of one chunk overlaps the next chunk's
+    // exponentials
 #pragma unroll
     for (int c = 0; c < BC / 16; ++c) {
       const int tt = c >> 1, r0p = 8 * (c & 1);
-      const u32x4 pk = {pack2<DT>(s[tt][r0p + 0], s[tt][r0p + 1]), pack2<DT>(s[tt][r0p + 2], s[tt][r0p + 3]),
-                        pack2<DT>(s[tt][r0p + 4], s[tt][r0p + 5]), pack2<DT>(s[tt][r0p + 6], s[tt][r0p + 7])};
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = fast_exp2(fmaf(s[tt][r0p + e], c2, nb));
+        psum += p[e];
+      }
+      const u32x4 pk = {pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3]), pack2<DT>(p[4], p[5]),
+                        pack2<DT>(p[6], p[7])};
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const uint16_t* p = vs + 16 * c * VP + 32 * dt;
-        const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * VP);
+        const uint16_t* vp = vs + 16 * c * VP + 32 * dt;
+        const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * VP);
         oacc[dt] = mfma32<DT>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pk, oacc[dt]);
       }
     }
+    l_run += psum;
   };
 
   // ---- key loop: two-stage LDS ring ------------------------------------------
