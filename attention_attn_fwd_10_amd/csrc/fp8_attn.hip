@@ -1,6 +1,307 @@
-// 8-bit fused forward (placeholder until the e4m3 kernel lands).
+// 8-bit fused attention forward for gfx950 ("Fused attention kernel" page,
+// section "8-bit forward pass"): both GEMMs run on e4m3 inputs, V tiles are
+// transposed on chip, and every block of Q, K and V carries its own scale.
+//
+// Layout and schedule follow the 16-bit kernel: 4 waves x 32 query rows per
+// workgroup, 64-key K/V tiles copied asynchronously into a two-stage LDS ring,
+// scores computed transposed (S^T = K Q^T) with v_mfma_f32_32x32x64_f8f6f4 so a
+// lane owns one query row, online softmax in exp2 form, then
+// O^T += V^T P^T with the probabilities quantised to e4m3 in registers.
+//
+// The 8-bit specifics:
+//  * V^T comes from the row-major V tile through ds_read_b64_tr_b8 (the pages'
+//    in-shared-memory transpose; no global pre-transpose);
+//  * scales: a tile's score scale sq * sk * softmax_scale * log2(e) is one
+//    scalar folded into the exp2 FMA.  The output accumulator is kept in units
+//    of a reference V scale (the largest block scale seen so far); a tile whose
+//    V block scale is smaller gets the ratio folded into the exp2 bias of its
+//    probabilities, so block scales cost no per-element work, and the
+//    accumulator is rescaled only when a larger block scale appears;
+//  * probabilities are quantised as p * 2^6 with the running max allowed to
+//    lag the true max by at most 2^2, so quantised values stay in (0, 256] —
+//    inside the e4m3 range (the converter does not saturate) and mostly in its
+//    normal range;
+//  * the row sum is accumulated from the unquantised float32 probabilities.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace attn {
-hipError_t launch_fwd_fp8(const Fp8Args&, int, bool, hipStream_t) { return hipErrorNotSupported; }
+
+namespace fp8cfg {
+constexpr int D = 128;
+constexpr int BR = 128;            // query rows per workgroup
+constexpr int BC = 64;             // keys per tile
+constexpr int SLOTS = D / 16 + 1;  // 16-byte slots per LDS row (one pad slot): pitch 144 bytes
+constexpr int PITCH = 16 * SLOTS;  // bytes
+constexpr int TILE_BYTES = BC * PITCH;
+constexpr int I_W = (SLOTS + 3) / 4;  // copy instructions per wave per tile (max)
+constexpr float kMu = 6.0f;        // probabilities are quantised as p * 2^kMu
+constexpr float kTau = 2.0f;       // the running max may lag by 2^kTau
+}  // namespace fp8cfg
+
+// two floats -> two e4m3 bytes (nearest-even; values above 464 would become NaN)
+// written into the low (HI = false) or high 16 bits of `old`
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt_pk_fp8(float a, float b, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+}
+
+// LDS transposing byte read (ds_read_b64_tr_b8).  Within each group of 16
+// lanes, lane i receives, as its byte t (t = 0..7), byte i % 8 of the 8-byte
+// chunk addressed by lane 2t + i/8 of the same group.
+__device__ __forceinline__ u32x2 lds_read_tr8(const uint8_t* p) {
+  typedef int v2i __attribute__((vector_size(8)));
+  typedef __attribute__((address_space(3))) v2i lds_v2i;
+  const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+template <bool CAUSAL>
+__global__ void __launch_bounds__(256, 2) fwd_fp8_kernel(Fp8Args a) {
+  using namespace fp8cfg;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_BYTES];
+  uint8_t* const ks_base = smem;
+  uint8_t* const vs_base = smem + 2 * TILE_BYTES;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = t / a.n_qblk;
+  int qblk = t - bh * a.n_qblk;
+  if (CAUSAL) qblk = a.n_qblk - 1 - qblk;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int Lq = a.Sq, Lk = a.Sk;
+  const int qs = qblk * BR;
+
+  const int64_t row_q = (int64_t)a.H * D;  // bytes between consecutive rows (contiguous [B,S,H,D])
+  const int64_t qoff = ((int64_t)b * Lq) * row_q + (int64_t)h * D;
+  const int64_t koff = ((int64_t)b * Lk) * row_q + (int64_t)h * D;
+
+  int n_kv = (Lk + BC - 1) / BC;
+  if (CAUSAL) {
+    const int last = min(qs + BR, Lq) - 1 + (Lk - Lq);
+    n_kv = last < 0 ? 0 : min(n_kv, last / BC + 1);
+  }
+  const int qw = qs + 32 * wave;
+  const int qi = qw + l32;
+  const bool wave_active = qw < Lq;
+  const int diag = Lk - Lq;
+  const int wave_last_key = CAUSAL ? min(qw + 31, Lq - 1) + diag : Lk - 1;
+
+  // scales: per (b, h, 128-row block), or one per tensor
+  const bool blocked = a.block_rows != 0;
+  const int nbq = (Lq + 127) / 128, nbk = (Lk + 127) / 128;
+  const float sq = blocked ? a.qs[(int64_t)bh * nbq + qblk] : a.qs[0];
+  const float* const ks_scale = blocked ? a.ks + (int64_t)bh * nbk : a.ks;
+  const float* const vs_scale = blocked ? a.vs + (int64_t)bh * nbk : a.vs;
+  const float qk_scale = sq * a.scale_log2;
+
+  // Q fragments: lane (query l32, half hh) holds q[64kk + 32hh .. +31]
+  i32x8 qf[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    if (qi < Lq) {
+      const uint8_t* qp = a.q + qoff + (int64_t)qi * row_q + 64 * kk + 32 * hh;
+      const u32x4 x0 = *(const u32x4*)qp, x1 = *(const u32x4*)(qp + 16);
+      qf[kk] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+    } else {
+      qf[kk] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+
+  // ---- asynchronous tile copies ----------------------------------------------
+  // LDS row R of a K tile holds key 32((m>>2)&1) + 16(R/32) + 4(m>>3) + (m&3),
+  // m = R % 32: then score register r of tile tt in lane half hh belongs to key
+  // 32hh + 16tt + r, so each lane's 32 probabilities are 32 consecutive keys.
+  auto k_row_key = [](int R) {
+    const int m = R & 31;
+    return 32 * ((m >> 2) & 1) + 16 * (R >> 5) + 4 * (m >> 3) + (m & 3);
+  };
+  const uint8_t* const kg = a.k + koff;
+  const uint8_t* const vg = a.v + koff;
+  int k_off[I_W], v_off[I_W];
+  int k_key[I_W], v_key[I_W], chunk[I_W];
+  uint32_t on = 0;
+#pragma unroll
+  for (int ii = 0; ii < I_W; ++ii) {
+    const int s = 64 * (wave + 4 * ii) + lane;
+    const int R = s / SLOTS, c = s - R * SLOTS;
+    k_key[ii] = k_row_key(R);
+    v_key[ii] = R;
+    chunk[ii] = c;
+    k_off[ii] = k_key[ii] * (int)row_q + 16 * c;
+    v_off[ii] = R * (int)row_q + 16 * c;
+    if (wave + 4 * ii < SLOTS && c < SLOTS - 1) on |= 1u << ii;
+  }
+  auto dma_tile = [&](int key0, int buf) {
+    uint8_t* kb = ks_base + buf * TILE_BYTES;
+    uint8_t* vb = vs_base + buf * TILE_BYTES;
+    if (key0 + BC <= Lk) {
+      const uint8_t* k0p = kg + (int64_t)key0 * row_q;
+#pragma unroll
+      for (int ii = 0; ii < I_W; ++ii)
+        if ((on >> ii) & 1u) dma16(k0p + k_off[ii], kb + (wave + 4 * ii) * 1024);
+#pragma unroll
+      for (int ii = 0; ii < I_W; ++ii)
+        if ((on >> ii) & 1u) dma16(vg + (int64_t)key0 * row_q + v_off[ii], vb + (wave + 4 * ii) * 1024);
+    } else {
+      // rows past Lk repeat row Lk-1 (finite data; masked scores, p = 0)
+#pragma unroll
+      for (int ii = 0; ii < I_W; ++ii)
+        if ((on >> ii) & 1u) {
+          dma16(kg + (int64_t)min(key0 + k_key[ii], Lk - 1) * row_q + 16 * chunk[ii], kb + (wave + 4 * ii) * 1024);
+          dma16(vg + (int64_t)min(key0 + v_key[ii], Lk - 1) * row_q + 16 * chunk[ii], vb + (wave + 4 * ii) * 1024);
+        }
+    }
+  };
+
+  // V^T operand: lane (group g, index j) addresses row 32(g/2) + 8u + j/2 and
+  // columns 32dt + 16(g%2) + 8(j%2); after the byte transpose lane l holds
+  // V[32(l/32) + 8u + t][32dt + l%32] as its elements 8u + t.
+  const int vgrp = lane >> 4, vj = lane & 15;
+  const int vtr_off = (32 * (vgrp >> 1) + (vj >> 1)) * PITCH + 16 * (vgrp & 1) + 8 * (vj & 1);
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+  float m_run = -INFINITY;  // running max of the log2-domain scores (lazy)
+  float l_run = 0.f;        // this half-wave's share of sum p * 2^kMu
+  float sv_ref = 0.f;       // V scale the accumulator is expressed in
+  const f32x16 zero16 = {};
+
+  auto compute = [&](int j, int buf) {
+    const int key0 = j * BC;
+    if (!wave_active) return;
+    if (CAUSAL && key0 > wave_last_key) return;
+    const float c2 = qk_scale * ks_scale[blocked ? key0 >> 7 : 0];
+    const float sv = vs_scale[blocked ? key0 >> 7 : 0];
+    // S^T = K Q^T: two 32-key tiles, two 64-wide k steps each
+    const uint8_t* ks = ks_base + buf * TILE_BYTES + l32 * PITCH + 32 * hh;
+    i32x8 kop[2][2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const u32x4 x0 = *(const u32x4*)(ks + tt * 32 * PITCH + 64 * kk);
+        const u32x4 x1 = *(const u32x4*)(ks + tt * 32 * PITCH + 64 * kk + 16);
+        kop[tt][kk] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      }
+    f32x16 s[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) s[tt] = mfma32_fp8(kop[tt][0], qf[0], zero16);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) s[tt] = mfma32_fp8(kop[tt][1], qf[1], s[tt]);
+    // register r of tile tt holds key key0 + 32hh + 16tt + r
+    const bool need_mask = (key0 + BC > Lk) || (CAUSAL && key0 + BC - 1 > qw + diag);
+    if (need_mask) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * hh + 16 * tt + r;
+          if (key >= Lk || (CAUSAL && key > qi + diag)) s[tt][r] = -INFINITY;
+        }
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tt][r]);
+    const float mxs = halfwave_max(mx) * c2;
+    // a larger V block scale becomes the accumulator's reference (uniform branch)
+    if (sv > sv_ref) {
+      const float ratio = sv_ref / sv;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= ratio;
+      sv_ref = sv;
+    }
+    if (__builtin_amdgcn_ballot_w64(mxs > m_run + kTau) != 0) {
+      const float m_new = fmaxf(m_run, mxs);
+      const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      m_run = m_new;
+    }
+    // p'' = 2^(c2 s - m + kMu) * sv / sv_ref is what enters the MFMA; the sum
+    // keeps p' = p'' * sv_ref / sv
+    const float vratio = sv / sv_ref, inv_vratio = sv_ref / sv;
+    const float bias = m_run == -INFINITY ? 0.f : kMu + __log2f(vratio) - m_run;
+    float psum = 0.f;
+    uint32_t pw[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int tt = w >> 2, r0 = 4 * (w & 3);
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[e] = fast_exp2(fmaf(s[tt][r0 + e], c2, bias));
+        psum += p[e];
+      }
+      pw[w] = cvt_pk_fp8<true>(p[2], p[3], cvt_pk_fp8<false>(p[0], p[1], 0u));
+    }
+    l_run += psum * inv_vratio;
+    const i32x8 pk = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
+    // O^T += V^T P^T (64 keys per MFMA)
+    const uint8_t* vs = vs_base + buf * TILE_BYTES + vtr_off;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      u32x2 r[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) r[u] = lds_read_tr8(vs + 8 * u * PITCH + 32 * dt);
+      const i32x8 vop = {(int)r[0][0], (int)r[0][1], (int)r[1][0], (int)r[1][1],
+                         (int)r[2][0], (int)r[2][1], (int)r[3][0], (int)r[3][1]};
+      oacc[dt] = mfma32_fp8(vop, pk, oacc[dt]);
+    }
+  };
+
+  if (n_kv > 0) {
+    dma_tile(0, 0);
+    wait_vmem();
+    __syncthreads();
+    for (int j = 0; j < n_kv; ++j) {
+      const int buf = j & 1;
+      if (j + 1 < n_kv) dma_tile((j + 1) * BC, buf ^ 1);
+      compute(j, buf);
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+
+  // epilogue: O = sv_ref * O_acc / l', lse = ln2 * (m - kMu + log2 l')
+  const float l_tot = halfwave_sum(l_run);
+  if (qi < Lq) {
+    const float inv = l_tot > 0.f ? sv_ref / l_tot : 0.f;
+    uint16_t* op = (uint16_t*)a.o + ((int64_t)b * Lq + qi) * a.H * D + (int64_t)h * D + 4 * hh;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& o = oacc[dt];
+        *(u32x2*)(op + 32 * dt + 8 * g) = u32x2{pack2<kBF16>(o[4 * g] * inv, o[4 * g + 1] * inv),
+                                                pack2<kBF16>(o[4 * g + 2] * inv, o[4 * g + 3] * inv)};
+      }
+    if (hh == 0 && a.lse != nullptr)
+      a.lse[(int64_t)bh * Lq + qi] = l_tot > 0.f ? (m_run - kMu + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+hipError_t launch_fwd_fp8(const Fp8Args& a, int D, bool causal, hipStream_t s) {
+  if (D != fp8cfg::D) return hipErrorNotSupported;
+  const int n = a.B * a.H * a.n_qblk;
+  if (causal)
+    hipLaunchKernelGGL((fwd_fp8_kernel<true>), dim3(n), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_fp8_kernel<false>), dim3(n), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace attn
