@@ -21,7 +21,9 @@
 //    lag the true max by at most 2^2, so quantised values stay in (0, 256] —
 //    inside the e4m3 range (the converter does not saturate) and mostly in its
 //    normal range;
-//  * the row sum is accumulated from the unquantised float32 probabilities.
+//  * the row sum is accumulated from the e4m3-rounded probabilities, the same
+//    values the second GEMM multiplies, so a row dominated by a few keys keeps
+//    its weights consistent.
 #include <type_traits>
 
 #include "common.hpp"
@@ -169,7 +171,8 @@ __global__ void __launch_bounds__(256, 2) fwd_fp8_kernel(Fp8Args a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
   float m_run = -INFINITY;  // running max of the log2-domain scores (lazy)
-  float l_run = 0.f;        // this half-wave's share of sum p * 2^kMu
+  float l_run = 0.f;        // this half-wave's share of sum p * 2^kMu (float32 terms)
+  float lq_run = 0.f;       // the same sum over the e4m3-rounded terms
   float sv_ref = 0.f;       // V scale the accumulator is expressed in
   const f32x16 zero16 = {};
 
@@ -225,6 +228,7 @@ __global__ void __launch_bounds__(256, 2) fwd_fp8_kernel(Fp8Args a) {
       const float m_new = fmaxf(m_run, mxs);
       const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
       l_run *= alpha;
+      lq_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -235,7 +239,10 @@ __global__ void __launch_bounds__(256, 2) fwd_fp8_kernel(Fp8Args a) {
     // keeps p' = p'' * sv_ref / sv
     const float vratio = sv / sv_ref, inv_vratio = sv_ref / sv;
     const float bias = m_run == -INFINITY ? 0.f : kMu + __log2f(vratio) - m_run;
-    float psum = 0.f;
+    // the row sum adds the e4m3-rounded probabilities, exactly the values the
+    // MFMA multiplies, so numerator and denominator share the rounding
+    // (the logsumexp keeps the float32 sum)
+    float psum = 0.f, qsum = 0.f;
     uint32_t pw[8];
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
@@ -247,8 +254,12 @@ __global__ void __launch_bounds__(256, 2) fwd_fp8_kernel(Fp8Args a) {
         psum += p[e];
       }
       pw[w] = cvt_pk_fp8<true>(p[2], p[3], cvt_pk_fp8<false>(p[0], p[1], 0u));
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], true);
+      qsum += (lo[0] + lo[1]) + (hi[0] + hi[1]);
     }
     l_run += psum * inv_vratio;
+    lq_run += qsum * inv_vratio;
     const i32x8 pk = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
     // O^T += V^T P^T (64 keys per MFMA)
     const uint8_t* vs = vs_base + buf * TILE_BYTES + vtr_off;
@@ -276,10 +287,11 @@ __global__ void __launch_bounds__(256, 2) fwd_fp8_kernel(Fp8Args a) {
     }
   }
 
-  // epilogue: O = sv_ref * O_acc / l', lse = ln2 * (m - kMu + log2 l')
+  // epilogue: O = sv_ref * O_acc / lq', lse = ln2 * (m - kMu + log2 l')
   const float l_tot = halfwave_sum(l_run);
+  const float lq_tot = halfwave_sum(lq_run);
   if (qi < Lq) {
-    const float inv = l_tot > 0.f ? sv_ref / l_tot : 0.f;
+    const float inv = lq_tot > 0.f ? sv_ref / lq_tot : 0.f;
     uint16_t* op = (uint16_t*)a.o + ((int64_t)b * Lq + qi) * a.H * D + (int64_t)h * D + 4 * hh;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
