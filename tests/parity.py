@@ -4,10 +4,24 @@ from __future__ import annotations
 
 import numpy as np
 
-# 16-bit path: max |O - O_ref| <= 1e-2, RMSE(O) <= 2e-3, max |LSE - LSE_ref| <= 1e-3
+# 16-bit path: max |O - O_ref| <= 1e-2, RMSE(O) <= 2e-3, max |LSE - LSE_ref| <= 1e-3.
+# The max-abs budget applies to the computed value; the output's own rounding
+# to its 16-bit storage type (half an ulp of the stored value) comes on top,
+# since no 16-bit output can be closer than that to the float64 result (at
+# |O| >= 4 half an ulp of bf16 already exceeds 1e-2).
 MAX_ABS = 1e-2
 RMSE = 2e-3
 LSE_TOL = 1e-3
+
+
+def half_ulp(x, dtype="bf16"):
+    """Half the spacing of the 16-bit format at |x|."""
+    mant = 7 if dtype == "bf16" else 10
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -126 if dtype == "bf16" else -14)
+    return 0.5 * np.exp2(e - mant)
 
 
 def to_dev(x: np.ndarray, dtype: str = "bf16"):
@@ -21,12 +35,15 @@ def to_host(t) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def errors(o, o_ref, lse=None, lse_ref=None):
-    """Max-abs and RMSE over the entries the reference computed (non-NaN), and
-    the LSE max-abs over finite reference entries (infinite ones must match)."""
+def errors(o, o_ref, lse=None, lse_ref=None, dtype="bf16"):
+    """Max-abs and RMSE over the entries the reference computed (non-NaN), the
+    max-abs beyond the storage rounding, and the LSE max-abs over finite
+    reference entries (infinite ones must match)."""
     sel = ~np.isnan(o_ref)
     d = o[sel] - o_ref[sel]
+    beyond = np.abs(d) - half_ulp(o[sel], dtype)
     out = {"max_abs": float(np.abs(d).max()) if d.size else 0.0,
+           "max_abs_beyond_rounding": float(beyond.max()) if d.size else 0.0,
            "rmse": float(np.sqrt(np.mean(d * d))) if d.size else 0.0,
            "nan_in_out": bool(np.isnan(o[sel]).any())}
     if lse is not None:
@@ -37,10 +54,10 @@ def errors(o, o_ref, lse=None, lse_ref=None):
     return out
 
 
-def assert_close16(o, o_ref, lse=None, lse_ref=None, what=""):
-    e = errors(o, o_ref, lse, lse_ref)
+def assert_close16(o, o_ref, lse=None, lse_ref=None, what="", dtype="bf16"):
+    e = errors(o, o_ref, lse, lse_ref, dtype)
     assert not e["nan_in_out"], f"{what}: NaN in output {e}"
-    assert e["max_abs"] <= MAX_ABS, f"{what}: {e}"
+    assert e["max_abs_beyond_rounding"] <= MAX_ABS, f"{what}: {e}"
     assert e["rmse"] <= RMSE, f"{what}: {e}"
     if lse is not None:
         assert e["lse_max_abs"] <= LSE_TOL, f"{what}: {e}"

@@ -1,0 +1,149 @@
+"""The C ABI on the CPU (no GPU needed): the shared library loads, exports every
+function include/attn.h declares, and rejects every invalid argument with its
+status code before anything reaches the device."""
+import ctypes
+import json
+import math
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+LIB = os.path.join(ROOT, "attention_attn_fwd_10_amd", "libattn_fwd.so")
+
+OK, INVALID, UNSUPPORTED, HIP = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        sys.path.insert(0, ROOT)
+        from attention_attn_fwd_10_amd import build
+        build.build(verbose=False)
+    L = ctypes.CDLL(LIB)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    I64P = ctypes.POINTER(ctypes.c_int64)
+    L.attn_fwd.argtypes = [I, P, I64P, P, I64P, P, I64P, P, I64P, P, I, I, I, I, I, F, I, P]
+    L.attn_fp8_quantize.argtypes = [P, I64P, P, P, I, I, I, I, I, P, P]
+    L.attn_fwd_fp8.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, I, F, I, P]
+    L.attn_fwd_varlen.argtypes = [I, P, P, P, P, P, P, I, I, P, P, I, I, I, I, I, I, F, I, P]
+    L.attn_status_string.argtypes = [I]
+    L.attn_status_string.restype = ctypes.c_char_p
+    L.attn_last_error.restype = ctypes.c_char_p
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("attn_fwd", "attn_fp8_quantize", "attn_fwd_fp8", "attn_fwd_varlen", "attn_status_string",
+              "attn_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if " T " in line)
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def _s(*v):
+    return (ctypes.c_int64 * 3)(*v)
+
+
+# fake, never dereferenced device addresses (validation fails or returns before use)
+A16 = ctypes.c_void_p(0x10000)
+A_ODD = ctypes.c_void_p(0x10008)
+GOOD = _s(1 << 20, 1024, 128)
+
+
+def fwd(lib, dtype=0, q=A16, k=A16, v=A16, o=A16, lse=None, B=1, H=1, Sq=1, Sk=1, D=128, scale=0.1, causal=0,
+        qs=GOOD, ks=GOOD, vs=GOOD, os_=GOOD):
+    return lib.attn_fwd(dtype, q, qs, k, ks, v, vs, o, os_, lse, B, H, Sq, Sk, D, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), INVALID),
+    (dict(D=96), UNSUPPORTED),
+    (dict(D=0), INVALID),
+    (dict(B=-1), INVALID),
+    (dict(Sk=-3), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(scale=0.0), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(causal=2), INVALID),
+    (dict(qs=_s(1 << 20, 1024, 12)), INVALID),     # not a multiple of 8 elements
+    (dict(ks=_s(-8, 1024, 128)), INVALID),         # negative stride
+    (dict(q=None), INVALID),
+    (dict(v=None), INVALID),
+    (dict(o=A_ODD), INVALID),                      # not 16-byte aligned
+    (dict(B=0, q=None, k=None, v=None, o=None), OK),  # empty problem: no-op
+    (dict(Sq=0), OK),
+])
+def test_fwd_validation(lib, kw, status):
+    assert fwd(lib, **kw) == status
+    if status != OK:
+        assert len(lib.attn_last_error()) > 0
+
+
+def test_null_stride_array(lib):
+    assert lib.attn_fwd(0, A16, None, A16, GOOD, A16, GOOD, A16, GOOD, None, 1, 1, 1, 1, 128, 0.1, 0, None) == INVALID
+
+
+def test_quantize_validation(lib):
+    q = lambda **k: lib.attn_fp8_quantize(k.get("x", A16), k.get("xs", GOOD), k.get("x8", A16), k.get("sc", A16),
+                                          k.get("B", 1), k.get("H", 1), k.get("S", 1), k.get("D", 128),
+                                          k.get("br", 128), None, None)
+    assert q(br=64) == INVALID
+    assert q(D=96) == UNSUPPORTED
+    assert q(x=None) == INVALID
+    assert q(sc=None) == INVALID
+    assert q(S=-1) == INVALID
+    assert q(S=0) == OK
+
+
+def test_fp8_fwd_validation(lib):
+    f = lambda **k: lib.attn_fwd_fp8(A16, A16, A16, A16, A16, A16, k.get("br", 128), A16, None, 1, 1, 1, 1,
+                                     k.get("D", 128), k.get("scale", 0.1), k.get("causal", 0), None)
+    assert f(D=64) == UNSUPPORTED
+    assert f(D=-1) == INVALID
+    assert f(br=7) == INVALID
+    assert f(scale=-1.0) == INVALID
+    assert f(causal=5) == INVALID
+
+
+def test_varlen_validation(lib):
+    def f(page=64, table=A16, maxp=4, maxk=200, D=128, B=2, total_q=10):
+        return lib.attn_fwd_varlen(0, A16, A16, A16, A16, A16, table, maxp, page, A16, None, B, 2, D, total_q, 100,
+                                   maxk, 0.1, 1, None)
+    assert f(page=48) == INVALID        # not a power of two
+    assert f(page=8) == INVALID         # below 16
+    assert f(maxp=3, maxk=200) == INVALID  # 3 pages of 64 cannot hold 200 keys
+    assert f(maxp=0) == INVALID
+    assert f(D=80) == UNSUPPORTED
+    assert f(B=0) == OK
+    assert f(total_q=0) == OK
+
+
+def test_status_strings(lib):
+    for code, name in ((0, b"ATTN_OK"), (1, b"ATTN_ERR_INVALID"), (2, b"ATTN_ERR_UNSUPPORTED"),
+                       (3, b"ATTN_ERR_HIP"), (99, b"ATTN_STATUS_UNKNOWN")):
+        assert lib.attn_status_string(code) == name
+
+
+def test_bench_refuses_several_gpus():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]

@@ -62,7 +62,7 @@ def test_fp16(lib, d, causal):
     q, k, v = (_f16_values(x) for x in W.qkv_normal(7 + d, (1, 190, 2, d), (1, 300, 2, d)))
     o, lse = _run(lib, q, k, v, causal, dtype="fp16")
     o_ref, lse_ref = OA.attention_bshd(q, k, v, 1 / math.sqrt(d), causal)
-    assert_close16(o, o_ref, lse, lse_ref, f"fp16 d{d} causal={causal}")
+    assert_close16(o, o_ref, lse, lse_ref, f"fp16 d{d} causal={causal}", dtype="fp16")
 
 
 def test_empty_key_set(lib):

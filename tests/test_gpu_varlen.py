@@ -1,0 +1,177 @@
+"""GPU tests of the packed variable-length and paged-KV forward (attn_fwd_varlen).
+
+Indexing is checked bit-exactly: a paged run equals the same packed run, a
+packed run equals per-sequence dense runs, Q = 0 turns every LSE into the log
+of the exact number of visible keys, and NaN poison in every byte the kernel
+must not read changes nothing.  Values are checked against the float64 oracle
+on seeded row samples of every sequence."""
+import math
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as OA
+from tests.parity import assert_close16, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import attention_attn_fwd_10_amd as A
+    return A
+
+
+def _pack(lens_q, lens_k, H, D, seed):
+    cu_q, cu_k = W.cu_seqlens(lens_q), W.cu_seqlens(lens_k)
+    rng = np.random.default_rng(seed)
+    q = W.normal_bf16(rng, (int(cu_q[-1]), H, D))
+    k = W.normal_bf16(rng, (int(cu_k[-1]), H, D))
+    v = W.normal_bf16(rng, (int(cu_k[-1]), H, D))
+    return q, k, v, cu_q, cu_k
+
+
+def _paginate(k, v, cu_k, lens_k, page, seed, poison=True):
+    table, npages = W.paged_layout(seed, lens_k, page)
+    H, D = k.shape[1:]
+    fill = np.nan if poison else 0.0
+    kp = np.full((npages, page, H, D), fill, dtype=np.float32)
+    vp = np.full((npages, page, H, D), fill, dtype=np.float32)
+    for b, n in enumerate(lens_k):
+        for t0 in range(0, n, page):
+            t1 = min(t0 + page, n)
+            phys = table[b, t0 // page]
+            kp[phys, :t1 - t0] = k[cu_k[b] + t0:cu_k[b] + t1]
+            vp[phys, :t1 - t0] = v[cu_k[b] + t0:cu_k[b] + t1]
+    return kp, vp, table
+
+
+def _t32(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
+
+
+def _run(lib, q, k, v, cu_q, cu_k, lens_q, lens_k, causal, table=None, page=0):
+    import torch
+    tq, tk, tv = to_dev(q), to_dev(k), to_dev(v)
+    o, lse = lib.fwd_varlen(tq, _t32(cu_q), tk, tv, _t32(cu_k), int(max(lens_q)), int(max(lens_k)),
+                            causal=causal, block_table=None if table is None else _t32(table), page_size=page)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _sample_rows_ref(q, k, v, cu_q, cu_k, lens_q, lens_k, causal, heads, seed, n_rand=6):
+    """float64 reference on a few rows of every sequence, for some heads."""
+    rng = np.random.default_rng(seed)
+    rows, o_ref, lse_ref = [], [], []
+    for b in range(len(lens_q)):
+        lq, lk = int(lens_q[b]), int(lens_k[b])
+        if lq == 0:
+            continue
+        rr = sorted(set([0, lq - 1, lq // 2] + list(rng.integers(0, lq, size=n_rand))))
+        kb = k[cu_k[b]:cu_k[b] + lk]
+        vb = v[cu_k[b]:cu_k[b] + lk]
+        for h in heads:
+            oo, ll = OA.naive_head(q[cu_q[b] + np.array(rr), h], kb[:, h], vb[:, h], 1 / math.sqrt(q.shape[2]),
+                                   causal, rows=np.array(rr), lq=lq)
+            for i, r in enumerate(rr):
+                rows.append((cu_q[b] + r, h))
+                o_ref.append(oo[i])
+                lse_ref.append(ll[i])
+    return rows, np.array(o_ref), np.array(lse_ref)
+
+
+def _gather(o, lse, rows):
+    on = o.float().cpu().numpy().astype(np.float64)
+    ln = lse.cpu().numpy().astype(np.float64)
+    return np.array([on[t, h] for t, h in rows]), np.array([ln[h, t] for t, h in rows])
+
+
+def test_varlen_paged_workload(lib):
+    """32 sequences, lengths U{128..4096}, 32 heads, d128, causal, 64-token
+    pages at randomly permuted slots (NaN in every unused slot)."""
+    import torch
+    cfg = W.VARLEN
+    lens = W.varlen_lengths(cfg["seed_lengths"], cfg["n_seq"], cfg["lo"], cfg["hi"])
+    q, k, v, cu_q, cu_k = _pack(lens, lens, cfg["heads"], cfg["head_dim"], cfg["seed_values"])
+    kp, vp, table = _paginate(k, v, cu_k, lens, cfg["page_size"], cfg["seed_pages"])
+    o_pg, lse_pg = _run(lib, q, kp, vp, cu_q, cu_k, lens, lens, True, table, cfg["page_size"])
+    o_pk, lse_pk = _run(lib, q, k, v, cu_q, cu_k, lens, lens, True)
+    # paged == packed, bit for bit
+    assert torch.equal(o_pg, o_pk) and torch.equal(lse_pg, lse_pk)
+    rows, o_ref, lse_ref = _sample_rows_ref(q, k, v, cu_q, cu_k, lens, lens, True, heads=[0, 17, 31], seed=9)
+    og, lg = _gather(o_pg, lse_pg, rows)
+    assert_close16(og, o_ref, lg, lse_ref, "varlen+paged workload")
+
+
+@pytest.mark.parametrize("page", [16, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_equals_dense_per_sequence(lib, page, causal):
+    import torch
+    lens = np.array([1, 130, 0, 77, 64, 300, 129], dtype=np.int64)
+    H, D = 3, 128
+    q, k, v, cu_q, cu_k = _pack(lens, lens, H, D, 5)
+    o_pk, lse_pk = _run(lib, q, k, v, cu_q, cu_k, lens, lens, causal)
+    kp, vp, table = _paginate(k, v, cu_k, lens, page, 8)
+    o_pg, lse_pg = _run(lib, q, kp, vp, cu_q, cu_k, lens, lens, causal, table, page)
+    assert torch.equal(o_pg, o_pk) and torch.equal(lse_pg, lse_pk)
+    for b, n in enumerate(lens):
+        if n == 0:
+            continue
+        sl = slice(int(cu_q[b]), int(cu_q[b + 1]))
+        od, ld = lib.fwd(to_dev(q[None, sl]), to_dev(k[None, sl]), to_dev(v[None, sl]), causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(od[0], o_pk[sl]), b
+        assert torch.equal(ld[0], lse_pk[:, sl]), b
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_different_query_and_key_lengths(lib, causal):
+    # decode-like rows (Lq << Lk), Lq > Lk (bottom-right causal leaves rows empty), empty sequences
+    lens_q = np.array([1, 5, 200, 0, 64, 3], dtype=np.int64)
+    lens_k = np.array([500, 64, 100, 10, 0, 300], dtype=np.int64)
+    H, D = 2, 64
+    q, k, v, cu_q, cu_k = _pack(lens_q, lens_k, H, D, 12)
+    o, lse = _run(lib, q, k, v, cu_q, cu_k, lens_q, lens_k, causal)
+    o_ref, lse_ref = OA.attention_varlen(q, cu_q, k, v, cu_k, 1 / math.sqrt(D), causal)
+    assert_close16(o.float().cpu().numpy().astype(np.float64), o_ref,
+                   lse.cpu().numpy().astype(np.float64), lse_ref, f"varlen Lq!=Lk causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_query_counts_visible_keys(lib, causal):
+    """Q = 0: every visible key has probability 1/|A_i|, so exp(LSE_i) = |A_i|
+    exactly after rounding; this pins the causal and sequence-length masks."""
+    import torch
+    lens_q = np.array([1, 64, 65, 200, 7], dtype=np.int64)
+    lens_k = np.array([1, 64, 130, 200, 300], dtype=np.int64)
+    H, D = 2, 128
+    q, k, v, cu_q, cu_k = _pack(lens_q, lens_k, H, D, 13)
+    q[:] = 0.0
+    kp, vp, table = _paginate(k, v, cu_k, lens_k, 64, 14)
+    _, lse = _run(lib, q, kp, vp, cu_q, cu_k, lens_q, lens_k, causal, table, 64)
+    lse = lse.cpu().numpy().astype(np.float64)
+    for b in range(len(lens_q)):
+        cnt = OA.valid_key_counts(int(lens_q[b]), int(lens_k[b]), causal)
+        got = lse[:, cu_q[b]:cu_q[b + 1]]
+        want = np.broadcast_to(cnt, got.shape)
+        vis = want > 0
+        assert np.array_equal(np.rint(np.exp(got[vis])).astype(np.int64), want[vis]), b
+        assert np.all(np.isneginf(got[~vis])), b
+
+
+def test_poison_does_not_leak(lib):
+    import torch
+    lens = np.array([70, 129, 1], dtype=np.int64)
+    H, D = 2, 256
+    q, k, v, cu_q, cu_k = _pack(lens, lens, H, D, 15)
+    kp0, vp0, table = _paginate(k, v, cu_k, lens, 64, 16, poison=False)
+    kp1, vp1, _ = _paginate(k, v, cu_k, lens, 64, 16, poison=True)
+    o0, l0 = _run(lib, q, kp0, vp0, cu_q, cu_k, lens, lens, True, table, 64)
+    o1, l1 = _run(lib, q, kp1, vp1, cu_q, cu_k, lens, lens, True, table, 64)
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    assert not torch.isnan(o1.float()).any()

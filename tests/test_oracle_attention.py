@@ -204,3 +204,9 @@ def test_varlen_and_paged_match_dense():
     o2, lse2 = A.attention_varlen(q, cu, kp, vp, cu, 0.35, True, block_table=table, page_size=page)
     np.testing.assert_array_equal(o2, o)
     np.testing.assert_array_equal(lse2, lse)
+
+
+def test_half_ulp_helper():
+    from tests.parity import half_ulp
+    assert half_ulp(1.0) == 2.0 ** -8 and half_ulp(3.0) == 2.0 ** -7 and half_ulp(-5.0) == 2.0 ** -6
+    assert half_ulp(1.0, "fp16") == 2.0 ** -11
