@@ -94,6 +94,8 @@ hipError_t dispatch_fwd16(const attn::FwdArgs& a, int D, int dtype, bool causal,
 }
 
 constexpr int kBR = 128;  // query rows per workgroup of every forward kernel
+// K/V tiles are read through 32-bit buffer offsets: 64 rows of a tile must fit in 2^31 bytes
+constexpr int64_t kMaxSeqStride = int64_t(1) << 24;
 
 }  // namespace
 
@@ -128,6 +130,10 @@ attn_status_t attn_fwd(int dtype, const void* q, const int64_t q_strides[3], con
   if (B == 0 || H == 0 || Sq == 0) return ok();
   if (q == nullptr || o == nullptr) return fail(ATTN_ERR_INVALID, "q or o is NULL");
   if (Sk > 0 && (k == nullptr || v == nullptr)) return fail(ATTN_ERR_INVALID, "k or v is NULL");
+  if (Sk > 1 && (k_strides[1] < D || v_strides[1] < D))
+    return fail(ATTN_ERR_INVALID, "k/v sequence strides must be at least head_dim (rows may not overlap)");
+  if (k_strides[1] > kMaxSeqStride || v_strides[1] > kMaxSeqStride)
+    return fail(ATTN_ERR_UNSUPPORTED, "k/v sequence strides above 2^24 elements are not supported");
   if (!aligned16(q) || !aligned16(o) || !aligned16(k) || !aligned16(v) || !aligned16(lse))
     return fail(ATTN_ERR_INVALID, "q, k, v, o and lse must be 16-byte aligned");
   const int64_t n_qblk = (Sq + kBR - 1) / kBR;
@@ -169,6 +175,7 @@ attn_status_t attn_fwd_varlen(int dtype, const void* q, const int32_t* cu_seqlen
   if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return fail(ATTN_ERR_INVALID, "cu_seqlens is NULL");
   if (q == nullptr || o == nullptr) return fail(ATTN_ERR_INVALID, "q or o is NULL");
   if (max_seqlen_k > 0 && (k == nullptr || v == nullptr)) return fail(ATTN_ERR_INVALID, "k or v is NULL");
+  if ((int64_t)H * D > kMaxSeqStride) return fail(ATTN_ERR_UNSUPPORTED, "H * head_dim above 2^24 elements");
   if (!aligned16(q) || !aligned16(o) || !aligned16(k) || !aligned16(v) || !aligned16(lse))
     return fail(ATTN_ERR_INVALID, "q, k, v, o and lse must be 16-byte aligned");
   const int64_t n_qblk = (max_seqlen_q + kBR - 1) / kBR;

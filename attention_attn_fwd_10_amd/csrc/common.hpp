@@ -91,6 +91,22 @@ __device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
                                    (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
+// Buffer resource (V#) for raw byte-addressed buffer loads: base address and
+// size in bytes; loads at or past `nbytes` return zeros.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t p = (uint64_t)base;
+  return i32x4{(int)(uint32_t)p, (int)((uint32_t)(p >> 32) & 0xffffu), (int)nbytes, 0x00020000};
+}
+__device__ void raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) void* lds, int size, int voffset,
+                                    int soffset, int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+// Asynchronous buffer -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds):
+// lane l reads rsrc.base + voffset (zeros when out of range) and writes
+// lds_wave_base + 16*l; lds_wave_base must be the same for every lane.
+__device__ __forceinline__ void dma16_buf(i32x4 rsrc, uint32_t voffset, void* lds_wave_base) {
+  raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16, (int)voffset, 0, 0, 0);
+}
+
 // wait until every global load (including LDS DMA) issued by this wave is done
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

@@ -25,9 +25,10 @@
 //    than 2^8 (in probability units): between moves the probabilities are
 //    bounded by 256, the result is the same exact identity, and the output
 //    rescale (D/32 x 16 multiplies per lane) is skipped on almost every tile;
-//  * query rows past the sequence end are zero-filled; key rows past Lk are
-//    never read from memory (the copy repeats row Lk-1) and are masked, so
-//    whatever memory lies past the sequence never reaches the result.
+//  * tiles are copied with buffer loads whose range ends at the sequence's
+//    last key row: rows past Lk arrive as zeros without being read, and are
+//    masked; query rows past the sequence end are zero-filled, so whatever
+//    memory lies past the sequence never reaches the result.
 #pragma once
 
 #include "common.hpp"
@@ -68,7 +69,8 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
   uint16_t* const vs_base = smem + 2 * C::K_ELEMS;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
 
   // ---- work item: (b, h, query block) -------------------------------------
   const int t = xcd_remap(blockIdx.x, gridDim.x);
@@ -144,22 +146,21 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
     key_local = s / C::VSLOTS;
     chunk = s - key_local * C::VSLOTS;
   };
-  // element offsets of this lane's slots for full tiles of the dense/varlen layouts
-  int k_off[C::KI_W], v_off[C::VI_W];
-  uint32_t k_on = 0, v_on = 0;  // bit ii: this lane copies a real chunk in its ii-th copy
+  // byte offsets of this lane's slots inside a tile for the dense/varlen
+  // layouts (padding slots point out of range and read zeros)
+  constexpr uint32_t kOutOfRange = 0x7ffffff0u;
+  uint32_t k_boff[C::KI_W], v_boff[C::VI_W];
 #pragma unroll
   for (int ii = 0; ii < C::KI_W; ++ii) {
     int kl, ch;
     k_slot(ii, kl, ch);
-    k_off[ii] = kl * (int)a.k_ss + ch * 8;
-    if (wave + 4 * ii < C::KSLOTS && ch < CPR) k_on |= 1u << ii;
+    k_boff[ii] = ch < CPR ? 2u * (uint32_t)(kl * (int)a.k_ss + ch * 8) : kOutOfRange;
   }
 #pragma unroll
   for (int ii = 0; ii < C::VI_W; ++ii) {
     int kl, ch;
     v_slot(ii, kl, ch);
-    v_off[ii] = kl * (int)a.v_ss + ch * 8;
-    if (wave + 4 * ii < C::VSLOTS && ch < CPR) v_on |= 1u << ii;
+    v_boff[ii] = ch < CPR ? 2u * (uint32_t)(kl * (int)a.v_ss + ch * 8) : kOutOfRange;
   }
   auto row_of = [&](int key) -> int64_t {  // element offset of key's row (paged: through the table)
     if constexpr (MODE == kPaged) {
@@ -172,18 +173,24 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
   auto dma_tile = [&](int key0, int buf) {
     uint16_t* kb = ks_base + buf * C::K_ELEMS;
     uint16_t* vb = vs_base + buf * C::V_ELEMS;
-    if (MODE != kPaged && key0 + BC <= Lk) {
-      const uint16_t* k0p = kg + (int64_t)key0 * a.k_ss;
-      const uint16_t* v0p = vg + (int64_t)key0 * a.v_ss;
+    if constexpr (MODE != kPaged) {
+      // one buffer resource per tile covers rows key0 .. Lk-1: rows past the
+      // sequence end read as zeros, so every tile takes the same path
+      // (the range is clamped below 2^31; the host limits seq strides to 2^24
+      // elements, so a tile's 64 rows always lie inside it)
+      const uint64_t kn = 2ull * (uint64_t)(Lk - key0) * (uint64_t)a.k_ss;
+      const uint64_t vn = 2ull * (uint64_t)(Lk - key0) * (uint64_t)a.v_ss;
+      const i32x4 kr = make_rsrc(kg + (int64_t)key0 * a.k_ss, (uint32_t)min(kn, (uint64_t)0x7fff0000u));
+      const i32x4 vr = make_rsrc(vg + (int64_t)key0 * a.v_ss, (uint32_t)min(vn, (uint64_t)0x7fff0000u));
 #pragma unroll
       for (int ii = 0; ii < C::KI_W; ++ii)
-        if ((k_on >> ii) & 1u) dma16(k0p + k_off[ii], kb + (wave + 4 * ii) * 512);
+        if (wave + 4 * ii < C::KSLOTS) dma16_buf(kr, k_boff[ii], kb + (wave + 4 * ii) * 512);
 #pragma unroll
       for (int ii = 0; ii < C::VI_W; ++ii)
-        if ((v_on >> ii) & 1u) dma16(v0p + v_off[ii], vb + (wave + 4 * ii) * 512);
+        if (wave + 4 * ii < C::VSLOTS) dma16_buf(vr, v_boff[ii], vb + (wave + 4 * ii) * 512);
     } else {
-      // partial last tile or paged cache: rows past Lk repeat row Lk-1 (finite
-      // data, masked out of the scores and multiplied by p = 0)
+      // paged cache: each row through the block table; rows past Lk repeat
+      // row Lk-1 (finite data, masked out of the scores and multiplied by p = 0)
 #pragma unroll
       for (int ii = 0; ii < C::KI_W; ++ii) {
         const int i = wave + 4 * ii;

@@ -29,17 +29,54 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA
 PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 
+# sources of the timed kernel; the committed counter summary names their hash
+KERNEL_SOURCES = ("attention_attn_fwd_10_amd/csrc/fwd16.hpp", "attention_attn_fwd_10_amd/csrc/common.hpp",
+                  "attention_attn_fwd_10_amd/csrc/fwd16_d128.hip")
+TRAFFIC_PROFILE = "profiles/fwd16_d128_bf16_b4_h16_s8448.md"
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic():
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, scaled by the factors measured on a plain copy; None when the
+    summary was taken on other kernel sources."""
+    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.strip().startswith(("source_sha256", "fetch_kib", "write_kib", "fetch_scale",
+                                                     "write_scale")):
+            k, v = line.strip().strip("`").split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    try:
+        if vals.get("source_sha256") != kernel_source_hash():
+            return None
+        return (float(vals["fetch_kib_per_launch"]) * float(vals["fetch_scale"]) +
+                float(vals["write_kib_per_launch"]) * float(vals["write_scale"])) * 1024.0
+    except (KeyError, ValueError):
+        return None
+
 
 def parse():
     p = argparse.ArgumentParser(description=__doc__)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--causal", action="store_true", help="time the causal variant instead")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-fp8", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--sweep", action="store_true", help="also time the 16384-token seq sweep (extra output)")
+    p.add_argument("--source-hash", action="store_true", help="print the timed kernel's source hash and exit")
     p.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (calibrates the FETCH_SIZE/WRITE_SIZE counters)")
     return p.parse_args()
@@ -105,6 +142,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.source_hash:
+        print(kernel_source_hash())
+        return
     if args.copy_reference:
         copy_reference(args.copy_reference)
         return
@@ -149,7 +189,7 @@ def main():
                    "flop_convention": "4*B*H*Sq*Sk*D, halved for causal"},
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": counter_traffic(),
                      "kernel": "fwd16_kernel<128, bf16, non-causal, dense>",
                      "algorithmic_bytes": algo_bytes},
     }

@@ -62,7 +62,9 @@ typedef enum {
  * addressed as base + b*s[0] + i*s[1] + h*s[2] + d with s the stride triple.
  * lse: float32 [B, H, Sq] contiguous, or NULL to skip it.
  * D must be 64, 128 or 256 (ATTN_ERR_UNSUPPORTED otherwise); strides must be
- * multiples of 8 elements and pointers 16-byte aligned.
+ * multiples of 8 elements and pointers 16-byte aligned; the k and v sequence
+ * strides must be at least D (rows may not overlap) and at most 2^24 elements
+ * (ATTN_ERR_UNSUPPORTED above).
  * softmax_scale must be finite and > 0 (1/sqrt(D) is the usual choice).
  * causal: 0 or 1.
  */

@@ -88,6 +88,8 @@ def fwd(lib, dtype=0, q=A16, k=A16, v=A16, o=A16, lse=None, B=1, H=1, Sq=1, Sk=1
     (dict(q=None), INVALID),
     (dict(v=None), INVALID),
     (dict(o=A_ODD), INVALID),                      # not 16-byte aligned
+    (dict(Sk=4, ks=_s(1 << 20, 64, 128)), INVALID),  # k rows overlap (seq stride < D)
+    (dict(vs=_s(1 << 30, 1 << 25, 128)), UNSUPPORTED),  # seq stride above 2^24
     (dict(B=0, q=None, k=None, v=None, o=None), OK),  # empty problem: no-op
     (dict(Sq=0), OK),
 ])
