@@ -60,14 +60,15 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const uint8_t* p) {
 }
 
 template <bool CAUSAL>
-__global__ void __launch_bounds__(256, 2) fwd_fp8_kernel(Fp8Args a) {
+__global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
   using namespace fp8cfg;
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_BYTES];
   uint8_t* const ks_base = smem;
   uint8_t* const vs_base = smem + 2 * TILE_BYTES;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
 
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = t / a.n_qblk;
@@ -123,40 +124,32 @@ __global__ void __launch_bounds__(256, 2) fwd_fp8_kernel(Fp8Args a) {
   };
   const uint8_t* const kg = a.k + koff;
   const uint8_t* const vg = a.v + koff;
-  int k_off[I_W], v_off[I_W];
-  int k_key[I_W], v_key[I_W], chunk[I_W];
-  uint32_t on = 0;
+  // byte offsets of this lane's slots inside a tile (padding slots point out of
+  // range and read zeros)
+  constexpr uint32_t kOutOfRange = 0x7ffffff0u;
+  uint32_t k_boff[I_W], v_boff[I_W];
 #pragma unroll
   for (int ii = 0; ii < I_W; ++ii) {
     const int s = 64 * (wave + 4 * ii) + lane;
     const int R = s / SLOTS, c = s - R * SLOTS;
-    k_key[ii] = k_row_key(R);
-    v_key[ii] = R;
-    chunk[ii] = c;
-    k_off[ii] = k_key[ii] * (int)row_q + 16 * c;
-    v_off[ii] = R * (int)row_q + 16 * c;
-    if (wave + 4 * ii < SLOTS && c < SLOTS - 1) on |= 1u << ii;
+    k_boff[ii] = c < SLOTS - 1 ? (uint32_t)(k_row_key(R) * (int)row_q + 16 * c) : kOutOfRange;
+    v_boff[ii] = c < SLOTS - 1 ? (uint32_t)(R * (int)row_q + 16 * c) : kOutOfRange;
   }
+  // one buffer resource per tile covers rows key0 .. Lk-1: rows past the
+  // sequence end read as zeros
   auto dma_tile = [&](int key0, int buf) {
     uint8_t* kb = ks_base + buf * TILE_BYTES;
     uint8_t* vb = vs_base + buf * TILE_BYTES;
-    if (key0 + BC <= Lk) {
-      const uint8_t* k0p = kg + (int64_t)key0 * row_q;
+    const uint64_t n = (uint64_t)(Lk - key0) * (uint64_t)row_q;
+    const uint32_t nb = (uint32_t)min(n, (uint64_t)0x7fff0000u);
+    const i32x4 kr = make_rsrc(kg + (int64_t)key0 * row_q, nb);
+    const i32x4 vr = make_rsrc(vg + (int64_t)key0 * row_q, nb);
 #pragma unroll
-      for (int ii = 0; ii < I_W; ++ii)
-        if ((on >> ii) & 1u) dma16(k0p + k_off[ii], kb + (wave + 4 * ii) * 1024);
-#pragma unroll
-      for (int ii = 0; ii < I_W; ++ii)
-        if ((on >> ii) & 1u) dma16(vg + (int64_t)key0 * row_q + v_off[ii], vb + (wave + 4 * ii) * 1024);
-    } else {
-      // rows past Lk repeat row Lk-1 (finite data; masked scores, p = 0)
-#pragma unroll
-      for (int ii = 0; ii < I_W; ++ii)
-        if ((on >> ii) & 1u) {
-          dma16(kg + (int64_t)min(key0 + k_key[ii], Lk - 1) * row_q + 16 * chunk[ii], kb + (wave + 4 * ii) * 1024);
-          dma16(vg + (int64_t)min(key0 + v_key[ii], Lk - 1) * row_q + 16 * chunk[ii], vb + (wave + 4 * ii) * 1024);
-        }
-    }
+    for (int ii = 0; ii < I_W; ++ii)
+      if (wave + 4 * ii < SLOTS) {
+        dma16_buf(kr, k_boff[ii], kb + (wave + 4 * ii) * 1024);
+        dma16_buf(vr, v_boff[ii], vb + (wave + 4 * ii) * 1024);
+      }
   };
 
   // V^T operand: lane (group g, index j) addresses row 32(g/2) + 8u + j/2 and
