@@ -247,12 +247,15 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
 #pragma unroll
         for (int tt = 0; tt < BC / 32; ++tt) kop[tt][kk] = *(const u32x4*)(ks + tt * 32 * KP + 16 * kk);
       __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the first MFMA
+      __builtin_amdgcn_s_setprio(1);       // favour this wave while it feeds the matrix core
 #pragma unroll
       for (int tt = 0; tt < BC / 32; ++tt) s[tt] = mfma32<DT>(kop[tt][0], qf[0], zero16);
 #pragma unroll
       for (int kk = 1; kk < NKK; ++kk)
 #pragma unroll
         for (int tt = 0; tt < BC / 32; ++tt) s[tt] = mfma32<DT>(kop[tt][kk], qf[kk], s[tt]);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
     }
     // register r of tile tt holds key key0 + 32tt + 16(r/8) + 8hh + r%8
     const bool need_mask = (key0 + BC > Lk) || (CAUSAL && key0 + BC - 1 > qw + diag);
