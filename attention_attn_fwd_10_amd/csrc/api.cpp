@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -17,6 +18,8 @@
 namespace attn {
 template <int D, int DT, bool CAUSAL, int MODE>
 hipError_t launch_fwd16(const FwdArgs& a, hipStream_t s);
+template <int D, int DT, bool CAUSAL, int MODE>
+hipError_t launch_fwd16pp(FwdArgs a, hipStream_t s);
 hipError_t launch_fp8_quantize(const QuantArgs& a, int D, hipStream_t s);
 hipError_t launch_fwd_fp8(const Fp8Args& a, int D, bool causal, hipStream_t s);
 }  // namespace attn
@@ -72,14 +75,34 @@ attn_status_t check_head_dim(int D) {
   return ATTN_OK;
 }
 
+// Schedule of the 16-bit kernels for head_dim 64/128: "pairs" (4 waves, two
+// independent workgroups per CU; the default, measured faster) or "pingpong"
+// (8 waves, two groups alternating matrix and softmax phases).  Read once from
+// ATTN_FWD16_SCHEDULE; head_dim 256 always uses the 4-wave kernel.
+bool use_pingpong() {
+  static const bool pp = [] {
+    const char* e = std::getenv("ATTN_FWD16_SCHEDULE");
+    return e != nullptr && std::strcmp(e, "pingpong") == 0;
+  }();
+  return pp;
+}
+
+template <int D, int DT, bool CAUSAL, int MODE>
+hipError_t launch_one(const attn::FwdArgs& a, hipStream_t s) {
+  if constexpr (D <= 128) {
+    if (use_pingpong()) return attn::launch_fwd16pp<D, DT, CAUSAL, MODE>(a, s);
+  }
+  return attn::launch_fwd16<D, DT, CAUSAL, MODE>(a, s);
+}
+
 template <int D, int DT>
 hipError_t dispatch_causal_mode(const attn::FwdArgs& a, bool causal, int mode, hipStream_t s) {
   using namespace attn;
   if (mode == kDense)
-    return causal ? launch_fwd16<D, DT, true, kDense>(a, s) : launch_fwd16<D, DT, false, kDense>(a, s);
+    return causal ? launch_one<D, DT, true, kDense>(a, s) : launch_one<D, DT, false, kDense>(a, s);
   if (mode == kVarlen)
-    return causal ? launch_fwd16<D, DT, true, kVarlen>(a, s) : launch_fwd16<D, DT, false, kVarlen>(a, s);
-  return causal ? launch_fwd16<D, DT, true, kPaged>(a, s) : launch_fwd16<D, DT, false, kPaged>(a, s);
+    return causal ? launch_one<D, DT, true, kVarlen>(a, s) : launch_one<D, DT, false, kVarlen>(a, s);
+  return causal ? launch_one<D, DT, true, kPaged>(a, s) : launch_one<D, DT, false, kPaged>(a, s);
 }
 
 hipError_t dispatch_fwd16(const attn::FwdArgs& a, int D, int dtype, bool causal, int mode, hipStream_t s) {

@@ -1,6 +1,7 @@
-// Instantiations of the 16-bit forward kernel for head_dim 128.
-#include "fwd16.hpp"
+// Instantiations of the 16-bit forward kernels for head_dim 128.
+#include "fwd16_pp.hpp"
 
 namespace attn {
 ATTN_INSTANTIATE_FWD16(128)
+ATTN_INSTANTIATE_FWD16PP(128)
 }  // namespace attn
