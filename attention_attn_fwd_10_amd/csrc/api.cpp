@@ -202,7 +202,8 @@ attn_status_t attn_fwd_varlen(int dtype, const void* q, const int32_t* cu_seqlen
   if (!aligned16(q) || !aligned16(o) || !aligned16(k) || !aligned16(v) || !aligned16(lse))
     return fail(ATTN_ERR_INVALID, "q, k, v, o and lse must be 16-byte aligned");
   const int64_t n_qblk = (max_seqlen_q + kBR - 1) / kBR;
-  if ((int64_t)B * H * n_qblk > INT32_MAX) return fail(ATTN_ERR_INVALID, "problem too large for one launch");
+  if ((int64_t)B * H * n_qblk > INT32_MAX || (int64_t)H * ((total_q + kBR - 1) / kBR + B) > INT32_MAX)
+    return fail(ATTN_ERR_INVALID, "problem too large for one launch");
 
   attn::FwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;

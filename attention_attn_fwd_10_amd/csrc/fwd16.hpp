@@ -74,10 +74,27 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
 
   // ---- work item: (b, h, query block) -------------------------------------
   const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = t / a.n_qblk;
-  int qblk = t - bh * a.n_qblk;
-  if (CAUSAL) qblk = a.n_qblk - 1 - qblk;  // longest key ranges first
-  const int b = bh / a.H, h = bh - b * a.H;
+  int b, h, qblk;
+  if constexpr (MODE == kDense) {
+    const int bh = t / a.n_qblk;
+    qblk = t - bh * a.n_qblk;
+    if (CAUSAL) qblk = a.n_qblk - 1 - qblk;  // longest key ranges first
+    b = bh / a.H;
+    h = bh - b * a.H;
+  } else {
+    // compact tile list: sequence b owns H * ceil(Lq_b / BR) consecutive tiles
+    // (head-major), so no workgroup is spent on query blocks past a sequence
+    int rem = t, nq = 0;
+    for (b = 0; b < a.B; ++b) {
+      nq = (a.cu_q[b + 1] - a.cu_q[b] + BR - 1) / BR;
+      if (rem < a.H * nq) break;
+      rem -= a.H * nq;
+    }
+    if (b == a.B) return;  // past the last tile (the grid is an upper bound)
+    h = rem / nq;
+    qblk = rem - h * nq;
+    if (CAUSAL) qblk = nq - 1 - qblk;
+  }
 
   int Lq, Lk;
   int64_t qoff, ooff, koff, voff, lse_base;
@@ -173,15 +190,23 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
   auto dma_tile = [&](int key0, int buf) {
     uint16_t* kb = ks_base + buf * C::K_ELEMS;
     uint16_t* vb = vs_base + buf * C::V_ELEMS;
-    if constexpr (MODE != kPaged) {
-      // one buffer resource per tile covers rows key0 .. Lk-1: rows past the
-      // sequence end read as zeros, so every tile takes the same path
+    // A 64-key tile is contiguous in memory for the dense and varlen layouts,
+    // and inside one page of a paged cache whose pages hold >= 64 tokens.  Then
+    // one buffer resource per tile covers rows key0 .. Lk-1 (rows past the
+    // sequence end read as zeros) and every copy is a single buffer load.
+    const bool contiguous = MODE != kPaged || a.page_shift >= 6;
+    if (contiguous) {
+      int64_t row0 = key0;  // element row of key0 (paged: page base + slot)
+      if constexpr (MODE == kPaged) {
+        const int page = a.block_table[(int64_t)b * a.max_pages + (key0 >> a.page_shift)];
+        row0 = ((int64_t)page << a.page_shift) + (key0 & ((1 << a.page_shift) - 1));
+      }
       // (the range is clamped below 2^31; the host limits seq strides to 2^24
       // elements, so a tile's 64 rows always lie inside it)
       const uint64_t kn = 2ull * (uint64_t)(Lk - key0) * (uint64_t)a.k_ss;
       const uint64_t vn = 2ull * (uint64_t)(Lk - key0) * (uint64_t)a.v_ss;
-      const i32x4 kr = make_rsrc(kg + (int64_t)key0 * a.k_ss, (uint32_t)min(kn, (uint64_t)0x7fff0000u));
-      const i32x4 vr = make_rsrc(vg + (int64_t)key0 * a.v_ss, (uint32_t)min(vn, (uint64_t)0x7fff0000u));
+      const i32x4 kr = make_rsrc(kg + row0 * a.k_ss, (uint32_t)min(kn, (uint64_t)0x7fff0000u));
+      const i32x4 vr = make_rsrc(vg + row0 * a.v_ss, (uint32_t)min(vn, (uint64_t)0x7fff0000u));
 #pragma unroll
       for (int ii = 0; ii < C::KI_W; ++ii)
         if (wave + 4 * ii < C::KSLOTS) dma16_buf(kr, k_boff[ii], kb + (wave + 4 * ii) * 512);
@@ -189,8 +214,9 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
       for (int ii = 0; ii < C::VI_W; ++ii)
         if (wave + 4 * ii < C::VSLOTS) dma16_buf(vr, v_boff[ii], vb + (wave + 4 * ii) * 512);
     } else {
-      // paged cache: each row through the block table; rows past Lk repeat
-      // row Lk-1 (finite data, masked out of the scores and multiplied by p = 0)
+      // pages of 16 or 32 tokens: each row through the block table; rows past
+      // Lk repeat row Lk-1 (finite data, masked out of the scores and
+      // multiplied by p = 0)
 #pragma unroll
       for (int ii = 0; ii < C::KI_W; ++ii) {
         const int i = wave + 4 * ii;
@@ -349,7 +375,9 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
 
 template <int D, int DT, bool CAUSAL, int MODE>
 hipError_t launch_fwd16(const FwdArgs& a, hipStream_t s) {
-  const int n = a.B * a.H * a.n_qblk;
+  // dense: every (b, h, q-block); varlen: an upper bound on the compact tile list
+  const int n = MODE == kDense ? a.B * a.H * a.n_qblk
+                               : a.H * ((a.total_q + Fwd16Cfg<D>::BR - 1) / Fwd16Cfg<D>::BR + a.B);
   hipLaunchKernelGGL((fwd16_kernel<D, DT, CAUSAL, MODE>), dim3(n), dim3(256), 0, s, a);
   return hipGetLastError();
 }

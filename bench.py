@@ -235,18 +235,47 @@ def bench_fp8(A, W, args):
 
 
 def bench_sweep(A, W, args):
+    """The 16384-token sequence sweep and the varlen/paged workload (extra
+    lines; inputs drawn on the device from the same seeds)."""
     import torch
     out = []
     for w in W.seq_sweep_points():
         qs, ks = w.shapes()
         g = torch.Generator(device="cuda").manual_seed(w.seed)
         q, k, v = (torch.randn(qs, generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
-        ms = time_launches(lambda: A.fwd(q, k, v, w.scale, w.causal), max(3, args.steps // 4), 2)
+        ms = time_launches(lambda: A.fwd(q, k, v, w.scale, w.causal), max(5, args.steps // 3), 10)
         tf = w.flops / (ms * 1e-3) / 1e12
         byts = 4 * q.numel() * 2 + 4 * w.batch * w.heads * w.seq_q
         out.append({"workload": w.name, "ms": round(ms, 4), "tflops": round(tf, 1),
                     "gbs": round(byts / (ms * 1e-3) / 1e9, 1)})
         print(f"[bench] {w.name}: {ms:.3f} ms {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    # varlen + paged: 32 sequences U{128..4096}, 32 heads, d128, causal, 64-token pages
+    cfg = W.VARLEN
+    lens = W.varlen_lengths(cfg["seed_lengths"], cfg["n_seq"], cfg["lo"], cfg["hi"])
+    H, D, page = cfg["heads"], cfg["head_dim"], cfg["page_size"]
+    cu = torch.from_numpy(W.cu_seqlens(lens)).cuda()
+    tot = int(lens.sum())
+    g = torch.Generator(device="cuda").manual_seed(cfg["seed_values"])
+    q, k, v = (torch.randn((tot, H, D), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+    table, npages = W.paged_layout(cfg["seed_pages"], lens, page)
+    kp = torch.zeros((npages, page, H, D), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros_like(kp)
+    cuh = W.cu_seqlens(lens)
+    for b, n in enumerate(lens):
+        for t0 in range(0, int(n), page):
+            t1 = min(t0 + page, int(n))
+            kp[table[b, t0 // page], :t1 - t0] = k[cuh[b] + t0:cuh[b] + t1]
+            vp[table[b, t0 // page], :t1 - t0] = v[cuh[b] + t0:cuh[b] + t1]
+    tab = torch.from_numpy(table).cuda()
+    flops = sum(4.0 * H * int(n) * int(n) * D / 2 for n in lens)
+    mx = int(lens.max())
+    for name, kk, vv, bt in (("varlen_packed", k, v, None), ("varlen_paged64", kp, vp, tab)):
+        ms = time_launches(lambda: A.fwd_varlen(q, cu, kk, vv, cu, mx, mx, None, True, block_table=bt,
+                                                page_size=page if bt is not None else 0),
+                           max(5, args.steps // 3), 10)
+        tf = flops / (ms * 1e-3) / 1e12
+        out.append({"workload": f"{name}_32seq_h32_d128_causal", "ms": round(ms, 4), "tflops": round(tf, 1)})
+        print(f"[bench] {name}: {ms:.3f} ms {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
     return out
 
 
