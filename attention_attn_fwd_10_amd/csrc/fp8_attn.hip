@@ -165,7 +165,7 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
   float m_run = -INFINITY;  // running max of the log2-domain scores (lazy)
   float l_run = 0.f;        // this half-wave's share of sum p * 2^kMu (float32 terms)
-  float lq_run = 0.f;       // the same sum over the e4m3-rounded terms
+  float lq_run = 0.f;       // sum over all 64 keys of the e4m3-rounded terms (full row, both halves)
   float sv_ref = 0.f;       // V scale the accumulator is expressed in
   const f32x16 zero16 = {};
 
@@ -235,7 +235,7 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
     // the row sum adds the e4m3-rounded probabilities, exactly the values the
     // MFMA multiplies, so numerator and denominator share the rounding
     // (the logsumexp keeps the float32 sum)
-    float psum = 0.f, qsum = 0.f;
+    float psum = 0.f;
     uint32_t pw[8];
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
@@ -247,13 +247,18 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
         psum += p[e];
       }
       pw[w] = cvt_pk_fp8<true>(p[2], p[3], cvt_pk_fp8<false>(p[0], p[1], 0u));
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], false);
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[w], true);
-      qsum += (lo[0] + lo[1]) + (hi[0] + hi[1]);
     }
     l_run += psum * inv_vratio;
-    lq_run += qsum * inv_vratio;
     const i32x8 pk = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
+    // the sum of the e4m3-rounded probabilities of all 64 keys, on the matrix
+    // core: an all-ones (e4m3 1.0) A operand turns every output row into the
+    // column sums of P^T, exact in float32
+    {
+      const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                          0x38383838, 0x38383838, 0x38383838, 0x38383838};
+      const f32x16 qs = mfma32_fp8(ones, pk, zero16);
+      lq_run += qs[0] * inv_vratio;
+    }
     // O^T += V^T P^T (64 keys per MFMA)
     const uint8_t* vs = vs_base + buf * TILE_BYTES + vtr_off;
 #pragma unroll
@@ -282,7 +287,7 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
 
   // epilogue: O = sv_ref * O_acc / lq', lse = ln2 * (m - kMu + log2 l')
   const float l_tot = halfwave_sum(l_run);
-  const float lq_tot = halfwave_sum(lq_run);
+  const float lq_tot = lq_run;  // already the full row sum
   if (qi < Lq) {
     const float inv = lq_tot > 0.f ? sv_ref / lq_tot : 0.f;
     uint16_t* op = (uint16_t*)a.o + ((int64_t)b * Lq + qi) * a.H * D + (int64_t)h * D + 4 * hh;
