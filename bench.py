@@ -53,9 +53,9 @@ def counter_traffic():
         return None
     vals = {}
     for line in open(path):
-        if ":" in line and line.strip().startswith(("source_sha256", "fetch_kib", "write_kib", "fetch_scale",
-                                                     "write_scale")):
-            k, v = line.strip().strip("`").split(":", 1)
+        line = line.strip().lstrip("-").strip()
+        if ":" in line and line.startswith(("source_sha256", "fetch_kib", "write_kib", "fetch_scale", "write_scale")):
+            k, v = line.split(":", 1)
             vals[k.strip()] = v.strip().strip("`")
     try:
         if vals.get("source_sha256") != kernel_source_hash():
