@@ -59,12 +59,28 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// max of three floats as one v_max3_f32 (the scores are never signalling NaNs,
+// so the quieting that fmaxf adds around its operands is not needed)
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+template <int N>
+using C = std::integral_constant<int, N>;
+
 template <bool CAUSAL>
 __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
   using namespace fp8cfg;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE_BYTES];
-  uint8_t* const ks_base = smem;
-  uint8_t* const vs_base = smem + 2 * TILE_BYTES;
+  // two-slot rings (tile j in slot j % 2) as four separate arrays, addressed
+  // with compile-time slot numbers: the compiler then sees that a tile's LDS
+  // reads never touch the slot the next tile is being copied into, and does
+  // not make them wait for that copy
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v1[TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
@@ -97,8 +113,11 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
   const bool blocked = a.block_rows != 0;
   const int nbq = (Lq + 127) / 128, nbk = (Lk + 127) / 128;
   const float sq = blocked ? a.qs[(int64_t)bh * nbq + qblk] : a.qs[0];
-  const float* const ks_scale = blocked ? a.ks + (int64_t)bh * nbk : a.ks;
-  const float* const vs_scale = blocked ? a.vs + (int64_t)bh * nbk : a.vs;
+  // (read through the constant address space: the kernel never writes them,
+  // so the uniform per-tile reads become scalar loads)
+  typedef const __attribute__((address_space(4))) float cfloat;
+  cfloat* const ks_scale = (cfloat*)(blocked ? a.ks + (int64_t)bh * nbk : a.ks);
+  cfloat* const vs_scale = (cfloat*)(blocked ? a.vs + (int64_t)bh * nbk : a.vs);
   const float qk_scale = sq * a.scale_log2;
 
   // Q fragments: lane (query l32, half hh) holds q[64kk + 32hh .. +31]
@@ -137,9 +156,9 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
   }
   // one buffer resource per tile covers rows key0 .. Lk-1: rows past the
   // sequence end read as zeros
-  auto dma_tile = [&](int key0, int buf) {
-    uint8_t* kb = ks_base + buf * TILE_BYTES;
-    uint8_t* vb = vs_base + buf * TILE_BYTES;
+  auto dma_tile = [&](int key0, auto buf) {
+    uint8_t* kb = decltype(buf)::value ? lds_k1 : lds_k0;
+    uint8_t* vb = decltype(buf)::value ? lds_v1 : lds_v0;
     const uint64_t n = (uint64_t)(Lk - key0) * (uint64_t)row_q;
     const uint32_t nb = (uint32_t)min(n, (uint64_t)0x7fff0000u);
     const i32x4 kr = make_rsrc(kg + (int64_t)key0 * row_q, nb);
@@ -168,15 +187,20 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
   float lq_run = 0.f;       // sum over all 64 keys of the e4m3-rounded terms (full row, both halves)
   float sv_ref = 0.f;       // V scale the accumulator is expressed in
   const f32x16 zero16 = {};
+  // e4m3 1.0 in every byte; kept in registers across the key loop
+  i32x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;
+  asm volatile("" : "+v"(ones));
 
-  auto compute = [&](int j, int buf) {
+  auto compute = [&](int j, auto buf) {
     const int key0 = j * BC;
     if (!wave_active) return;
     if (CAUSAL && key0 > wave_last_key) return;
     const float c2 = qk_scale * ks_scale[blocked ? key0 >> 7 : 0];
     const float sv = vs_scale[blocked ? key0 >> 7 : 0];
     // S^T = K Q^T: two 32-key tiles, two 64-wide k steps each
-    const uint8_t* ks = ks_base + buf * TILE_BYTES + l32 * PITCH + 32 * hh;
+    const uint8_t* ks = (decltype(buf)::value ? lds_k1 : lds_k0) + l32 * PITCH + 32 * hh;
     i32x8 kop[2][2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -204,13 +228,13 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
     }
     float mx = s[0][0];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tt][r]);
-    const float mxs = halfwave_max(mx) * c2;
+    for (int i = 1; i < 31; i += 2) mx = max3(mx, s[i >> 4][i & 15], s[(i + 1) >> 4][(i + 1) & 15]);
+    mx = max3(mx, s[1][15], s[1][15]);
+    const auto mxw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    const float mxs = max3(mx, __uint_as_float(mxw[0]), __uint_as_float(mxw[1])) * c2;
     // a larger V block scale becomes the accumulator's reference (uniform branch)
     if (sv > sv_ref) {
-      const float ratio = sv_ref / sv;
+      const float ratio = sv_ref * __builtin_amdgcn_rcpf(sv);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -229,8 +253,9 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
       m_run = m_new;
     }
     // p'' = 2^(c2 s - m + kMu) * sv / sv_ref is what enters the MFMA; the sum
-    // keeps p' = p'' * sv_ref / sv
-    const float vratio = sv / sv_ref, inv_vratio = sv_ref / sv;
+    // keeps p' = p'' * sv_ref / sv (approximate reciprocals: both factors only
+    // need to be consistent to float precision)
+    const float vratio = sv * __builtin_amdgcn_rcpf(sv_ref), inv_vratio = sv_ref * __builtin_amdgcn_rcpf(sv);
     const float bias = m_run == -INFINITY ? 0.f : kMu + __log2f(vratio) - m_run;
     // the row sum adds the e4m3-rounded probabilities, exactly the values the
     // MFMA multiplies, so numerator and denominator share the rounding
@@ -246,21 +271,14 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
         p[e] = fast_exp2(fmaf(s[tt][r0 + e], c2, bias));
         psum += p[e];
       }
-      pw[w] = cvt_pk_fp8<true>(p[2], p[3], cvt_pk_fp8<false>(p[0], p[1], 0u));
+      // (the untouched half of the first conversion's destination is
+      // overwritten by the second, so any register serves as its old value)
+      pw[w] = cvt_pk_fp8<true>(p[2], p[3], cvt_pk_fp8<false>(p[0], p[1], __float_as_uint(p[0])));
     }
     l_run += psum * inv_vratio;
     const i32x8 pk = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
-    // the sum of the e4m3-rounded probabilities of all 64 keys, on the matrix
-    // core: an all-ones (e4m3 1.0) A operand turns every output row into the
-    // column sums of P^T, exact in float32
-    {
-      const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                          0x38383838, 0x38383838, 0x38383838, 0x38383838};
-      const f32x16 qs = mfma32_fp8(ones, pk, zero16);
-      lq_run += qs[0] * inv_vratio;
-    }
     // O^T += V^T P^T (64 keys per MFMA)
-    const uint8_t* vs = vs_base + buf * TILE_BYTES + vtr_off;
+    const uint8_t* vs = (decltype(buf)::value ? lds_v1 : lds_v0) + vtr_off;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
       u32x2 r[4];
@@ -270,18 +288,29 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
                          (int)r[2][0], (int)r[2][1], (int)r[3][0], (int)r[3][1]};
       oacc[dt] = mfma32_fp8(vop, pk, oacc[dt]);
     }
+    // the sum of the e4m3-rounded probabilities of all 64 keys, on the matrix
+    // core: an all-ones (e4m3 1.0) A operand turns every output row into the
+    // column sums of P^T, exact in float32
+    const f32x16 qs = mfma32_fp8(ones, pk, zero16);
+    lq_run += qs[0] * inv_vratio;
   };
 
   if (n_kv > 0) {
-    dma_tile(0, 0);
+    dma_tile(0, C<0>{});
     wait_vmem();
     __syncthreads();
-    for (int j = 0; j < n_kv; ++j) {
-      const int buf = j & 1;
-      if (j + 1 < n_kv) dma_tile((j + 1) * BC, buf ^ 1);
-      compute(j, buf);
+    // two tiles per iteration, so that every slot number is a constant
+    for (int j = 0; j < n_kv; j += 2) {
+      if (j + 1 < n_kv) dma_tile((j + 1) * BC, C<1>{});
+      compute(j, C<0>{});
       wait_vmem();
       __syncthreads();
+      if (j + 1 < n_kv) {
+        if (j + 2 < n_kv) dma_tile((j + 2) * BC, C<0>{});
+        compute(j + 1, C<1>{});
+        wait_vmem();
+        __syncthreads();
+      }
     }
   }
 
