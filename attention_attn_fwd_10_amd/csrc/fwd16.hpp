@@ -256,6 +256,15 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
   float l_run = 0.f;        // this half-wave's share of the running sum
   const float c2 = a.scale_log2;
   const f32x16 zero16 = {};
+  if constexpr (D == 256) {
+    // At D = 256 the registers exceed the 256 VGPRs; an AGPR operand here makes
+    // the compiler select the MFMA forms whose accumulators live in AGPRs, so
+    // the 128 output accumulators stay there instead of being copied between
+    // the two register files every tile.
+    int agpr_hint;
+    asm volatile("v_accvgpr_write_b32 %0, 0" : "=a"(agpr_hint));
+    (void)agpr_hint;
+  }
 
   auto compute = [&](int key0, int buf) {
     if (!wave_active) return;
@@ -264,24 +273,29 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
     const uint16_t* ks = ks_base + buf * C::K_ELEMS + l32 * KP + 8 * hh;
     f32x16 s[BC / 32];
     {
-      // all K operands of the tile are read before the first MFMA so that the
-      // LDS latency is paid once; the two score tiles form independent chains
+      // the K operands of the tile are read before the first MFMA so that the
+      // LDS latency is paid once (at D = 256 in two halves, which keeps them
+      // within the register budget); the two score tiles form independent
+      // chains
       constexpr int NKK = D / 16;
-      u32x4 kop[BC / 32][NKK];
+      constexpr int KG = D == 256 ? NKK / 4 : NKK;  // k steps read per group
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
+      for (int g = 0; g < NKK / KG; ++g) {
+        u32x4 kop[BC / 32][KG];
 #pragma unroll
-        for (int tt = 0; tt < BC / 32; ++tt) kop[tt][kk] = *(const u32x4*)(ks + tt * 32 * KP + 16 * kk);
-      __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the first MFMA
-      __builtin_amdgcn_s_setprio(1);       // favour this wave while it feeds the matrix core
+        for (int kk = 0; kk < KG; ++kk)
 #pragma unroll
-      for (int tt = 0; tt < BC / 32; ++tt) s[tt] = mfma32<DT>(kop[tt][0], qf[0], zero16);
+          for (int tt = 0; tt < BC / 32; ++tt) kop[tt][kk] = *(const u32x4*)(ks + tt * 32 * KP + 16 * (g * KG + kk));
+        __builtin_amdgcn_sched_barrier(0);  // keep the group's reads ahead of its MFMAs
+        __builtin_amdgcn_s_setprio(1);       // favour this wave while it feeds the matrix core
 #pragma unroll
-      for (int kk = 1; kk < NKK; ++kk)
+        for (int kk = 0; kk < KG; ++kk)
 #pragma unroll
-        for (int tt = 0; tt < BC / 32; ++tt) s[tt] = mfma32<DT>(kop[tt][kk], qf[kk], s[tt]);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(0);
+          for (int tt = 0; tt < BC / 32; ++tt)
+            s[tt] = mfma32<DT>(kop[tt][kk], qf[g * KG + kk], g == 0 && kk == 0 ? zero16 : s[tt]);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+      }
     }
     // register r of tile tt holds key key0 + 32tt + 16(r/8) + 8hh + r%8
     const bool need_mask = (key0 + BC > Lk) || (CAUSAL && key0 + BC - 1 > qw + diag);
@@ -309,7 +323,17 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        for (int r = 0; r < 16; ++r) {
+          if constexpr (D == 256) {
+            // the accumulator stays in its AGPR: read, scale, write back
+            float t;
+            asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32_e32 %1, %2, %1\n\tv_accvgpr_write_b32 %0, %1"
+                         : "+a"(oacc[dt][r]), "=&v"(t)
+                         : "v"(alpha));
+          } else {
+            oacc[dt][r] *= alpha;
+          }
+        }
       m_run = m_new;
     }
     const float nb = m_run == -INFINITY ? 0.f : -m_run;

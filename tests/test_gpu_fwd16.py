@@ -58,6 +58,30 @@ def test_shapes_bf16(lib, d, causal, sq, sk):
 
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_running_max_jumps(lib, d, causal, dtype):
+    # scores grow by about 12 (natural units, > 2^8 in exp2 terms) from one
+    # 64-key tile to the next, so the running max moves and the accumulator is
+    # rescaled on every tile (the path ordinary inputs reach only on tile 0)
+    q, k, v = W.qkv_normal(500 + d, (1, 300, 2, d), (1, 512, 2, d))
+    w = np.zeros(d, dtype=np.float32)
+    w[::2] = 1.0
+    w /= np.linalg.norm(w)
+    tile = (np.arange(512) // 64).astype(np.float32)
+    q = q + 4.0 * w
+    k = k + (3.0 * math.sqrt(d) * tile)[None, :, None, None] * w
+    if dtype == "bf16":
+        q, k = (W.bf16_bits_to_f32(W.bf16_round(x)) for x in (q, k))
+    else:
+        q, k, v = (_f16_values(x) for x in (q, k, v))
+    o, lse = _run(lib, q, k, v, causal, dtype=dtype)
+    o_ref, lse_ref = OA.attention_bshd(q, k, v, 1 / math.sqrt(d), causal)
+    assert np.nanmax(lse_ref) > 60.0  # the scores really span several jumps
+    assert_close16(o, o_ref, lse, lse_ref, f"{dtype} d{d} causal={causal} growing scores", dtype=dtype)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
 def test_fp16(lib, d, causal):
     q, k, v = (_f16_values(x) for x in W.qkv_normal(7 + d, (1, 190, 2, d), (1, 300, 2, d)))
     o, lse = _run(lib, q, k, v, causal, dtype="fp16")
