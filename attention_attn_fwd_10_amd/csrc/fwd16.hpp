@@ -266,6 +266,7 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
     (void)agpr_hint;
   }
 
+  // one key tile (head dims up to 128)
   auto compute = [&](int key0, int buf) {
     if (!wave_active) return;
     if (CAUSAL && key0 > wave_last_key) return;  // tile fully masked for this wave
@@ -363,17 +364,151 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
     l_run += psum;
   };
 
+  // ---- one key tile in three pieces (head dim 256) ---------------------------
+  f32x16 s[BC / 32];  // scores of the current tile
+  float mxs = 0.f;    // their row max (scaled, log2 units)
+  // tiles past this wave's causal diagonal are skipped whole
+  auto tile_active = [&](int key0) { return wave_active && !(CAUSAL && key0 > wave_last_key); };
+  // S^T = K Q^T, masking and the row max; true when the running max must move
+  auto scores_max = [&](int key0, int buf) -> bool {
+    const uint16_t* ks = ks_base + buf * C::K_ELEMS + l32 * KP + 8 * hh;
+    {
+      // the K operands of the tile are read before the first MFMA so that the
+      // LDS latency is paid once (at D = 256 in quarters, which keeps them
+      // within the register budget); the two score tiles form independent
+      // chains
+      constexpr int NKK = D / 16;
+      constexpr int KG = D == 256 ? NKK / 4 : NKK;  // k steps read per group
+#pragma unroll
+      for (int g = 0; g < NKK / KG; ++g) {
+        u32x4 kop[BC / 32][KG];
+#pragma unroll
+        for (int kk = 0; kk < KG; ++kk)
+#pragma unroll
+          for (int tt = 0; tt < BC / 32; ++tt) kop[tt][kk] = *(const u32x4*)(ks + tt * 32 * KP + 16 * (g * KG + kk));
+        __builtin_amdgcn_sched_barrier(0);  // keep the group's reads ahead of its MFMAs
+        __builtin_amdgcn_s_setprio(1);       // favour this wave while it feeds the matrix core
+#pragma unroll
+        for (int kk = 0; kk < KG; ++kk)
+#pragma unroll
+          for (int tt = 0; tt < BC / 32; ++tt)
+            s[tt] = mfma32<DT>(kop[tt][kk], qf[g * KG + kk], g == 0 && kk == 0 ? zero16 : s[tt]);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+      }
+    }
+    // register r of tile tt holds key key0 + 32tt + 16(r/8) + 8hh + r%8
+    const bool need_mask = (key0 + BC > Lk) || (CAUSAL && key0 + BC - 1 > qw + diag);
+    if (need_mask) {
+#pragma unroll
+      for (int tt = 0; tt < BC / 32; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * tt + 16 * (r >> 3) + 8 * hh + (r & 7);
+          const bool bad = key >= Lk || (CAUSAL && key > qi + diag);
+          if (bad) s[tt][r] = -INFINITY;
+        }
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int tt = 0; tt < BC / 32; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tt][r]);
+    mxs = halfwave_max(mx) * c2;
+    // move the running max only when some row's new max exceeds it by > 2^8
+    return __builtin_amdgcn_ballot_w64(mxs > m_run + kLazyRescale) != 0;
+  };
+  // move the running max and rescale the sums and accumulators
+  auto rescale = [&]() {
+    const float m_new = fmaxf(m_run, mxs);
+    const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if constexpr (D == 256) {
+          // the accumulator stays in its AGPR: read, scale, write back
+          float t;
+          asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32_e32 %1, %2, %1\n\tv_accvgpr_write_b32 %0, %1"
+                       : "+a"(oacc[dt][r]), "=&v"(t)
+                       : "v"(alpha));
+        } else {
+          oacc[dt][r] *= alpha;
+        }
+      }
+    m_run = m_new;
+  };
+  // P = exp2(c2 s - m), O^T += V^T P^T over four 16-key chunks: the
+  // exponentials of a chunk, then its D/32 MFMAs, so the matrix work of one
+  // chunk overlaps the next chunk's exponentials
+  auto softmax_pv = [&](int buf) {
+    const float nb = m_run == -INFINITY ? 0.f : -m_run;
+    const uint16_t* vs = vs_base + buf * C::V_ELEMS + vtr_off;
+    float psum = 0.f;
+#pragma unroll
+    for (int c = 0; c < BC / 16; ++c) {
+      const int tt = c >> 1, r0p = 8 * (c & 1);
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = fast_exp2(fmaf(s[tt][r0p + e], c2, nb));
+        psum += p[e];
+      }
+      const u32x4 pk = {pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3]), pack2<DT>(p[4], p[5]),
+                        pack2<DT>(p[6], p[7])};
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const uint16_t* vp = vs + 16 * c * VP + 32 * dt;
+        const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * VP);
+        oacc[dt] = mfma32<DT>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pk, oacc[dt]);
+      }
+    }
+    l_run += psum;
+  };
+
   // ---- key loop: two-stage LDS ring ------------------------------------------
   if (n_kv > 0) {
     dma_tile(0, 0);
     wait_vmem();
     __syncthreads();
-    for (int j = 0; j < n_kv; ++j) {
-      const int buf = j & 1;
-      if (j + 1 < n_kv) dma_tile((j + 1) * BC, buf ^ 1);  // lands while tile j is computed
-      compute(j * BC, buf);
-      wait_vmem();
-      __syncthreads();
+    if constexpr (D != 256) {
+      for (int j = 0; j < n_kv; ++j) {
+        const int buf = j & 1;
+        if (j + 1 < n_kv) dma_tile((j + 1) * BC, buf ^ 1);  // lands while tile j is computed
+        compute(j * BC, buf);
+        wait_vmem();
+        __syncthreads();
+      }
+    } else {
+      // The inner loop runs the tiles that need no rescale and leaves at the
+      // first that does; the rescale (rare after the first tiles) happens
+      // outside it, so the accumulators, which live in AGPRs at this head
+      // dim, are only ever touched by MFMAs inside the inner loop.
+      int j = 0;
+      while (j < n_kv) {
+        bool pending = false;
+        for (; j < n_kv; ++j) {
+          const int buf = j & 1;
+          if (j + 1 < n_kv) dma_tile((j + 1) * BC, buf ^ 1);
+          if (tile_active(j * BC)) {
+            if (scores_max(j * BC, buf)) {
+              pending = true;
+              break;
+            }
+            softmax_pv(buf);
+          }
+          wait_vmem();
+          __syncthreads();
+        }
+        if (pending) {
+          rescale();
+          softmax_pv(j & 1);
+          wait_vmem();
+          __syncthreads();
+          ++j;
+        }
+      }
     }
   }
 
