@@ -55,6 +55,11 @@ def _load():
     lib.attn_fwd_fp8.restype = I
     lib.attn_fwd_varlen.argtypes = [I, P, P, P, P, P, P, I, I, P, P, I, I, I, I, I, I, F, I, P]
     lib.attn_fwd_varlen.restype = I
+    SZ = ctypes.c_size_t
+    lib.attn_fwd_splitkv.argtypes = [I, P, P, P, P, P, P, I, I, P, P, I, I, I, I, I, I, F, I, I, P, SZ, P]
+    lib.attn_fwd_splitkv.restype = I
+    lib.attn_fwd_splitkv_workspace_bytes.argtypes = [I, I, I, I]
+    lib.attn_fwd_splitkv_workspace_bytes.restype = SZ
     lib.attn_status_string.argtypes = [I]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
@@ -205,4 +210,58 @@ def fwd_varlen(q, cu_seqlens_q, k, v, cu_seqlens_k, max_seqlen_q, max_seqlen_k, 
                                 _ptr(cu_seqlens_k), _ptr(block_table), max_pages, int(page_size), _ptr(out),
                                 _ptr(lse), B, H, D, total_q, int(max_seqlen_q), int(max_seqlen_k), scale,
                                 int(bool(causal)), _stream(stream)))
+    return out, lse
+
+
+def splitkv_num_splits(n_work, max_seqlen_k, target=1024, min_tiles=4, max_splits=256):
+    """A split count for attn_fwd_splitkv: enough work items (n_work tiles x
+    splits) to reach `target` workgroups, with at least `min_tiles` 64-key
+    tiles per split."""
+    tiles = max(1, (int(max_seqlen_k) + 63) // 64)
+    want = max(1, -(-target // max(1, int(n_work))))
+    return int(max(1, min(want, tiles // min_tiles, max_splits)))
+
+
+def fwd_splitkv(q, cu_seqlens_q, k, v, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale=None,
+                causal=False, block_table=None, page_size=0, num_splits=None, out=None, lse=None,
+                workspace=None, stream=None):
+    """fwd_varlen with each sequence's keys cut into num_splits ranges that run
+    as separate work items, then merged through their logsumexps (for short
+    queries over long key caches).  num_splits=None picks a count from the
+    problem size.  The fp32 workspace is allocated here unless given.
+    Returns (o [total_q, H, D], lse fp32 [H, total_q])."""
+    import torch
+    _require_cuda(q, cu_seqlens_q, k, v, cu_seqlens_k, block_table, out, lse, workspace)
+    total_q, H, D = q.shape
+    B = cu_seqlens_q.numel() - 1
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("varlen tensors must be contiguous")
+    for t in (cu_seqlens_q, cu_seqlens_k):
+        if t.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+    max_pages = 0
+    if block_table is not None:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
+            raise ValueError("block_table must be contiguous int32 [B, max_pages]")
+        max_pages = block_table.shape[1]
+        if k.shape[1] != page_size:
+            raise ValueError("paged k/v must be [num_pages, page_size, H, D]")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if num_splits is None:
+        n_work = H * (-(-int(total_q) // 128) + B)
+        num_splits = splitkv_num_splits(n_work, max_seqlen_k)
+    num_splits = int(num_splits)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    need = int(_lib.attn_fwd_splitkv_workspace_bytes(total_q, H, D, num_splits))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.attn_fwd_splitkv(_dtype_code(q.dtype), _ptr(q), _ptr(cu_seqlens_q), _ptr(k), _ptr(v),
+                                 _ptr(cu_seqlens_k), _ptr(block_table), max_pages, int(page_size), _ptr(out),
+                                 _ptr(lse), B, H, D, total_q, int(max_seqlen_q), int(max_seqlen_k), scale,
+                                 int(bool(causal)), num_splits, _ptr(workspace), ws_bytes, _stream(stream)))
     return out, lse

@@ -21,6 +21,7 @@ hipError_t launch_fwd16(const FwdArgs& a, hipStream_t s);
 template <int D, int DT, bool CAUSAL, int MODE>
 hipError_t launch_fwd16pp(FwdArgs a, hipStream_t s);
 hipError_t launch_fp8_quantize(const QuantArgs& a, int D, hipStream_t s);
+hipError_t launch_splitkv_merge(const MergeArgs& a, int D, int dtype, hipStream_t s);
 hipError_t launch_fwd_fp8(const Fp8Args& a, int D, bool causal, hipStream_t s);
 }  // namespace attn
 
@@ -90,7 +91,8 @@ bool use_pingpong() {
 template <int D, int DT, bool CAUSAL, int MODE>
 hipError_t launch_one(const attn::FwdArgs& a, hipStream_t s) {
   if constexpr (D <= 128) {
-    if (use_pingpong()) return attn::launch_fwd16pp<D, DT, CAUSAL, MODE>(a, s);
+    // (the ping-pong kernel has no split-key form)
+    if (use_pingpong() && a.n_split <= 1) return attn::launch_fwd16pp<D, DT, CAUSAL, MODE>(a, s);
   }
   return attn::launch_fwd16<D, DT, CAUSAL, MODE>(a, s);
 }
@@ -119,6 +121,7 @@ hipError_t dispatch_fwd16(const attn::FwdArgs& a, int D, int dtype, bool causal,
 constexpr int kBR = 128;  // query rows per workgroup of every forward kernel
 // K/V tiles are read through 32-bit buffer offsets: 64 rows of a tile must fit in 2^31 bytes
 constexpr int64_t kMaxSeqStride = int64_t(1) << 24;
+constexpr int kMaxSplits = 256;  // key splits per sequence in attn_fwd_splitkv
 
 }  // namespace
 
@@ -174,11 +177,19 @@ attn_status_t attn_fwd(int dtype, const void* q, const int64_t q_strides[3], con
   return hip_status(dispatch_fwd16(a, D, dtype, causal != 0, attn::kDense, (hipStream_t)stream), "attn_fwd launch");
 }
 
-attn_status_t attn_fwd_varlen(int dtype, const void* q, const int32_t* cu_seqlens_q, const void* k, const void* v,
-                              const int32_t* cu_seqlens_k, const int32_t* block_table, int max_pages_per_seq,
-                              int page_size, void* o, float* lse, int B, int H, int D, int total_q,
-                              int max_seqlen_q, int max_seqlen_k, float softmax_scale, int causal, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and argument set-up shared by attn_fwd_varlen and
+// attn_fwd_splitkv.  *empty is set when there is nothing to compute.
+attn_status_t varlen_args(int dtype, const void* q, const int32_t* cu_seqlens_q, const void* k, const void* v,
+                          const int32_t* cu_seqlens_k, const int32_t* block_table, int max_pages_per_seq,
+                          int page_size, void* o, float* lse, int B, int H, int D, int total_q, int max_seqlen_q,
+                          int max_seqlen_k, float softmax_scale, int causal, attn::FwdArgs* a, int* mode,
+                          bool* empty) {
   attn_status_t st;
+  *empty = false;
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return fail(ATTN_ERR_INVALID, "dtype %d is not bf16/fp16", dtype);
   if (B < 0 || H < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
     return fail(ATTN_ERR_INVALID, "negative size");
@@ -194,7 +205,10 @@ attn_status_t attn_fwd_varlen(int dtype, const void* q, const int32_t* cu_seqlen
       return fail(ATTN_ERR_INVALID, "max_pages_per_seq * page_size < max_seqlen_k");
     while ((1 << page_shift) < page_size) ++page_shift;
   }
-  if (B == 0 || H == 0 || total_q == 0 || max_seqlen_q == 0) return ok();
+  if (B == 0 || H == 0 || total_q == 0 || max_seqlen_q == 0) {
+    *empty = true;
+    return ok();
+  }
   if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return fail(ATTN_ERR_INVALID, "cu_seqlens is NULL");
   if (q == nullptr || o == nullptr) return fail(ATTN_ERR_INVALID, "q or o is NULL");
   if (max_seqlen_k > 0 && (k == nullptr || v == nullptr)) return fail(ATTN_ERR_INVALID, "k or v is NULL");
@@ -205,21 +219,80 @@ attn_status_t attn_fwd_varlen(int dtype, const void* q, const int32_t* cu_seqlen
   if ((int64_t)B * H * n_qblk > INT32_MAX || (int64_t)H * ((total_q + kBR - 1) / kBR + B) > INT32_MAX)
     return fail(ATTN_ERR_INVALID, "problem too large for one launch");
 
-  attn::FwdArgs a{};
-  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  *a = attn::FwdArgs{};
+  a->q = q; a->k = k; a->v = v; a->o = o; a->lse = lse;
   const int64_t tok = (int64_t)H * D;  // packed [tokens, H, D]
-  a.q_ss = tok; a.q_sh = D;
-  a.k_ss = tok; a.k_sh = D;
-  a.v_ss = tok; a.v_sh = D;
-  a.o_ss = tok; a.o_sh = D;
-  a.B = B; a.H = H; a.Sq = max_seqlen_q; a.Sk = max_seqlen_k;
-  a.scale_log2 = softmax_scale * attn::kLog2e;
-  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
-  a.block_table = block_table; a.max_pages = max_pages_per_seq; a.page_shift = page_shift;
-  a.n_qblk = (int)n_qblk;
-  a.total_q = total_q;
-  const int mode = block_table != nullptr ? attn::kPaged : attn::kVarlen;
+  a->q_ss = tok; a->q_sh = D;
+  a->k_ss = tok; a->k_sh = D;
+  a->v_ss = tok; a->v_sh = D;
+  a->o_ss = tok; a->o_sh = D;
+  a->B = B; a->H = H; a->Sq = max_seqlen_q; a->Sk = max_seqlen_k;
+  a->scale_log2 = softmax_scale * attn::kLog2e;
+  a->cu_q = cu_seqlens_q; a->cu_k = cu_seqlens_k;
+  a->block_table = block_table; a->max_pages = max_pages_per_seq; a->page_shift = page_shift;
+  a->n_qblk = (int)n_qblk;
+  a->total_q = total_q;
+  a->n_split = 1;
+  *mode = block_table != nullptr ? attn::kPaged : attn::kVarlen;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_fwd_varlen(int dtype, const void* q, const int32_t* cu_seqlens_q, const void* k, const void* v,
+                              const int32_t* cu_seqlens_k, const int32_t* block_table, int max_pages_per_seq,
+                              int page_size, void* o, float* lse, int B, int H, int D, int total_q,
+                              int max_seqlen_q, int max_seqlen_k, float softmax_scale, int causal, void* stream) {
+  attn::FwdArgs a;
+  int mode;
+  bool empty;
+  const attn_status_t st = varlen_args(dtype, q, cu_seqlens_q, k, v, cu_seqlens_k, block_table, max_pages_per_seq,
+                                       page_size, o, lse, B, H, D, total_q, max_seqlen_q, max_seqlen_k,
+                                       softmax_scale, causal, &a, &mode, &empty);
+  if (st != ATTN_OK || empty) return st;
   return hip_status(dispatch_fwd16(a, D, dtype, causal != 0, mode, (hipStream_t)stream), "attn_fwd_varlen launch");
+}
+
+size_t attn_fwd_splitkv_workspace_bytes(int total_q, int H, int D, int num_splits) {
+  if (num_splits <= 1 || total_q <= 0 || H <= 0 || D <= 0) return 0;
+  return (size_t)num_splits * (size_t)total_q * (size_t)H * (size_t)(D + 1) * sizeof(float);
+}
+
+attn_status_t attn_fwd_splitkv(int dtype, const void* q, const int32_t* cu_seqlens_q, const void* k, const void* v,
+                               const int32_t* cu_seqlens_k, const int32_t* block_table, int max_pages_per_seq,
+                               int page_size, void* o, float* lse, int B, int H, int D, int total_q,
+                               int max_seqlen_q, int max_seqlen_k, float softmax_scale, int causal, int num_splits,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(ATTN_ERR_INVALID, "num_splits %d must be in 1..%d", num_splits, kMaxSplits);
+  attn::FwdArgs a;
+  int mode;
+  bool empty;
+  const attn_status_t st = varlen_args(dtype, q, cu_seqlens_q, k, v, cu_seqlens_k, block_table, max_pages_per_seq,
+                                       page_size, o, lse, B, H, D, total_q, max_seqlen_q, max_seqlen_k,
+                                       softmax_scale, causal, &a, &mode, &empty);
+  if (st != ATTN_OK || empty) return st;
+  if (num_splits == 1)
+    return hip_status(dispatch_fwd16(a, D, dtype, causal != 0, mode, (hipStream_t)stream), "attn_fwd_splitkv launch");
+  const size_t need = attn_fwd_splitkv_workspace_bytes(total_q, H, D, num_splits);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(ATTN_ERR_INVALID, "workspace of %zu bytes needed (got %zu)", need, workspace == nullptr ? 0 : workspace_bytes);
+  if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID, "workspace must be 16-byte aligned");
+  if ((int64_t)H * ((total_q + kBR - 1) / kBR + B) * num_splits > INT32_MAX)
+    return fail(ATTN_ERR_INVALID, "problem too large for one launch");
+  const int tiles = (max_seqlen_k + 63) / 64;
+  a.n_split = num_splits;
+  a.split_tiles = (tiles + num_splits - 1) / num_splits;
+  a.part_o = (float*)workspace;
+  a.part_lse = a.part_o + (size_t)num_splits * total_q * H * D;
+  hipError_t e = dispatch_fwd16(a, D, dtype, causal != 0, mode, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "attn_fwd_splitkv launch");
+  attn::MergeArgs m{};
+  m.part_o = a.part_o; m.part_lse = a.part_lse; m.o = o; m.lse = lse;
+  m.n_split = num_splits; m.total_q = total_q; m.H = H;
+  return hip_status(attn::launch_splitkv_merge(m, D, dtype, (hipStream_t)stream), "attn_fwd_splitkv merge launch");
 }
 
 attn_status_t attn_fp8_quantize(const void* x, const int64_t x_strides[3], uint8_t* x8, float* scales, int B, int H,

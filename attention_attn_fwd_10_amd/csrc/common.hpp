@@ -152,6 +152,21 @@ struct FwdArgs {
   int page_shift;            // log2(page_size)
   int n_qblk;                // query blocks per (b, h)
   int total_q;               // varlen: rows of the packed q (LSE row length)
+  // split keys (varlen / paged only): n_split > 1 gives every (tile, split) a
+  // workgroup over key tiles [split * split_tiles, (split + 1) * split_tiles);
+  // each writes its normalised partial output and logsumexp in fp32
+  int n_split;
+  int split_tiles;
+  float* part_o;             // [n_split, total_q, H, D]
+  float* part_lse;           // [n_split, H, total_q]
+};
+
+struct MergeArgs {
+  const float* part_o;    // [n_split, total_q, H, D]
+  const float* part_lse;  // [n_split, H, total_q]
+  void* o;                // [total_q, H, D] bf16 / fp16
+  float* lse;             // [H, total_q] or null
+  int n_split, total_q, H;
 };
 
 struct Fp8Args {

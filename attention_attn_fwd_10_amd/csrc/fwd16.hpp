@@ -74,7 +74,7 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
 
   // ---- work item: (b, h, query block) -------------------------------------
   const int t = xcd_remap(blockIdx.x, gridDim.x);
-  int b, h, qblk;
+  int b, h, qblk, split = 0;
   if constexpr (MODE == kDense) {
     const int bh = t / a.n_qblk;
     qblk = t - bh * a.n_qblk;
@@ -83,8 +83,13 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
     h = bh - b * a.H;
   } else {
     // compact tile list: sequence b owns H * ceil(Lq_b / BR) consecutive tiles
-    // (head-major), so no workgroup is spent on query blocks past a sequence
+    // (head-major), so no workgroup is spent on query blocks past a sequence;
+    // with split keys, consecutive workgroups are the splits of one tile
     int rem = t, nq = 0;
+    if (a.n_split > 1) {
+      split = t % a.n_split;
+      rem = t / a.n_split;
+    }
     for (b = 0; b < a.B; ++b) {
       nq = (a.cu_q[b + 1] - a.cu_q[b] + BR - 1) / BR;
       if (rem < a.H * nq) break;
@@ -129,6 +134,14 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
   if (CAUSAL) {
     const int last = min(qs + BR, Lq) - 1 + (Lk - Lq);  // last key any row of the block may see
     n_kv = last < 0 ? 0 : min(n_kv, last / BC + 1);
+  }
+  // key tiles [j0, j1) of this work item (all of them unless keys are split)
+  int j0 = 0, j1 = n_kv;
+  if constexpr (MODE != kDense) {
+    if (a.n_split > 1) {
+      j0 = min(n_kv, split * a.split_tiles);
+      j1 = min(n_kv, j0 + a.split_tiles);
+    }
   }
 
   const int qw = qs + 32 * wave;  // first query row of this wave
@@ -468,14 +481,14 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
   };
 
   // ---- key loop: two-stage LDS ring ------------------------------------------
-  if (n_kv > 0) {
-    dma_tile(0, 0);
+  if (j1 > j0) {
+    dma_tile(j0 * BC, j0 & 1);
     wait_vmem();
     __syncthreads();
     if constexpr (D != 256) {
-      for (int j = 0; j < n_kv; ++j) {
+      for (int j = j0; j < j1; ++j) {
         const int buf = j & 1;
-        if (j + 1 < n_kv) dma_tile((j + 1) * BC, buf ^ 1);  // lands while tile j is computed
+        if (j + 1 < j1) dma_tile((j + 1) * BC, buf ^ 1);  // lands while tile j is computed
         compute(j * BC, buf);
         wait_vmem();
         __syncthreads();
@@ -485,12 +498,12 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
       // first that does; the rescale (rare after the first tiles) happens
       // outside it, so the accumulators, which live in AGPRs at this head
       // dim, are only ever touched by MFMAs inside the inner loop.
-      int j = 0;
-      while (j < n_kv) {
+      int j = j0;
+      while (j < j1) {
         bool pending = false;
-        for (; j < n_kv; ++j) {
+        for (; j < j1; ++j) {
           const int buf = j & 1;
-          if (j + 1 < n_kv) dma_tile((j + 1) * BC, buf ^ 1);
+          if (j + 1 < j1) dma_tile((j + 1) * BC, buf ^ 1);
           if (tile_active(j * BC)) {
             if (scores_max(j * BC, buf)) {
               pending = true;
@@ -514,6 +527,31 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
 
   // ---- epilogue: o / l, lse = ln2 * (m + log2 l) -----------------------------
   const float l_tot = halfwave_sum(l_run);
+  if constexpr (MODE != kDense) {
+    if (a.n_split > 1) {
+      // partial result of this key split, in fp32; register r of tile dt is
+      // head-dim column 32dt + 16(r/8) + 8hh + r%8
+      if (qi < Lq) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const int64_t row = (int64_t)split * a.total_q + (lse_base - (int64_t)h * a.total_q) + qi;
+        float* pp = a.part_o + (row * a.H + h) * D + 8 * hh;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const f32x16& o = oacc[dt];
+            const int r0p = 8 * half;
+            float* dst = pp + 32 * dt + 16 * half;
+            *(f32x4*)dst = f32x4{o[r0p] * inv, o[r0p + 1] * inv, o[r0p + 2] * inv, o[r0p + 3] * inv};
+            *(f32x4*)(dst + 4) = f32x4{o[r0p + 4] * inv, o[r0p + 5] * inv, o[r0p + 6] * inv, o[r0p + 7] * inv};
+          }
+        if (hh == 0)
+          a.part_lse[(int64_t)split * a.H * a.total_q + lse_base + qi] =
+              l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      }
+      return;
+    }
+  }
   if (qi < Lq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* op = (uint16_t*)a.o + ooff + (int64_t)qi * a.o_ss + 8 * hh;
@@ -536,7 +574,7 @@ template <int D, int DT, bool CAUSAL, int MODE>
 hipError_t launch_fwd16(const FwdArgs& a, hipStream_t s) {
   // dense: every (b, h, q-block); varlen: an upper bound on the compact tile list
   const int n = MODE == kDense ? a.B * a.H * a.n_qblk
-                               : a.H * ((a.total_q + Fwd16Cfg<D>::BR - 1) / Fwd16Cfg<D>::BR + a.B);
+                               : a.H * ((a.total_q + Fwd16Cfg<D>::BR - 1) / Fwd16Cfg<D>::BR + a.B) * max(a.n_split, 1);
   hipLaunchKernelGGL((fwd16_kernel<D, DT, CAUSAL, MODE>), dim3(n), dim3(256), 0, s, a);
   return hipGetLastError();
 }

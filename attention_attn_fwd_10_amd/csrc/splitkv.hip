@@ -1,0 +1,77 @@
+// Combine of split-key partial results ("Fused attention kernel" page,
+// Implementation sketch: the per-row running max and sum are exactly the state
+// needed to merge two key ranges).  Each key split s of a row produced a
+// normalised output O_s and logsumexp L_s; the row's result is
+//   L = ln sum_s exp(L_s),   O = sum_s exp(L_s - L) O_s,
+// computed as m = max_s L_s, w_s = exp(L_s - m), O = sum w_s O_s / sum w_s,
+// L = m + ln sum w_s.  Splits that saw no key (L_s = -inf) weigh nothing; a row
+// with no key at all gets O = 0 and L = -inf.
+#include "common.hpp"
+
+namespace attn {
+
+// one wave per (row, head); lane l owns head-dim columns E*l .. E*l+E-1
+template <int D, int DT>
+__global__ void __launch_bounds__(256) splitkv_merge_kernel(MergeArgs a) {
+  constexpr int E = D / 64;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (item >= (int64_t)a.total_q * a.H) return;
+  const int row = (int)(item / a.H), h = (int)(item - (int64_t)row * a.H);
+  const int64_t lse_stride = (int64_t)a.H * a.total_q;
+  const float* pl = a.part_lse + (int64_t)h * a.total_q + row;
+  float m = -INFINITY;
+  for (int s = 0; s < a.n_split; ++s) m = fmaxf(m, pl[s * lse_stride]);
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  float wsum = 0.f;
+  if (m != -INFINITY) {
+    const int64_t o_stride = (int64_t)a.total_q * a.H * D;
+    const float* po = a.part_o + ((int64_t)row * a.H + h) * D + E * lane;
+    for (int s = 0; s < a.n_split; ++s) {
+      const float ls = pl[s * lse_stride];
+      if (ls == -INFINITY) continue;  // uniform over the wave
+      const float w = fast_exp2((ls - m) * kLog2e);
+      wsum += w;
+      const float* src = po + s * o_stride;
+      if constexpr (E == 4) {
+        const f32x4 x = *(const f32x4*)src;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += w * x[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += w * src[e];
+      }
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  uint16_t* op = (uint16_t*)a.o + ((int64_t)row * a.H + h) * D + E * lane;
+  if constexpr (E == 1) {
+    const uint32_t p = pack2<DT>(acc[0] * inv, 0.f);
+    *op = (uint16_t)(p & 0xffffu);
+  } else if constexpr (E == 2) {
+    *(uint32_t*)op = pack2<DT>(acc[0] * inv, acc[1] * inv);
+  } else {
+    *(u32x2*)op = u32x2{pack2<DT>(acc[0] * inv, acc[1] * inv), pack2<DT>(acc[2] * inv, acc[3] * inv)};
+  }
+  if (lane == 0 && a.lse != nullptr)
+    a.lse[(int64_t)h * a.total_q + row] = wsum > 0.f ? m + __log2f(wsum) * kLn2 : -INFINITY;
+}
+
+hipError_t launch_splitkv_merge(const MergeArgs& a, int D, int dtype, hipStream_t s) {
+  const int64_t items = (int64_t)a.total_q * a.H;
+  const dim3 grid((unsigned)((items + 3) / 4)), block(256);
+  if (dtype == kBF16) {
+    if (D == 64) hipLaunchKernelGGL((splitkv_merge_kernel<64, kBF16>), grid, block, 0, s, a);
+    else if (D == 128) hipLaunchKernelGGL((splitkv_merge_kernel<128, kBF16>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((splitkv_merge_kernel<256, kBF16>), grid, block, 0, s, a);
+  } else {
+    if (D == 64) hipLaunchKernelGGL((splitkv_merge_kernel<64, kFP16>), grid, block, 0, s, a);
+    else if (D == 128) hipLaunchKernelGGL((splitkv_merge_kernel<128, kFP16>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((splitkv_merge_kernel<256, kFP16>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace attn

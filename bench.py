@@ -76,6 +76,7 @@ def parse():
     p.add_argument("--no-fp8", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--sweep", action="store_true", help="also time the 16384-token seq sweep (extra output)")
+    p.add_argument("--no-decode", action="store_true", help="skip the long-cache decoding leg")
     p.add_argument("--source-hash", action="store_true", help="print the timed kernel's source hash and exit")
     p.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (calibrates the FETCH_SIZE/WRITE_SIZE counters)")
@@ -197,6 +198,9 @@ def main():
     if not args.no_fp8:
         result["fp8"] = bench_fp8(A, W, args)
 
+    if not args.no_decode:
+        result["decode"] = bench_decode(A, W, args)
+
     if args.sweep:
         result["sweep"] = bench_sweep(A, W, args)
 
@@ -232,6 +236,45 @@ def bench_fp8(A, W, args):
             "quantize_ms_per_tensor": round(ms_q, 4),
             "quantize_gbs": round(q_bytes / (ms_q * 1e-3) / 1e9, 1),
             "end_to_end_ms": round(ms + 3 * ms_q, 4)}
+
+
+def bench_decode(A, W, args):
+    """One query row per sequence over a long paged cache: the whole-sequence
+    kernel (attn_fwd_varlen, one work item per sequence and head) against the
+    split-key path (attn_fwd_splitkv).  HBM-bound: reported in GB/s of K and V
+    read."""
+    import torch
+    cfg = W.DECODE
+    B, Lq, Lk, H, D, page = (cfg[x] for x in ("n_seq", "seq_q", "seq_k", "heads", "head_dim", "page_size"))
+    lens_q, lens_k = [Lq] * B, [Lk] * B
+    table, npages = W.paged_layout(cfg["seed_pages"], lens_k, page)
+    g = torch.Generator(device="cuda").manual_seed(cfg["seed_values"])
+    q = torch.randn((B * Lq, H, D), generator=g, device="cuda").to(torch.bfloat16)
+    kp, vp = (torch.randn((npages, page, H, D), generator=g, device="cuda").to(torch.bfloat16) for _ in range(2))
+    cu_q = torch.from_numpy(W.cu_seqlens(lens_q)).cuda()
+    cu_k = torch.from_numpy(W.cu_seqlens(lens_k)).cuda()
+    tab = torch.from_numpy(table).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((H, B * Lq), dtype=torch.float32, device="cuda")
+    n_work = H * (-(-(B * Lq) // 128) + B)
+    splits = A.splitkv_num_splits(n_work, Lk)
+    ws = torch.empty(A._lib.attn_fwd_splitkv_workspace_bytes(B * Lq, H, D, splits) // 4 + 4, dtype=torch.float32,
+                     device="cuda")
+    kv_bytes = 2 * B * Lk * H * D * 2
+    algo = kv_bytes + 2 * 2 * B * Lq * H * D + 4 * H * B * Lq + 4 * table.size
+    steps = max(5, args.steps // 3)
+    ms_whole = time_launches(lambda: A.fwd_varlen(q, cu_q, kp, vp, cu_k, Lq, Lk, None, cfg["causal"],
+                                                  block_table=tab, page_size=page, out=o, lse=lse), steps, 10)
+    ms_split = time_launches(lambda: A.fwd_splitkv(q, cu_q, kp, vp, cu_k, Lq, Lk, None, cfg["causal"],
+                                                   block_table=tab, page_size=page, num_splits=splits, out=o,
+                                                   lse=lse, workspace=ws), steps, 10)
+    gbs = algo / (ms_split * 1e-3) / 1e9
+    print(f"[bench] decode: whole {ms_whole:.3f} ms, split x{splits} {ms_split:.3f} ms ({gbs:.0f} GB/s)",
+          file=sys.stderr, flush=True)
+    return {"workload": f"decode_paged{page}_b{B}_h{H}_sk{Lk}_d{D}", "splits": splits,
+            "ms_whole_sequence": round(ms_whole, 4), "ms_split": round(ms_split, 4),
+            "gbs_split": round(gbs, 1), "gbs_whole_sequence": round(algo / (ms_whole * 1e-3) / 1e9, 1),
+            "pct_of_hbm_peak": round(100 * gbs / 8000.0, 1), "algorithmic_bytes": algo}
 
 
 def bench_sweep(A, W, args):

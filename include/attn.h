@@ -35,6 +35,7 @@
 #ifndef ATTN_FWD_MI355X_H
 #define ATTN_FWD_MI355X_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -150,6 +151,43 @@ attn_status_t attn_fwd_varlen(int dtype,
                               void* o, float* lse,
                               int B, int H, int D, int total_q, int max_seqlen_q, int max_seqlen_k,
                               float softmax_scale, int causal, void* stream);
+
+/*
+ * attn_fwd_splitkv — attn_fwd_varlen with every sequence's keys cut into
+ * num_splits ranges that run as separate work items, followed by a merge.
+ * (The "Fused attention kernel" page's implementation sketch keeps a running
+ * row max and row sum per query; the partial results of two key ranges merge
+ * exactly through their logsumexps, L = ln(e^L1 + e^L2) and
+ * O = e^(L1-L) O1 + e^(L2-L) O2.  The FlashAttention-3 summary page names
+ * LLM inference as future work; short queries over long, paged key caches are
+ * that case.)
+ *
+ * Arguments as for attn_fwd_varlen, plus:
+ * num_splits >= 1: ranges of ceil(ceil(max_seqlen_k / 64) / num_splits) key
+ *   tiles of 64 keys each; sequences shorter than max_seqlen_k leave their last
+ *   ranges empty.  num_splits == 1 is attn_fwd_varlen itself and needs no
+ *   workspace.
+ * workspace: device memory of at least
+ *   attn_fwd_splitkv_workspace_bytes(total_q, H, D, num_splits) bytes, 16-byte
+ *   aligned, owned by the caller, free for this call only (it holds the
+ *   partial outputs and logsumexps in fp32).  workspace_bytes is its size;
+ *   a smaller workspace is an error.
+ * The result is the same attention as attn_fwd_varlen up to floating-point
+ * rounding (two extra fp32 roundings of the partial outputs).
+ */
+attn_status_t attn_fwd_splitkv(int dtype,
+                               const void* q, const int32_t* cu_seqlens_q,
+                               const void* k, const void* v,
+                               const int32_t* cu_seqlens_k,
+                               const int32_t* block_table, int max_pages_per_seq, int page_size,
+                               void* o, float* lse,
+                               int B, int H, int D, int total_q, int max_seqlen_q, int max_seqlen_k,
+                               float softmax_scale, int causal, int num_splits,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace attn_fwd_splitkv needs: num_splits * total_q * H * (D + 1) * 4
+ * bytes (0 for num_splits <= 1 or an empty problem). */
+size_t attn_fwd_splitkv_workspace_bytes(int total_q, int H, int D, int num_splits);
 
 /* Human-readable name of a status code (static storage). */
 const char* attn_status_string(int status);

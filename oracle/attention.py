@@ -190,3 +190,24 @@ def attention_varlen(q, cu_q, k, v, cu_k, scale: float, causal: bool = False,
             o[q0:q1, h] = oo
             lse[h, q0:q1] = ll
     return o, lse
+
+
+def merge_partials(outs, lses):
+    """Combine the results of disjoint key ranges of the same query rows.
+
+    ``outs[s]`` [rows, Dv] is the normalised output and ``lses[s]`` [rows] the
+    natural-log logsumexp of range s (-inf: the range held no allowed key).
+    The running max and sum of [FAK Implementation sketch] make this exact:
+    with L = ln sum_s exp(L_s), the merged output is sum_s exp(L_s - L) O_s and
+    the merged logsumexp is L.  A row no range saw gets O = 0, L = -inf."""
+    L = np.stack([np.asarray(x, dtype=np.float64) for x in lses])      # [S, rows]
+    O = np.stack([np.asarray(x, dtype=np.float64) for x in outs])      # [S, rows, Dv]
+    m = L.max(axis=0)
+    seen = np.isfinite(m)
+    shift = np.where(seen, m, 0.0)
+    w = np.where(np.isfinite(L), np.exp(L - shift[None, :]), 0.0)      # [S, rows]
+    wsum = w.sum(axis=0)
+    o = np.einsum("sr,srd->rd", w, O)
+    o = np.where(seen[:, None], o / np.where(seen, wsum, 1.0)[:, None], 0.0)
+    lse = np.where(seen, shift + np.log(np.where(seen, wsum, 1.0)), -np.inf)
+    return o, lse

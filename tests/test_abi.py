@@ -31,6 +31,10 @@ def lib():
     L.attn_fp8_quantize.argtypes = [P, I64P, P, P, I, I, I, I, I, P, P]
     L.attn_fwd_fp8.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, I, F, I, P]
     L.attn_fwd_varlen.argtypes = [I, P, P, P, P, P, P, I, I, P, P, I, I, I, I, I, I, F, I, P]
+    L.attn_fwd_splitkv.argtypes = [I, P, P, P, P, P, P, I, I, P, P, I, I, I, I, I, I, F, I, I, P,
+                                   ctypes.c_size_t, P]
+    L.attn_fwd_splitkv_workspace_bytes.argtypes = [I, I, I, I]
+    L.attn_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
     L.attn_status_string.argtypes = [I]
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_last_error.restype = ctypes.c_char_p
@@ -45,8 +49,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("attn_fwd", "attn_fp8_quantize", "attn_fwd_fp8", "attn_fwd_varlen", "attn_status_string",
-              "attn_last_error"):
+    for n in ("attn_fwd", "attn_fp8_quantize", "attn_fwd_fp8", "attn_fwd_varlen", "attn_fwd_splitkv",
+              "attn_fwd_splitkv_workspace_bytes", "attn_status_string", "attn_last_error"):
         assert n in names
 
 
@@ -136,6 +140,26 @@ def test_varlen_validation(lib):
     assert f(D=80) == UNSUPPORTED
     assert f(B=0) == OK
     assert f(total_q=0) == OK
+
+
+def test_splitkv_validation(lib):
+    def f(splits=4, ws=A16, ws_bytes=1 << 30, B=2, total_q=10, D=128, page=64, table=A16):
+        return lib.attn_fwd_splitkv(0, A16, A16, A16, A16, A16, table, 4, page, A16, None, B, 2, D, total_q, 100,
+                                    200, 0.1, 1, splits, ws, ws_bytes, None)
+    assert f(splits=0) == INVALID
+    assert f(splits=257) == INVALID
+    assert f(ws=None) == INVALID                      # workspace needed for splits > 1
+    assert f(ws_bytes=1000) == INVALID                # workspace too small
+    assert f(ws=A_ODD) == INVALID                     # not 16-byte aligned
+    assert f(page=48) == INVALID                      # the varlen checks apply
+    assert f(D=80) == UNSUPPORTED
+    assert f(B=0) == OK and f(total_q=0) == OK          # empty problems: no-op
+
+
+def test_splitkv_workspace_bytes(lib):
+    assert lib.attn_fwd_splitkv_workspace_bytes(10, 2, 128, 4) == 4 * 10 * 2 * 129 * 4
+    assert lib.attn_fwd_splitkv_workspace_bytes(10, 2, 128, 1) == 0
+    assert lib.attn_fwd_splitkv_workspace_bytes(0, 2, 128, 4) == 0
 
 
 def test_status_strings(lib):

@@ -210,3 +210,27 @@ def test_half_ulp_helper():
     from tests.parity import half_ulp
     assert half_ulp(1.0) == 2.0 ** -8 and half_ulp(3.0) == 2.0 ** -7 and half_ulp(-5.0) == 2.0 ** -6
     assert half_ulp(1.0, "fp16") == 2.0 ** -11
+
+
+@pytest.mark.parametrize("bounds", [(0, 7, 7, 40, 100), (0, 1, 2, 3, 100), (0, 100)])
+def test_merge_of_key_ranges_equals_full_attention(bounds):
+    # ranges of keys (one may be empty) attended separately and merged give the
+    # attention over all keys: a pin of merge_partials against the definition
+    q, k, v = _rand(23, 8), _rand(100, 8), _rand(100, 5)
+    parts = [A.naive_head(q, k[lo:hi], v[lo:hi], 0.4) for lo, hi in zip(bounds[:-1], bounds[1:])]
+    o, lse = A.merge_partials([p[0] for p in parts], [p[1] for p in parts])
+    o_ref, lse_ref = A.naive_head(q, k, v, 0.4)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-12)
+
+
+def test_merge_rows_without_keys():
+    # causal rows that see no key in any range stay O = 0, LSE = -inf
+    q, k, v = _rand(6, 4), _rand(3, 4), _rand(3, 4)
+    o1, l1 = A.naive_head(q, k[:2], v[:2], 1.0, causal=True, lq=6)
+    o2, l2 = A.naive_head(q, k[2:], v[2:], 1.0)
+    o2[:] = 0.0
+    l2[:] = -np.inf
+    o, lse = A.merge_partials([o1, o2], [l1, l2])
+    np.testing.assert_array_equal(np.isinf(lse), np.isinf(l1))
+    np.testing.assert_allclose(o, o1, rtol=0, atol=1e-15)

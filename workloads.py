@@ -199,3 +199,8 @@ def seq_sweep_points():
 # causal, 64-token pages at random physical slots
 VARLEN = dict(n_seq=32, lo=128, hi=4096, heads=32, head_dim=128, page_size=64,
               causal=True, seed_lengths=5, seed_pages=6, seed_values=7)
+
+# decoding against a long paged cache: one query row per sequence, every
+# sequence 32768 keys in 64-token pages at a seeded permutation of slots
+DECODE = dict(n_seq=4, seq_q=1, seq_k=32768, heads=32, head_dim=128, page_size=64, causal=True,
+              seed_pages=12, seed_values=13)
