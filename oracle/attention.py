@@ -57,11 +57,14 @@ def valid_key_counts(lq: int, lk: int, causal: bool) -> np.ndarray:
 # one head, three passes (the plain definition)
 # ---------------------------------------------------------------------------
 def naive_head(q, k, v, scale: float, causal: bool = False, rows=None, lq=None,
-               return_p: bool = False):
+               return_p: bool = False, bias=None):
     """Scores, then row max, then row sum, then P and O = P V.
 
     q: [n, D] query rows (their indices in the sequence are ``rows``, default
     0..n-1, and the sequence has ``lq`` rows, default n); k, v: [Lk, D].
+    ``bias`` [n, Lk] (optional) is added to the scaled scores before the mask
+    and the softmax: s = scale <q, k> + bias (the additive-bias variant the
+    pages list; -inf entries exclude keys).
     Returns (o [n, D], lse [n]) and P [n, Lk] when ``return_p``."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -69,9 +72,11 @@ def naive_head(q, k, v, scale: float, causal: bool = False, rows=None, lq=None,
     n, lk = q.shape[0], k.shape[0]
     rows = np.arange(n) if rows is None else np.asarray(rows)
     lq = n if lq is None else lq
-    # pass 1: scaled scores, masked
+    # pass 1: scaled scores (plus the bias), masked
     s = scale * (q @ k.T)
-    ok = allowed(rows, lq, lk, causal)
+    if bias is not None:
+        s = s + np.asarray(bias, dtype=np.float64)
+    ok = allowed(rows, lq, lk, causal) & ~np.isneginf(s)
     s = np.where(ok, s, NEG_INF)
     # pass 2: row max and row sum of exp(s - max)
     m = s.max(axis=1) if lk > 0 else np.full(n, NEG_INF)
@@ -131,10 +136,11 @@ def online_head(q, k, v, scale: float, block_c: int, causal: bool = False,
 # batched layouts
 # ---------------------------------------------------------------------------
 def attention_bshd(q, k, v, scale: float, causal: bool = False, heads=None,
-                   rows=None, method: str = "naive", block_c: int = 64):
+                   rows=None, method: str = "naive", block_c: int = 64, bias=None):
     """Dense [B, S, H, D] attention.  ``heads`` limits the work to a list of
     (b, h) pairs and ``rows`` to a list of query rows; outputs not computed are
-    NaN.  Returns (o [B, Sq, H, D], lse [B, H, Sq])."""
+    NaN.  ``bias`` (naive method only) broadcasts to [B, H, Sq, Sk] and is added
+    to the scaled scores.  Returns (o [B, Sq, H, D], lse [B, H, Sq])."""
     B, sq, H, D = q.shape
     lk = k.shape[1]
     o = np.full((B, sq, H, v.shape[3]), np.nan)
@@ -146,7 +152,10 @@ def attention_bshd(q, k, v, scale: float, causal: bool = False, heads=None,
         kk = np.asarray(k[b, :, h, :], dtype=np.float64)
         vv = np.asarray(v[b, :, h, :], dtype=np.float64)
         if method == "naive":
-            oo, ll = naive_head(qq, kk, vv, scale, causal, rows=ridx, lq=sq)
+            bb = None
+            if bias is not None:
+                bb = np.broadcast_to(bias, (B, H, sq, lk))[b, h][ridx]
+            oo, ll = naive_head(qq, kk, vv, scale, causal, rows=ridx, lq=sq, bias=bb)
         else:
             oo, ll = online_head(qq, kk, vv, scale, block_c, causal, rows=ridx, lq=sq)
         o[b, ridx, h, :] = oo

@@ -234,3 +234,44 @@ def test_merge_rows_without_keys():
     o, lse = A.merge_partials([o1, o2], [l1, l2])
     np.testing.assert_array_equal(np.isinf(lse), np.isinf(l1))
     np.testing.assert_allclose(o, o1, rtol=0, atol=1e-15)
+
+
+def test_bias_row_constant_shifts_lse_only():
+    # adding c_i to every score of row i leaves the softmax unchanged
+    q, k, v = _rand(11, 8), _rand(30, 8), _rand(30, 8)
+    c = _rand(11)
+    o1, l1 = A.naive_head(q, k, v, 0.3, True)
+    o2, l2 = A.naive_head(q, k, v, 0.3, True, bias=np.repeat(c[:, None], 30, axis=1))
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l2, l1 + c, rtol=0, atol=1e-12)
+
+
+def test_bias_log_multiplicity_equals_repeated_keys():
+    # a bias of ln(m_j) on key j counts that key m_j times: the same attention
+    # as the key set with key j written out m_j times
+    q, k, v = _rand(9, 6), _rand(12, 6), _rand(12, 6)
+    mult = RNG.integers(1, 4, size=12)
+    o1, l1 = A.naive_head(q, k, v, 0.5, bias=np.repeat(np.log(mult)[None, :], 9, axis=0))
+    o2, l2 = A.naive_head(q, np.repeat(k, mult, axis=0), np.repeat(v, mult, axis=0), 0.5)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+
+
+def test_bias_minus_inf_upper_triangle_is_causal():
+    q, k, v = _rand(16, 8), _rand(16, 8), _rand(16, 8)
+    mask = np.where(np.triu(np.ones((16, 16)), 1) > 0, -np.inf, 0.0)
+    o1, l1 = A.naive_head(q, k, v, 0.4, bias=mask)
+    o2, l2 = A.naive_head(q, k, v, 0.4, True)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-14)
+
+
+def test_bias_against_torch_sdpa_float64():
+    torch = pytest.importorskip("torch")
+    B, S, H, D = 2, 33, 3, 16
+    q, k, v = _rand(B, S, H, D), _rand(B, S, H, D), _rand(B, S, H, D)
+    bias = _rand(B, H, S, S)
+    o, lse = A.attention_bshd(q, k, v, 0.25, False, bias=bias)
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x.transpose(0, 2, 1, 3))) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(bias), scale=0.25)
+    np.testing.assert_allclose(o, ref.numpy().transpose(0, 2, 1, 3), rtol=0, atol=1e-12)
