@@ -49,6 +49,8 @@ def _load():
     I64P = ctypes.POINTER(ctypes.c_int64)
     lib.attn_fwd.argtypes = [I, P, I64P, P, I64P, P, I64P, P, I64P, P, I, I, I, I, I, F, I, P]
     lib.attn_fwd.restype = I
+    lib.attn_fwd_bias.argtypes = [I, P, I64P, P, I64P, P, I64P, P, I64P, P, I64P, P, I, I, I, I, I, F, I, P]
+    lib.attn_fwd_bias.restype = I
     lib.attn_fp8_quantize.argtypes = [P, I64P, P, P, I, I, I, I, I, P, P]
     lib.attn_fp8_quantize.restype = I
     lib.attn_fwd_fp8.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, I, F, I, P]
@@ -132,6 +134,48 @@ def fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None, return_ls
     _check(_lib.attn_fwd(_dtype_code(q.dtype), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
                          _ptr(out), _strides(out), _ptr(lse), B, H, Sq, Sk, D, scale, int(bool(causal)),
                          _stream(stream)))
+    return out, lse
+
+
+def pad_bias(bias):
+    """Copy a [B, H, Sq, Sk] bias into storage whose key rows are padded to a
+    multiple of 8 elements (the layout fwd_bias needs); returns the padded
+    view."""
+    import torch
+    B, H, Sq, Sk = bias.shape
+    pitch = -(-Sk // 8) * 8
+    buf = torch.zeros((B, H, Sq, pitch), dtype=bias.dtype, device=bias.device)
+    buf[..., :Sk] = bias
+    return buf[..., :Sk]
+
+
+def fwd_bias(q, k, v, bias, softmax_scale=None, causal=False, out=None, lse=None, stream=None):
+    """Fused attention forward with an additive score bias: s = scale <q, k> +
+    bias[b, h, i, j].  bias is [B, H, Sq, Sk] of q's dtype (any of its first
+    three dims may be broadcast with stride 0); its key dim must be contiguous
+    and its other strides multiples of 8 (see pad_bias).  Returns (o, lse)."""
+    import torch
+    _require_cuda(q, k, v, bias, out, lse)
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    if k.shape != (B, Sk, H, D) or v.shape != (B, Sk, H, D):
+        raise ValueError("k and v must be [B, Sk, H, D] matching q")
+    if not (q.dtype == k.dtype == v.dtype == bias.dtype):
+        raise TypeError("q, k, v and bias must share a dtype")
+    if bias.dim() != 4 or bias.shape[3] != Sk or any(bias.shape[i] not in (1, n) for i, n in enumerate((B, H, Sq))):
+        raise ValueError("bias must broadcast to [B, H, Sq, Sk]")
+    if Sk > 1 and bias.stride(3) != 1:
+        raise ValueError("bias keys must be contiguous")
+    bst = [0 if bias.shape[i] == 1 else bias.stride(i) for i in range(3)]
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format) if not q.is_contiguous() \
+            else torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _check(_lib.attn_fwd_bias(_dtype_code(q.dtype), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
+                              _strides(v), _ptr(bias), (ctypes.c_int64 * 3)(*bst), _ptr(out), _strides(out),
+                              _ptr(lse), B, H, Sq, Sk, D, scale, int(bool(causal)), _stream(stream)))
     return out, lse
 
 

@@ -91,8 +91,9 @@ bool use_pingpong() {
 template <int D, int DT, bool CAUSAL, int MODE>
 hipError_t launch_one(const attn::FwdArgs& a, hipStream_t s) {
   if constexpr (D <= 128) {
-    // (the ping-pong kernel has no split-key form)
-    if (use_pingpong() && a.n_split <= 1) return attn::launch_fwd16pp<D, DT, CAUSAL, MODE>(a, s);
+    // (the ping-pong kernel has no split-key or bias form)
+    if constexpr (MODE != attn::kDenseBias)
+      if (use_pingpong() && a.n_split <= 1) return attn::launch_fwd16pp<D, DT, CAUSAL, MODE>(a, s);
   }
   return attn::launch_fwd16<D, DT, CAUSAL, MODE>(a, s);
 }
@@ -100,6 +101,10 @@ hipError_t launch_one(const attn::FwdArgs& a, hipStream_t s) {
 template <int D, int DT>
 hipError_t dispatch_causal_mode(const attn::FwdArgs& a, bool causal, int mode, hipStream_t s) {
   using namespace attn;
+  if constexpr (D <= 128) {
+    if (mode == kDenseBias)
+      return causal ? launch_one<D, DT, true, kDenseBias>(a, s) : launch_one<D, DT, false, kDenseBias>(a, s);
+  }
   if (mode == kDense)
     return causal ? launch_one<D, DT, true, kDense>(a, s) : launch_one<D, DT, false, kDense>(a, s);
   if (mode == kVarlen)
@@ -139,11 +144,17 @@ const char* attn_status_string(int status) {
 
 const char* attn_last_error(void) { return g_last_error.c_str(); }
 
-attn_status_t attn_fwd(int dtype, const void* q, const int64_t q_strides[3], const void* k,
-                       const int64_t k_strides[3], const void* v, const int64_t v_strides[3], void* o,
-                       const int64_t o_strides[3], float* lse, int B, int H, int Sq, int Sk, int D,
-                       float softmax_scale, int causal, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and argument set-up of the dense forward (attn_fwd, attn_fwd_bias).
+attn_status_t dense_args(int dtype, const void* q, const int64_t q_strides[3], const void* k,
+                         const int64_t k_strides[3], const void* v, const int64_t v_strides[3], void* o,
+                         const int64_t o_strides[3], float* lse, int B, int H, int Sq, int Sk, int D,
+                         float softmax_scale, int causal, attn::FwdArgs* a, bool* empty) {
   attn_status_t st;
+  *empty = false;
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return fail(ATTN_ERR_INVALID, "dtype %d is not bf16/fp16", dtype);
   if (B < 0 || H < 0 || Sq < 0 || Sk < 0) return fail(ATTN_ERR_INVALID, "negative size (B=%d H=%d Sq=%d Sk=%d)", B, H, Sq, Sk);
   if ((st = check_head_dim(D)) != ATTN_OK) return st;
@@ -153,7 +164,10 @@ attn_status_t attn_fwd(int dtype, const void* q, const int64_t q_strides[3], con
   if ((st = check_strides("k", k_strides)) != ATTN_OK) return st;
   if ((st = check_strides("v", v_strides)) != ATTN_OK) return st;
   if ((st = check_strides("o", o_strides)) != ATTN_OK) return st;
-  if (B == 0 || H == 0 || Sq == 0) return ok();
+  if (B == 0 || H == 0 || Sq == 0) {
+    *empty = true;
+    return ok();
+  }
   if (q == nullptr || o == nullptr) return fail(ATTN_ERR_INVALID, "q or o is NULL");
   if (Sk > 0 && (k == nullptr || v == nullptr)) return fail(ATTN_ERR_INVALID, "k or v is NULL");
   if (Sk > 1 && (k_strides[1] < D || v_strides[1] < D))
@@ -165,19 +179,63 @@ attn_status_t attn_fwd(int dtype, const void* q, const int64_t q_strides[3], con
   const int64_t n_qblk = (Sq + kBR - 1) / kBR;
   if ((int64_t)B * H * n_qblk > INT32_MAX) return fail(ATTN_ERR_INVALID, "problem too large for one launch");
 
-  attn::FwdArgs a{};
-  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-  a.q_sb = q_strides[0]; a.q_ss = q_strides[1]; a.q_sh = q_strides[2];
-  a.k_sb = k_strides[0]; a.k_ss = k_strides[1]; a.k_sh = k_strides[2];
-  a.v_sb = v_strides[0]; a.v_ss = v_strides[1]; a.v_sh = v_strides[2];
-  a.o_sb = o_strides[0]; a.o_ss = o_strides[1]; a.o_sh = o_strides[2];
-  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk;
-  a.scale_log2 = softmax_scale * attn::kLog2e;
-  a.n_qblk = (int)n_qblk;
+  *a = attn::FwdArgs{};
+  a->q = q; a->k = k; a->v = v; a->o = o; a->lse = lse;
+  a->q_sb = q_strides[0]; a->q_ss = q_strides[1]; a->q_sh = q_strides[2];
+  a->k_sb = k_strides[0]; a->k_ss = k_strides[1]; a->k_sh = k_strides[2];
+  a->v_sb = v_strides[0]; a->v_ss = v_strides[1]; a->v_sh = v_strides[2];
+  a->o_sb = o_strides[0]; a->o_ss = o_strides[1]; a->o_sh = o_strides[2];
+  a->B = B; a->H = H; a->Sq = Sq; a->Sk = Sk;
+  a->scale_log2 = softmax_scale * attn::kLog2e;
+  a->n_qblk = (int)n_qblk;
+  a->n_split = 1;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_fwd(int dtype, const void* q, const int64_t q_strides[3], const void* k,
+                       const int64_t k_strides[3], const void* v, const int64_t v_strides[3], void* o,
+                       const int64_t o_strides[3], float* lse, int B, int H, int Sq, int Sk, int D,
+                       float softmax_scale, int causal, void* stream) {
+  attn::FwdArgs a;
+  bool empty;
+  const attn_status_t st = dense_args(dtype, q, q_strides, k, k_strides, v, v_strides, o, o_strides, lse, B, H, Sq,
+                                      Sk, D, softmax_scale, causal, &a, &empty);
+  if (st != ATTN_OK || empty) return st;
   return hip_status(dispatch_fwd16(a, D, dtype, causal != 0, attn::kDense, (hipStream_t)stream), "attn_fwd launch");
 }
 
+attn_status_t attn_fwd_bias(int dtype, const void* q, const int64_t q_strides[3], const void* k,
+                            const int64_t k_strides[3], const void* v, const int64_t v_strides[3],
+                            const void* bias, const int64_t bias_strides[3], void* o, const int64_t o_strides[3],
+                            float* lse, int B, int H, int Sq, int Sk, int D, float softmax_scale, int causal,
+                            void* stream) {
+  attn::FwdArgs a;
+  bool empty;
+  const attn_status_t st = dense_args(dtype, q, q_strides, k, k_strides, v, v_strides, o, o_strides, lse, B, H, Sq,
+                                      Sk, D, softmax_scale, causal, &a, &empty);
+  if (st != ATTN_OK) return st;
+  if (D > 128) return fail(ATTN_ERR_UNSUPPORTED, "the score bias supports head_dim 64 and 128 (got %d)", D);
+  if (bias_strides == nullptr) return fail(ATTN_ERR_INVALID, "bias_strides is NULL");
+  for (int i = 0; i < 3; ++i)
+    if (bias_strides[i] < 0 || bias_strides[i] % 8 != 0)
+      return fail(ATTN_ERR_INVALID, "bias strides must be non-negative multiples of 8 elements");
+  if (empty) return ok();
+  if (Sk > 0 && (bias == nullptr || !aligned16(bias))) return fail(ATTN_ERR_INVALID, "bias must be a 16-byte aligned pointer");
+  if (2 * ((int64_t)(Sq - 1) * bias_strides[2] + ((Sk + 7) & ~7)) >= (int64_t(1) << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "one (batch, head) plane of the bias must span less than 2^31 bytes");
+  a.bias = bias;
+  a.bias_sb = bias_strides[0]; a.bias_sh = bias_strides[1]; a.bias_ss = bias_strides[2];
+  return hip_status(dispatch_fwd16(a, D, dtype, causal != 0, attn::kDenseBias, (hipStream_t)stream),
+                    "attn_fwd_bias launch");
+}
+
 }  // extern "C"
+
+
 
 namespace {
 

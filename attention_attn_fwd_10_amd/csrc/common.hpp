@@ -100,6 +100,8 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t nbytes) {
 }
 __device__ void raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) void* lds, int size, int voffset,
                                     int soffset, int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+// buffer_load_dwordx4 into registers (zeros past the resource's range)
+__device__ i32x4 raw_buffer_load_v4(i32x4 rsrc, int voffset, int soffset, int aux) __asm("llvm.amdgcn.raw.buffer.load.v4i32");
 // Asynchronous buffer -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds):
 // lane l reads rsrc.base + voffset (zeros when out of range) and writes
 // lds_wave_base + 16*l; lds_wave_base must be the same for every lane.
@@ -131,7 +133,7 @@ __device__ __forceinline__ int xcd_remap(int p, int n) {
 // ---------------------------------------------------------------------------
 // launch-side argument blocks (plain data, passed by value)
 // ---------------------------------------------------------------------------
-enum KvMode { kDense = 0, kVarlen = 1, kPaged = 2 };
+enum KvMode { kDense = 0, kVarlen = 1, kPaged = 2, kDenseBias = 3 };
 
 struct FwdArgs {
   const void* q;
@@ -155,6 +157,10 @@ struct FwdArgs {
   // split keys (varlen / paged only): n_split > 1 gives every (tile, split) a
   // workgroup over key tiles [split * split_tiles, (split + 1) * split_tiles);
   // each writes its normalised partial output and logsumexp in fp32
+  // additive score bias (dense only): [B, H, Sq, Sk] by these element strides
+  // (keys contiguous; a stride of 0 broadcasts)
+  const void* bias;
+  int64_t bias_sb, bias_sh, bias_ss;
   int n_split;
   int split_tiles;
   float* part_o;             // [n_split, total_q, H, D]

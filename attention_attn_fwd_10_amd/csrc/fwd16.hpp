@@ -64,6 +64,9 @@ template <int D, int DT, bool CAUSAL, int MODE>
 __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(FwdArgs a) {
   using C = Fwd16Cfg<D>;
   constexpr int BR = C::BR, BC = C::BC, KP = C::KP, VP = C::VP, CPR = C::CPR;
+  constexpr bool DENSE = MODE == kDense || MODE == kDenseBias;
+  constexpr bool BIAS = MODE == kDenseBias;
+  static_assert(!BIAS || D <= 128, "the score bias is supported up to head dim 128");
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::K_ELEMS + 2 * C::V_ELEMS];
   uint16_t* const ks_base = smem;
   uint16_t* const vs_base = smem + 2 * C::K_ELEMS;
@@ -75,7 +78,7 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
   // ---- work item: (b, h, query block) -------------------------------------
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   int b, h, qblk, split = 0;
-  if constexpr (MODE == kDense) {
+  if constexpr (DENSE) {
     const int bh = t / a.n_qblk;
     qblk = t - bh * a.n_qblk;
     if (CAUSAL) qblk = a.n_qblk - 1 - qblk;  // longest key ranges first
@@ -103,7 +106,7 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
 
   int Lq, Lk;
   int64_t qoff, ooff, koff, voff, lse_base;
-  if constexpr (MODE == kDense) {
+  if constexpr (DENSE) {
     Lq = a.Sq;
     Lk = a.Sk;
     qoff = b * a.q_sb + h * a.q_sh;
@@ -137,7 +140,7 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
   }
   // key tiles [j0, j1) of this work item (all of them unless keys are split)
   int j0 = 0, j1 = n_kv;
-  if constexpr (MODE != kDense) {
+  if constexpr (!DENSE) {
     if (a.n_split > 1) {
       j0 = min(n_kv, split * a.split_tiles);
       j1 = min(n_kv, j0 + a.split_tiles);
@@ -163,6 +166,18 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
   // Slot s of a tile (16 bytes) holds LDS row s / SLOTS, column chunk s % SLOTS;
   // chunks >= CPR are padding and are not copied.  K rows are stored with the
   // rows of each 32-row group in swz23 order, V rows in natural order.
+  // score bias: one buffer resource over this (b, h) plane (rows of bias_ss
+  // elements, the last one readable up to a multiple of 8 elements, so that no
+  // 16-byte read straddles the range end; reads past it return zeros), and
+  // this lane's row offset
+  i32x4 bias_rsrc = {0, 0, 0, 0};
+  uint32_t bias_row = 0;
+  if constexpr (BIAS) {
+    const uint16_t* bp = (const uint16_t*)a.bias + b * a.bias_sb + h * a.bias_sh;
+    const uint64_t nbytes = 2ull * ((uint64_t)(Lq - 1) * (uint64_t)a.bias_ss + (uint64_t)((Lk + 7) & ~7));
+    bias_rsrc = make_rsrc(bp, (uint32_t)min(nbytes, (uint64_t)0x7fff0000u));
+    bias_row = 2u * (uint32_t)((int64_t)min(qi, Lq - 1) * a.bias_ss);
+  }
   const uint16_t* const kg = (const uint16_t*)a.k + koff;
   const uint16_t* const vg = (const uint16_t*)a.v + voff;
   auto k_slot = [&](int ii, int& key_local, int& chunk) {
@@ -279,8 +294,48 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
     (void)agpr_hint;
   }
 
+  // score bias of this lane's row for the tile at key0: four 16-byte loads,
+  // one per run of 8 consecutive keys it holds (issued before the tile's copy
+  // of the next tile so that waiting for them does not wait for that copy)
+  struct BiasRaw {
+    i32x4 r[BC / 32][2];
+  };
+  auto bias_fetch = [&](int key0) {
+    BiasRaw br;
+#pragma unroll
+    for (int tt = 0; tt < BC / 32; ++tt)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+        br.r[tt][half] = raw_buffer_load_v4(bias_rsrc, (int)(bias_row + 2u * (uint32_t)(key0 + 32 * tt + 16 * half + 8 * hh)), 0, 0);
+    return br;
+  };
+  // s <- s * c2 + bias * log2(e): the scores in exp2 units with the bias added
+  auto bias_apply = [&](f32x16 (&sc)[BC / 32], const BiasRaw& br) {
+#pragma unroll
+    for (int tt = 0; tt < BC / 32; ++tt)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t u = (uint32_t)br.r[tt][half][w];
+          float lo, hi;
+          if constexpr (DT == kBF16) {
+            lo = __uint_as_float(u << 16);
+            hi = __uint_as_float(u & 0xffff0000u);
+          } else {
+            lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu));
+            hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+          }
+          const int r = 8 * half + 2 * w;
+          sc[tt][r] = fmaf(sc[tt][r], c2, lo * kLog2e);
+          sc[tt][r + 1] = fmaf(sc[tt][r + 1], c2, hi * kLog2e);
+        }
+  };
+  // with a bias the scores are already in exp2 units after bias_apply
+  const float c2k = BIAS ? 1.f : c2;
+
   // one key tile (head dims up to 128)
-  auto compute = [&](int key0, int buf) {
+  auto compute = [&](int key0, int buf, const BiasRaw& br) {
     if (!wave_active) return;
     if (CAUSAL && key0 > wave_last_key) return;  // tile fully masked for this wave
     // S^T = K Q^T
@@ -311,6 +366,7 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
         __builtin_amdgcn_s_setprio(0);
       }
     }
+    if constexpr (BIAS) bias_apply(s, br);
     // register r of tile tt holds key key0 + 32tt + 16(r/8) + 8hh + r%8
     const bool need_mask = (key0 + BC > Lk) || (CAUSAL && key0 + BC - 1 > qw + diag);
     if (need_mask) {
@@ -328,7 +384,7 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
     for (int tt = 0; tt < BC / 32; ++tt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tt][r]);
-    const float mxs = halfwave_max(mx) * c2;
+    const float mxs = halfwave_max(mx) * c2k;
     // move the running max only when some row's new max exceeds it by > 2^8
     if (__builtin_amdgcn_ballot_w64(mxs > m_run + kLazyRescale) != 0) {
       const float m_new = fmaxf(m_run, mxs);
@@ -362,7 +418,7 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[e] = fast_exp2(fmaf(s[tt][r0p + e], c2, nb));
+        p[e] = fast_exp2(fmaf(s[tt][r0p + e], c2k, nb));
         psum += p[e];
       }
       const u32x4 pk = {pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3]), pack2<DT>(p[4], p[5]),
@@ -488,8 +544,10 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
     if constexpr (D != 256) {
       for (int j = j0; j < j1; ++j) {
         const int buf = j & 1;
+        BiasRaw br{};
+        if constexpr (BIAS) br = bias_fetch(j * BC);
         if (j + 1 < j1) dma_tile((j + 1) * BC, buf ^ 1);  // lands while tile j is computed
-        compute(j * BC, buf);
+        compute(j * BC, buf, br);
         wait_vmem();
         __syncthreads();
       }
@@ -527,7 +585,7 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
 
   // ---- epilogue: o / l, lse = ln2 * (m + log2 l) -----------------------------
   const float l_tot = halfwave_sum(l_run);
-  if constexpr (MODE != kDense) {
+  if constexpr (!DENSE) {
     if (a.n_split > 1) {
       // partial result of this key split, in fp32; register r of tile dt is
       // head-dim column 32dt + 16(r/8) + 8hh + r%8
@@ -573,11 +631,17 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
 template <int D, int DT, bool CAUSAL, int MODE>
 hipError_t launch_fwd16(const FwdArgs& a, hipStream_t s) {
   // dense: every (b, h, q-block); varlen: an upper bound on the compact tile list
-  const int n = MODE == kDense ? a.B * a.H * a.n_qblk
+  const int n = (MODE == kDense || MODE == kDenseBias) ? a.B * a.H * a.n_qblk
                                : a.H * ((a.total_q + Fwd16Cfg<D>::BR - 1) / Fwd16Cfg<D>::BR + a.B) * max(a.n_split, 1);
   hipLaunchKernelGGL((fwd16_kernel<D, DT, CAUSAL, MODE>), dim3(n), dim3(256), 0, s, a);
   return hipGetLastError();
 }
+
+#define ATTN_INSTANTIATE_FWD16_BIAS(D)                                                        \
+  template hipError_t launch_fwd16<D, kBF16, false, kDenseBias>(const FwdArgs&, hipStream_t); \
+  template hipError_t launch_fwd16<D, kBF16, true, kDenseBias>(const FwdArgs&, hipStream_t);  \
+  template hipError_t launch_fwd16<D, kFP16, false, kDenseBias>(const FwdArgs&, hipStream_t); \
+  template hipError_t launch_fwd16<D, kFP16, true, kDenseBias>(const FwdArgs&, hipStream_t);
 
 #define ATTN_INSTANTIATE_FWD16(D)                                          \
   template hipError_t launch_fwd16<D, kBF16, false, kDense>(const FwdArgs&, hipStream_t);  \

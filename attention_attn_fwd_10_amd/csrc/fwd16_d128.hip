@@ -3,5 +3,6 @@
 
 namespace attn {
 ATTN_INSTANTIATE_FWD16(128)
+ATTN_INSTANTIATE_FWD16_BIAS(128)
 ATTN_INSTANTIATE_FWD16PP(128)
 }  // namespace attn

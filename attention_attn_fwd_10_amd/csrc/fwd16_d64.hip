@@ -3,5 +3,6 @@
 
 namespace attn {
 ATTN_INSTANTIATE_FWD16(64)
+ATTN_INSTANTIATE_FWD16_BIAS(64)
 ATTN_INSTANTIATE_FWD16PP(64)
 }  // namespace attn

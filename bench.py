@@ -77,6 +77,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--sweep", action="store_true", help="also time the 16384-token seq sweep (extra output)")
     p.add_argument("--no-decode", action="store_true", help="skip the long-cache decoding leg")
+    p.add_argument("--no-bias", action="store_true", help="skip the additive-bias leg")
     p.add_argument("--source-hash", action="store_true", help="print the timed kernel's source hash and exit")
     p.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (calibrates the FETCH_SIZE/WRITE_SIZE counters)")
@@ -201,6 +202,9 @@ def main():
     if not args.no_decode:
         result["decode"] = bench_decode(A, W, args)
 
+    if not args.no_bias:
+        result["bias"] = bench_bias(A, W, args)
+
     if args.sweep:
         result["sweep"] = bench_sweep(A, W, args)
 
@@ -275,6 +279,35 @@ def bench_decode(A, W, args):
             "ms_whole_sequence": round(ms_whole, 4), "ms_split": round(ms_split, 4),
             "gbs_split": round(gbs, 1), "gbs_whole_sequence": round(algo / (ms_whole * 1e-3) / 1e9, 1),
             "pct_of_hbm_peak": round(100 * gbs / 8000.0, 1), "algorithmic_bytes": algo}
+
+
+def bench_bias(A, W, args):
+    """Additive score bias (attn_fwd_bias) on batch 1 x seq 8192 x 16 heads x
+    d128: a full [B, H, Sq, Sk] bf16 bias (2 GiB read once) and a per-(head,
+    key) bias broadcast over queries, beside the same problem without bias."""
+    import torch
+    B, S, H, D = 1, 8192, 16, 128
+    g = torch.Generator(device="cuda").manual_seed(21)
+    q, k, v = (torch.randn((B, S, H, D), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+    full = torch.randn((B, H, S, S), generator=g, device="cuda").to(torch.bfloat16)
+    per_key = torch.randn((1, H, 1, S), generator=g, device="cuda").to(torch.bfloat16)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    flops = 4.0 * B * H * S * S * D
+    steps = max(5, args.steps // 3)
+    out = {"workload": f"bias_b{B}_h{H}_s{S}_d{D}"}
+    ms0 = time_launches(lambda: A.fwd(q, k, v, None, False, out=o, lse=lse), steps, 10)
+    out["ms_no_bias"] = round(ms0, 4)
+    for name, bias in (("full", full), ("per_head_key", per_key)):
+        ms = time_launches(lambda: A.fwd_bias(q, k, v, bias, None, False, out=o, lse=lse), steps, 10)
+        out[f"ms_{name}"] = round(ms, 4)
+        out[f"tflops_{name}"] = round(flops / (ms * 1e-3) / 1e12, 1)
+        print(f"[bench] bias {name}: {ms:.3f} ms ({flops / (ms * 1e-3) / 1e12:.0f} TFLOP/s; no bias {ms0:.3f} ms)",
+              file=sys.stderr, flush=True)
+    out["full_bias_bytes"] = full.numel() * 2
+    out["full_bias_gbs"] = round(full.numel() * 2 / (out["ms_full"] * 1e-3) / 1e9, 1)
+    del full
+    return out
 
 
 def bench_sweep(A, W, args):

@@ -79,6 +79,31 @@ attn_status_t attn_fwd(int dtype,
                        float softmax_scale, int causal, void* stream);
 
 /*
+ * attn_fwd_bias — attn_fwd with an additive score bias: s = scale <q, k> +
+ * bias[b, h, i, j] before the causal mask and the softmax (the additive-bias
+ * variant listed on the FlashAttention-2-on-Hopper page).  -inf entries
+ * exclude a key; a row whose keys are all excluded gets O = 0, LSE = -inf.
+ *
+ * bias: same dtype as q, element (b, h, i, j) at
+ *   bias + b*bias_strides[0] + h*bias_strides[1] + i*bias_strides[2] + j
+ *   (keys contiguous; a stride of 0 broadcasts over that index).  The strides
+ *   must be multiples of 8 elements and the pointer 16-byte aligned; every
+ *   row, the last one included, must be readable up to Sk rounded up to a
+ *   multiple of 8 elements (padding values are never used); one (b, h) plane
+ *   must span less than 2^31 bytes.
+ * D must be 64 or 128 (ATTN_ERR_UNSUPPORTED otherwise).  Other arguments as
+ * for attn_fwd.
+ */
+attn_status_t attn_fwd_bias(int dtype,
+                            const void* q, const int64_t q_strides[3],
+                            const void* k, const int64_t k_strides[3],
+                            const void* v, const int64_t v_strides[3],
+                            const void* bias, const int64_t bias_strides[3],
+                            void* o, const int64_t o_strides[3], float* lse,
+                            int B, int H, int Sq, int Sk, int D,
+                            float softmax_scale, int causal, void* stream);
+
+/*
  * attn_fp8_quantize — the 8-bit prologue for one tensor.
  * ("Fused attention kernel" page, section "8-bit forward pass": e4m3 format,
  * block quantisation, incoherent processing with a random-sign Hadamard

@@ -35,6 +35,7 @@ def lib():
                                    ctypes.c_size_t, P]
     L.attn_fwd_splitkv_workspace_bytes.argtypes = [I, I, I, I]
     L.attn_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
+    L.attn_fwd_bias.argtypes = [I, P, I64P, P, I64P, P, I64P, P, I64P, P, I64P, P, I, I, I, I, I, F, I, P]
     L.attn_status_string.argtypes = [I]
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_last_error.restype = ctypes.c_char_p
@@ -50,7 +51,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("attn_fwd", "attn_fp8_quantize", "attn_fwd_fp8", "attn_fwd_varlen", "attn_fwd_splitkv",
-              "attn_fwd_splitkv_workspace_bytes", "attn_status_string", "attn_last_error"):
+              "attn_fwd_splitkv_workspace_bytes", "attn_fwd_bias", "attn_status_string", "attn_last_error"):
         assert n in names
 
 
@@ -154,6 +155,19 @@ def test_splitkv_validation(lib):
     assert f(page=48) == INVALID                      # the varlen checks apply
     assert f(D=80) == UNSUPPORTED
     assert f(B=0) == OK and f(total_q=0) == OK          # empty problems: no-op
+
+
+def test_bias_validation(lib):
+    def f(D=128, bs=_s(1 << 20, 1024, 64), bias=A16, Sk=4, B=1):
+        return lib.attn_fwd_bias(0, A16, GOOD, A16, GOOD, A16, GOOD, bias, bs, A16, GOOD, None, B, 1, 4, Sk, D, 0.1,
+                                 0, None)
+    assert f(D=256) == UNSUPPORTED
+    assert f(bs=_s(1 << 20, 1024, 12)) == INVALID     # row stride not a multiple of 8
+    assert f(bs=_s(-8, 0, 8)) == INVALID              # negative stride
+    assert f(bias=None) == INVALID
+    assert f(bias=A_ODD) == INVALID
+    assert f(bs=_s(0, 0, 1 << 29)) == UNSUPPORTED     # a plane beyond 2^31 bytes
+    assert f(B=0) == OK
 
 
 def test_splitkv_workspace_bytes(lib):
