@@ -80,8 +80,9 @@ attn_status_t attn_fwd(int dtype,
 
 /*
  * attn_fwd_bias — attn_fwd with an additive score bias: s = scale <q, k> +
- * bias[b, h, i, j] before the causal mask and the softmax (the additive-bias
- * variant listed on the FlashAttention-2-on-Hopper page).  -inf entries
+ * bias[b, h, i, j] before the causal mask and the softmax (Bias is among the
+ * features the StreamHPC case study, section "Our approach", adds to its
+ * fused kernel).  -inf entries
  * exclude a key; a row whose keys are all excluded gets O = 0, LSE = -inf.
  *
  * bias: same dtype as q, element (b, h, i, j) at
