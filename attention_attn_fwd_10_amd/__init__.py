@@ -10,8 +10,8 @@ The entry points mirror the C ABI in ``include/attn.h``:
 * ``fwd_varlen``     -> ``attn_fwd_varlen``     (packed sequences, optional paged KV)
 
 Tensors use the [batch, seq, heads, head_dim] layout (varlen: [tokens, heads,
-head_dim]).  If the library has not been built, importing this package fails:
-there is no fallback implementation.
+head_dim]).  If the library has not been built, the first call raises
+ImportError: there is no fallback implementation.
 """
 from __future__ import annotations
 
@@ -69,7 +69,20 @@ def _load():
     return lib
 
 
-_lib = _load()
+class _Library:
+    """The loaded ``libattn_fwd.so``, opened at the first call into it, so
+    that the build step can import this package before the library exists.
+    A call without the library raises ImportError (there is no fallback)."""
+
+    _handle = None
+
+    def __getattr__(self, name):
+        if _Library._handle is None:
+            _Library._handle = _load()
+        return getattr(_Library._handle, name)
+
+
+_lib = _Library()
 
 
 def _check(status: int):

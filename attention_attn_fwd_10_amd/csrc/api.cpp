@@ -17,7 +17,7 @@
 
 namespace attn {
 template <int D, int DT, bool CAUSAL, int MODE>
-hipError_t launch_fwd16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd16(FwdArgs a, hipStream_t s);
 template <int D, int DT, bool CAUSAL, int MODE>
 hipError_t launch_fwd16pp(FwdArgs a, hipStream_t s);
 hipError_t launch_fp8_quantize(const QuantArgs& a, int D, hipStream_t s);

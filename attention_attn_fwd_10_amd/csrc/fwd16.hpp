@@ -7,12 +7,18 @@
 // is scored, and o / l and lse = m + log l are formed once at the end.
 //
 // How it maps to CDNA4:
-//  * one workgroup = 4 waves = 128 query rows; each wave owns 32 rows and keeps
-//    its Q fragments in registers for the whole key loop;
+//  * one workgroup = 4 waves = 128 query rows (8 waves = 256 rows for the
+//    dense causal layout); each wave owns 32 rows and keeps its Q fragments in
+//    registers for the whole key loop;
 //  * K and V tiles of 64 keys go through a two-stage LDS ring filled by
-//    asynchronous global -> LDS copies (global_load_lds_dwordx4): the copies of
-//    tile j+1 are issued before the matrix work on tile j and need no
+//    asynchronous global -> LDS copies (buffer_load_dwordx4 ... lds): the
+//    copies of a tile are issued a step before it is used and need no
 //    registers (one barrier per tile);
+//  * tiles that need no mask are software-pipelined inside each wave: the
+//    score MFMAs of tile j+1 are interleaved, in a fixed order, with the
+//    softmax of tile j, then the P V MFMAs of tile j with its last
+//    exponentials, so one wave keeps the matrix core and the vector ALU busy
+//    at the same time; tiles with a mask run one at a time;
 //  * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16, so
 //    every lane owns one query column: the row max and row sum are in-lane
 //    reductions plus one half-wave exchange (v_permlane32_swap);
@@ -31,13 +37,25 @@
 //    memory lies past the sequence never reaches the result.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace attn {
 
-template <int D>
+// Waves per workgroup: 8 (256 query rows, one workgroup per CU, each K/V tile
+// copied once for all 8 waves) for the dense causal layout at head dims up to
+// 128, where it measured faster; otherwise 4 (128 rows, two workgroups per CU
+// whose waves run out of phase), which measured faster without the mask, suits
+// the packed layouts, whose sequences may be short, and is the only choice at
+// head dim 256, where a SIMD holds one wave.
+constexpr int fwd16_waves(int D, int MODE, bool CAUSAL) {
+  return D <= 128 && CAUSAL && (MODE == 0 || MODE == 3) ? 8 : 4;
+}
+
+template <int D, int NW = 4>
 struct Fwd16Cfg {
-  static constexpr int BR = 128;                  // query rows per workgroup
+  static constexpr int BR = 32 * NW;              // query rows per workgroup
   static constexpr int BC = 64;                   // keys per tile
   static constexpr int CPR = D / 8;               // 16-byte chunks per row
   // LDS row pitches in 16-byte slots.  K: one pad slot, so the 16 rows read by
@@ -51,25 +69,44 @@ struct Fwd16Cfg {
   static constexpr int K_ELEMS = BC * KP;
   static constexpr int V_ELEMS = BC * VP;
   // a tile is copied by KSLOTS (VSLOTS) wave instructions of 64 x 16 bytes,
-  // dealt round-robin to the 4 waves
-  static constexpr int KI_W = (KSLOTS + 3) / 4;
-  static constexpr int VI_W = (VSLOTS + 3) / 4;
+  // dealt round-robin to the NW waves
+  static constexpr int KI_W = (KSLOTS + NW - 1) / NW;
+  static constexpr int VI_W = (VSLOTS + NW - 1) / NW;
+  // waves per SIMD: two at head dims up to 128 (one workgroup of 8 waves or
+  // two of 4 per CU), one at 256
   static constexpr int WAVES_PER_EU = D <= 128 ? 2 : 1;
+  static constexpr int MIN_BLOCKS = WAVES_PER_EU * 4 / NW;
 };
 
 // Probabilities may grow to 2^kLazyRescale before the running max is moved.
 constexpr float kLazyRescale = 8.0f;
 
 template <int D, int DT, bool CAUSAL, int MODE>
-__global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(FwdArgs a) {
-  using C = Fwd16Cfg<D>;
+__global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg<D, fwd16_waves(D, MODE, CAUSAL)>::MIN_BLOCKS))
+    fwd16_kernel(FwdArgs a) {
+  constexpr int NW = fwd16_waves(D, MODE, CAUSAL);
+  using C = Fwd16Cfg<D, NW>;
   constexpr int BR = C::BR, BC = C::BC, KP = C::KP, VP = C::VP, CPR = C::CPR;
   constexpr bool DENSE = MODE == kDense || MODE == kDenseBias;
   constexpr bool BIAS = MODE == kDenseBias;
   static_assert(!BIAS || D <= 128, "the score bias is supported up to head dim 128");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::K_ELEMS + 2 * C::V_ELEMS];
-  uint16_t* const ks_base = smem;
-  uint16_t* const vs_base = smem + 2 * C::K_ELEMS;
+  // The two stages of the K and V rings are separate arrays: when a stage is
+  // named by a compile-time constant, the compiler can tell the copies into
+  // one stage from the reads of the other and does not make those reads wait
+  // for the copies (with a run-time stage index it waits for all of them).
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k0[C::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k1[C::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v0[C::V_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v1[C::V_ELEMS];
+  // stage -> array; `buf` is an int or a std::integral_constant
+  auto kbuf = [&](auto buf) -> uint16_t* {
+    if constexpr (std::is_same_v<decltype(buf), int>) return buf ? lds_k1 : lds_k0;
+    else return decltype(buf)::value ? lds_k1 : lds_k0;
+  };
+  auto vbuf = [&](auto buf) -> uint16_t* {
+    if constexpr (std::is_same_v<decltype(buf), int>) return buf ? lds_v1 : lds_v0;
+    else return decltype(buf)::value ? lds_v1 : lds_v0;
+  };
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
@@ -181,13 +218,13 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
   const uint16_t* const kg = (const uint16_t*)a.k + koff;
   const uint16_t* const vg = (const uint16_t*)a.v + voff;
   auto k_slot = [&](int ii, int& key_local, int& chunk) {
-    const int s = 64 * (wave + 4 * ii) + lane;
+    const int s = 64 * (wave + NW * ii) + lane;
     const int r = s / C::KSLOTS;
     chunk = s - r * C::KSLOTS;
     key_local = (r & ~31) | swz23(r & 31);
   };
   auto v_slot = [&](int ii, int& key_local, int& chunk) {
-    const int s = 64 * (wave + 4 * ii) + lane;
+    const int s = 64 * (wave + NW * ii) + lane;
     key_local = s / C::VSLOTS;
     chunk = s - key_local * C::VSLOTS;
   };
@@ -215,48 +252,55 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
       return key;
     }
   };
-  auto dma_tile = [&](int key0, int buf) {
-    uint16_t* kb = ks_base + buf * C::K_ELEMS;
-    uint16_t* vb = vs_base + buf * C::V_ELEMS;
-    // A 64-key tile is contiguous in memory for the dense and varlen layouts,
-    // and inside one page of a paged cache whose pages hold >= 64 tokens.  Then
-    // one buffer resource per tile covers rows key0 .. Lk-1 (rows past the
-    // sequence end read as zeros) and every copy is a single buffer load.
-    const bool contiguous = MODE != kPaged || a.page_shift >= 6;
+  // A 64-key tile is contiguous in memory for the dense and varlen layouts,
+  // and inside one page of a paged cache whose pages hold >= 64 tokens.  Then
+  // one buffer resource per tile covers rows key0 .. Lk-1 (rows past the
+  // sequence end read as zeros) and every copy is a single buffer load.
+  // Smaller pages: each row through the block table; rows past Lk repeat row
+  // Lk-1 (finite data, masked out of the scores and multiplied by p = 0).
+  const bool contiguous = MODE != kPaged || a.page_shift >= 6;
+  auto tile_row0 = [&](int key0) -> int64_t {  // element row of key0 (paged: page base + slot)
+    if constexpr (MODE == kPaged) {
+      const int page = a.block_table[(int64_t)b * a.max_pages + (key0 >> a.page_shift)];
+      return ((int64_t)page << a.page_shift) + (key0 & ((1 << a.page_shift) - 1));
+    } else {
+      return key0;
+    }
+  };
+  // (tile ranges are clamped below 2^31; the host limits seq strides to 2^24
+  // elements, so a tile's 64 rows always lie inside them)
+  auto dma_k = [&](int key0, auto buf) {
+    uint16_t* kb = kbuf(buf);
     if (contiguous) {
-      int64_t row0 = key0;  // element row of key0 (paged: page base + slot)
-      if constexpr (MODE == kPaged) {
-        const int page = a.block_table[(int64_t)b * a.max_pages + (key0 >> a.page_shift)];
-        row0 = ((int64_t)page << a.page_shift) + (key0 & ((1 << a.page_shift) - 1));
-      }
-      // (the range is clamped below 2^31; the host limits seq strides to 2^24
-      // elements, so a tile's 64 rows always lie inside it)
       const uint64_t kn = 2ull * (uint64_t)(Lk - key0) * (uint64_t)a.k_ss;
-      const uint64_t vn = 2ull * (uint64_t)(Lk - key0) * (uint64_t)a.v_ss;
-      const i32x4 kr = make_rsrc(kg + row0 * a.k_ss, (uint32_t)min(kn, (uint64_t)0x7fff0000u));
-      const i32x4 vr = make_rsrc(vg + row0 * a.v_ss, (uint32_t)min(vn, (uint64_t)0x7fff0000u));
+      const i32x4 kr = make_rsrc(kg + tile_row0(key0) * a.k_ss, (uint32_t)min(kn, (uint64_t)0x7fff0000u));
 #pragma unroll
       for (int ii = 0; ii < C::KI_W; ++ii)
-        if (wave + 4 * ii < C::KSLOTS) dma16_buf(kr, k_boff[ii], kb + (wave + 4 * ii) * 512);
-#pragma unroll
-      for (int ii = 0; ii < C::VI_W; ++ii)
-        if (wave + 4 * ii < C::VSLOTS) dma16_buf(vr, v_boff[ii], vb + (wave + 4 * ii) * 512);
+        if (wave + NW * ii < C::KSLOTS) dma16_buf(kr, k_boff[ii], kb + (wave + NW * ii) * 512);
     } else {
-      // pages of 16 or 32 tokens: each row through the block table; rows past
-      // Lk repeat row Lk-1 (finite data, masked out of the scores and
-      // multiplied by p = 0)
 #pragma unroll
       for (int ii = 0; ii < C::KI_W; ++ii) {
-        const int i = wave + 4 * ii;
+        const int i = wave + NW * ii;
         if (i < C::KSLOTS) {
           int kl, ch;
           k_slot(ii, kl, ch);
           if (ch < CPR) dma16(kg + row_of(min(key0 + kl, Lk - 1)) * a.k_ss + ch * 8, kb + i * 512);
         }
       }
+    }
+  };
+  auto dma_v = [&](int key0, auto buf) {
+    uint16_t* vb = vbuf(buf);
+    if (contiguous) {
+      const uint64_t vn = 2ull * (uint64_t)(Lk - key0) * (uint64_t)a.v_ss;
+      const i32x4 vr = make_rsrc(vg + tile_row0(key0) * a.v_ss, (uint32_t)min(vn, (uint64_t)0x7fff0000u));
+#pragma unroll
+      for (int ii = 0; ii < C::VI_W; ++ii)
+        if (wave + NW * ii < C::VSLOTS) dma16_buf(vr, v_boff[ii], vb + (wave + NW * ii) * 512);
+    } else {
 #pragma unroll
       for (int ii = 0; ii < C::VI_W; ++ii) {
-        const int i = wave + 4 * ii;
+        const int i = wave + NW * ii;
         if (i < C::VSLOTS) {
           int kl, ch;
           v_slot(ii, kl, ch);
@@ -264,6 +308,10 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
         }
       }
     }
+  };
+  auto dma_tile = [&](int key0, int buf) {
+    dma_k(key0, buf);
+    dma_v(key0, buf);
   };
 
   // V^T operand addressing for ds_read_b64_tr_b16: lane (group g, index j)
@@ -339,7 +387,7 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
     if (!wave_active) return;
     if (CAUSAL && key0 > wave_last_key) return;  // tile fully masked for this wave
     // S^T = K Q^T
-    const uint16_t* ks = ks_base + buf * C::K_ELEMS + l32 * KP + 8 * hh;
+    const uint16_t* ks = kbuf(buf) + l32 * KP + 8 * hh;
     f32x16 s[BC / 32];
     {
       // the K operands of the tile are read before the first MFMA so that the
@@ -407,7 +455,7 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
       m_run = m_new;
     }
     const float nb = m_run == -INFINITY ? 0.f : -m_run;
-    const uint16_t* vs = vs_base + buf * C::V_ELEMS + vtr_off;
+    const uint16_t* vs = vbuf(buf) + vtr_off;
     float psum = 0.f;
     // O^T += V^T P^T over four 16-key chunks: the exponentials of a chunk, then
     // its D/32 MFMAs, so the matrix work of one chunk overlaps the next chunk's
@@ -440,7 +488,7 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
   auto tile_active = [&](int key0) { return wave_active && !(CAUSAL && key0 > wave_last_key); };
   // S^T = K Q^T, masking and the row max; true when the running max must move
   auto scores_max = [&](int key0, int buf) -> bool {
-    const uint16_t* ks = ks_base + buf * C::K_ELEMS + l32 * KP + 8 * hh;
+    const uint16_t* ks = kbuf(buf) + l32 * KP + 8 * hh;
     {
       // the K operands of the tile are read before the first MFMA so that the
       // LDS latency is paid once (at D = 256 in quarters, which keeps them
@@ -513,7 +561,7 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
   // chunk overlaps the next chunk's exponentials
   auto softmax_pv = [&](int buf) {
     const float nb = m_run == -INFINITY ? 0.f : -m_run;
-    const uint16_t* vs = vs_base + buf * C::V_ELEMS + vtr_off;
+    const uint16_t* vs = vbuf(buf) + vtr_off;
     float psum = 0.f;
 #pragma unroll
     for (int c = 0; c < BC / 16; ++c) {
@@ -536,14 +584,208 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
     l_run += psum;
   };
 
-  // ---- key loop: two-stage LDS ring ------------------------------------------
+  // ---- software-pipelined pieces (head dims up to 128, tiles needing no mask)
+  // S^T = K Q^T of one tile
+  auto qk_tile = [&](auto buf, f32x16 (&sc)[BC / 32]) {
+    const uint16_t* ks = kbuf(buf) + l32 * KP + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int tt = 0; tt < BC / 32; ++tt) {
+        const u32x4 kop = *(const u32x4*)(ks + tt * 32 * KP + 16 * kk);
+        sc[tt] = mfma32<DT>(kop, qf[kk], kk == 0 ? zero16 : sc[tt]);
+      }
+  };
+  // row max, lazy max move, P = exp2(c2 s - m) packed to 16 bits and the row
+  // sum, with no branch; returns whether the running max moved, in which case
+  // the accumulators must still be multiplied by alpha
+  auto softmax_pack = [&](const f32x16 (&sc)[BC / 32], u32x4 (&pk)[BC / 16], float& alpha) -> bool {
+    float mx = sc[0][0];
+#pragma unroll
+    for (int tt = 0; tt < BC / 32; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[tt][r]);
+    const float mxs = halfwave_max(mx) * c2;
+    const bool moved = __builtin_amdgcn_ballot_w64(mxs > m_run + kLazyRescale) != 0;
+    const float m_new = moved ? fmaxf(m_run, mxs) : m_run;
+    const float m_safe = m_new == -INFINITY ? 0.f : m_new;
+    alpha = fast_exp2(m_run - m_safe);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int c = 0; c < BC / 16; ++c) {
+      const int tt = c >> 1, r0p = 8 * (c & 1);
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = fast_exp2(fmaf(sc[tt][r0p + e], c2, -m_safe));
+        psum += p[e];
+      }
+      pk[c] = u32x4{pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3]), pack2<DT>(p[4], p[5]), pack2<DT>(p[6], p[7])};
+    }
+    l_run = fmaf(l_run, alpha, psum);
+    return moved;
+  };
+  auto scale_acc = [&](float alpha) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+  };
+  // O^T += V^T P^T of one tile
+  auto pv_tile = [&](auto buf, const u32x4 (&pk)[BC / 16]) {
+    const uint16_t* vs = vbuf(buf) + vtr_off;
+#pragma unroll
+    for (int c = 0; c < BC / 16; ++c)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const uint16_t* vp = vs + 16 * c * VP + 32 * dt;
+        const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * VP);
+        oacc[dt] = mfma32<DT>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pk[c], oacc[dt]);
+      }
+  };
+  // ---- key loop: two-stage LDS ring; tile j uses stage (j - j0) % 2 --------
   if (j1 > j0) {
-    dma_tile(j0 * BC, j0 & 1);
-    wait_vmem();
-    __syncthreads();
     if constexpr (D != 256) {
-      for (int j = j0; j < j1; ++j) {
-        const int buf = j & 1;
+      int jg = j0;  // first tile of the generic loop below
+      if constexpr (!BIAS) {
+        // Tiles [j0, jm) need no mask for any row of the block.  They run
+        // software-pipelined: while the softmax of tile j is on the vector
+        // units, the same wave issues the score MFMAs of tile j+1; then P V of
+        // tile j.  K and V copies are a step apart (K(j+2) and V(j+1) land
+        // during step j), so the ring keeps two stages of each.
+        int jm = CAUSAL ? (qs + diag + 1) / BC : Lk / BC;
+        jm = min(j1, max(j0, jm));
+        if (jm > j0) {
+          constexpr std::integral_constant<int, 0> S0{};
+          constexpr std::integral_constant<int, 1> S1{};
+          f32x16 sa[BC / 32], sb[BC / 32];
+          dma_k(j0 * BC, S0);
+          dma_v(j0 * BC, S0);
+          if (j0 + 1 < j1) dma_k((j0 + 1) * BC, S1);  // (j0 + 1 <= jm)
+          wait_vmem();
+          __syncthreads();
+          qk_tile(S0, sa);
+          // One step with the next tile's scores overlapped (needs j + 1 < jm).
+          // The order of the work is fixed by scheduling fences: region A
+          // issues the NA score MFMAs of tile j+1, and after each one a share
+          // of the softmax of tile j (row max, lazy max move, then the first
+          // 24 of the 32 exponentials per lane); region B issues the NB P V
+          // MFMAs of tile j, in 16-key chunks, and the last 8 exponentials
+          // after its first MFMAs (they feed the last chunk).
+          auto step = [&](int j, auto cur, auto nxt, f32x16 (&sc)[BC / 32], f32x16 (&sn)[BC / 32]) {
+            if (j + 2 <= jm && j + 2 < j1) dma_k((j + 2) * BC, cur);
+            dma_v((j + 1) * BC, nxt);
+            constexpr int NA = (D / 16) * (BC / 32), NB = (D / 32) * (BC / 16);
+            constexpr int KPRE = 3, VPRE = 2;
+            const uint16_t* ks = kbuf(nxt) + l32 * KP + 8 * hh;
+            const uint16_t* vs = vbuf(cur) + vtr_off;
+            float p[BC / 2];
+            u32x4 pk[BC / 16];
+            float psum = 0.f, mx = 0.f, m_safe = 0.f, alpha = 1.f;
+            bool moved = false;
+            // exponentials [lo, hi) in chunk-major order (value 8c + e is
+            // register 8(c%2) + e of score tile c/2); a chunk is packed as soon
+            // as its 8 values exist
+            auto exps = [&](int lo, int hi) {
+#pragma unroll
+              for (int x = lo; x < hi; ++x) {
+                const int c = x >> 3, e = x & 7;
+                p[x] = fast_exp2(fmaf(sc[c >> 1][8 * (c & 1) + e], c2, -m_safe));
+                psum += p[x];
+                if (e == 7)
+                  pk[c] = u32x4{pack2<DT>(p[x - 7], p[x - 6]), pack2<DT>(p[x - 5], p[x - 4]),
+                                pack2<DT>(p[x - 3], p[x - 2]), pack2<DT>(p[x - 1], p[x])};
+              }
+            };
+            __builtin_amdgcn_sched_barrier(0);
+            u32x4 kop[NA];
+#pragma unroll
+            for (int i = 0; i < KPRE; ++i) kop[i] = *(const u32x4*)(ks + (i & 1) * 32 * KP + 16 * (i >> 1));
+#pragma unroll
+            for (int i = 0; i < NA; ++i) {
+              const int kk = i >> 1, tt = i & 1;
+              sn[tt] = mfma32<DT>(kop[i], qf[kk], kk == 0 ? zero16 : sn[tt]);
+              if (i + KPRE < NA)
+                kop[i + KPRE] = *(const u32x4*)(ks + ((i + KPRE) & 1) * 32 * KP + 16 * ((i + KPRE) >> 1));
+              if (i == 0) {
+                mx = sc[0][0];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
+              } else if (i == 1) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
+              } else if (i == 2) {
+                const float mxs = halfwave_max(mx) * c2;
+                moved = __builtin_amdgcn_ballot_w64(mxs > m_run + kLazyRescale) != 0;
+                const float m_new = moved ? fmaxf(m_run, mxs) : m_run;
+                m_safe = m_new == -INFINITY ? 0.f : m_new;
+                alpha = fast_exp2(m_run - m_safe);
+                m_run = m_new;
+              } else {
+                exps((i - 3) * 24 / (NA - 3), (i - 2) * 24 / (NA - 3));
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            // keep P here: otherwise it is sunk past the rescale branch below
+#pragma unroll
+            for (int c = 0; c < 3; ++c) asm volatile("" : "+v"(pk[c]));
+            if (moved) scale_acc(alpha);
+            __builtin_amdgcn_sched_barrier(0);
+            u32x2 vop[NB][2];
+#pragma unroll
+            for (int i = 0; i < VPRE; ++i) {
+              const uint16_t* vp = vs + 16 * (i / (D / 32)) * VP + 32 * (i % (D / 32));
+              vop[i][0] = lds_read_tr16(vp);
+              vop[i][1] = lds_read_tr16(vp + 4 * VP);
+            }
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+              const int c = i / (D / 32), dt = i % (D / 32);
+              oacc[dt] = mfma32<DT>(u32x4{vop[i][0][0], vop[i][0][1], vop[i][1][0], vop[i][1][1]}, pk[c], oacc[dt]);
+              if (i + VPRE < NB) {
+                const uint16_t* vp = vs + 16 * ((i + VPRE) / (D / 32)) * VP + 32 * ((i + VPRE) % (D / 32));
+                vop[i + VPRE][0] = lds_read_tr16(vp);
+                vop[i + VPRE][1] = lds_read_tr16(vp + 4 * VP);
+              }
+              if (i < NB / 2) exps(24 + i * 8 / (NB / 2), 24 + (i + 1) * 8 / (NB / 2));
+              if (i == NB / 2 - 1) l_run = fmaf(l_run, alpha, psum);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            wait_vmem();
+            __syncthreads();
+          };
+          // the last pipelined tile: softmax and P V only
+          auto last = [&](int j, auto cur, auto nxt, f32x16 (&sc)[BC / 32]) {
+            if (j + 1 < j1) dma_v((j + 1) * BC, nxt);
+            u32x4 pk[BC / 16];
+            float alpha;
+            if (softmax_pack(sc, pk, alpha)) scale_acc(alpha);
+            pv_tile(cur, pk);
+            wait_vmem();
+            __syncthreads();
+          };
+          int j = j0;
+          for (; j + 2 < jm; j += 2) {
+            step(j, S0, S1, sa, sb);
+            step(j + 1, S1, S0, sb, sa);
+          }
+          if (j + 1 < jm) {
+            step(j, S0, S1, sa, sb);
+            last(j + 1, S1, S0, sb);
+          } else {
+            last(j, S0, S1, sa);
+          }
+          jg = jm;  // tile jm (if any) is in stage (jm - j0) % 2
+        }
+      }
+      if (jg == j0) {
+        dma_tile(j0 * BC, 0);
+        wait_vmem();
+        __syncthreads();
+      }
+      for (int j = jg; j < j1; ++j) {
+        const int buf = (j - j0) & 1;
         BiasRaw br{};
         if constexpr (BIAS) br = bias_fetch(j * BC);
         if (j + 1 < j1) dma_tile((j + 1) * BC, buf ^ 1);  // lands while tile j is computed
@@ -552,6 +794,9 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
         __syncthreads();
       }
     } else {
+      dma_tile(j0 * BC, 0);
+      wait_vmem();
+      __syncthreads();
       // The inner loop runs the tiles that need no rescale and leaves at the
       // first that does; the rescale (rare after the first tiles) happens
       // outside it, so the accumulators, which live in AGPRs at this head
@@ -560,7 +805,7 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
       while (j < j1) {
         bool pending = false;
         for (; j < j1; ++j) {
-          const int buf = j & 1;
+          const int buf = (j - j0) & 1;
           if (j + 1 < j1) dma_tile((j + 1) * BC, buf ^ 1);
           if (tile_active(j * BC)) {
             if (scores_max(j * BC, buf)) {
@@ -574,7 +819,7 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
         }
         if (pending) {
           rescale();
-          softmax_pv(j & 1);
+          softmax_pv((j - j0) & 1);
           wait_vmem();
           __syncthreads();
           ++j;
@@ -629,32 +874,38 @@ __global__ void __launch_bounds__(256, Fwd16Cfg<D>::WAVES_PER_EU) fwd16_kernel(F
 }
 
 template <int D, int DT, bool CAUSAL, int MODE>
-hipError_t launch_fwd16(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_fwd16(FwdArgs a, hipStream_t s) {
+  constexpr int NW = fwd16_waves(D, MODE, CAUSAL), BR = Fwd16Cfg<D, NW>::BR;
   // dense: every (b, h, q-block); varlen: an upper bound on the compact tile list
-  const int n = (MODE == kDense || MODE == kDenseBias) ? a.B * a.H * a.n_qblk
-                               : a.H * ((a.total_q + Fwd16Cfg<D>::BR - 1) / Fwd16Cfg<D>::BR + a.B) * max(a.n_split, 1);
-  hipLaunchKernelGGL((fwd16_kernel<D, DT, CAUSAL, MODE>), dim3(n), dim3(256), 0, s, a);
+  int n;
+  if constexpr (MODE == kDense || MODE == kDenseBias) {
+    a.n_qblk = (a.Sq + BR - 1) / BR;
+    n = a.B * a.H * a.n_qblk;
+  } else {
+    n = a.H * ((a.total_q + BR - 1) / BR + a.B) * max(a.n_split, 1);
+  }
+  hipLaunchKernelGGL((fwd16_kernel<D, DT, CAUSAL, MODE>), dim3(n), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
 #define ATTN_INSTANTIATE_FWD16_BIAS(D)                                                        \
-  template hipError_t launch_fwd16<D, kBF16, false, kDenseBias>(const FwdArgs&, hipStream_t); \
-  template hipError_t launch_fwd16<D, kBF16, true, kDenseBias>(const FwdArgs&, hipStream_t);  \
-  template hipError_t launch_fwd16<D, kFP16, false, kDenseBias>(const FwdArgs&, hipStream_t); \
-  template hipError_t launch_fwd16<D, kFP16, true, kDenseBias>(const FwdArgs&, hipStream_t);
+  template hipError_t launch_fwd16<D, kBF16, false, kDenseBias>(FwdArgs, hipStream_t); \
+  template hipError_t launch_fwd16<D, kBF16, true, kDenseBias>(FwdArgs, hipStream_t);  \
+  template hipError_t launch_fwd16<D, kFP16, false, kDenseBias>(FwdArgs, hipStream_t); \
+  template hipError_t launch_fwd16<D, kFP16, true, kDenseBias>(FwdArgs, hipStream_t);
 
 #define ATTN_INSTANTIATE_FWD16(D)                                          \
-  template hipError_t launch_fwd16<D, kBF16, false, kDense>(const FwdArgs&, hipStream_t);  \
-  template hipError_t launch_fwd16<D, kBF16, true, kDense>(const FwdArgs&, hipStream_t);   \
-  template hipError_t launch_fwd16<D, kFP16, false, kDense>(const FwdArgs&, hipStream_t);  \
-  template hipError_t launch_fwd16<D, kFP16, true, kDense>(const FwdArgs&, hipStream_t);   \
-  template hipError_t launch_fwd16<D, kBF16, false, kVarlen>(const FwdArgs&, hipStream_t); \
-  template hipError_t launch_fwd16<D, kBF16, true, kVarlen>(const FwdArgs&, hipStream_t);  \
-  template hipError_t launch_fwd16<D, kFP16, false, kVarlen>(const FwdArgs&, hipStream_t); \
-  template hipError_t launch_fwd16<D, kFP16, true, kVarlen>(const FwdArgs&, hipStream_t);  \
-  template hipError_t launch_fwd16<D, kBF16, false, kPaged>(const FwdArgs&, hipStream_t);  \
-  template hipError_t launch_fwd16<D, kBF16, true, kPaged>(const FwdArgs&, hipStream_t);   \
-  template hipError_t launch_fwd16<D, kFP16, false, kPaged>(const FwdArgs&, hipStream_t);  \
-  template hipError_t launch_fwd16<D, kFP16, true, kPaged>(const FwdArgs&, hipStream_t);
+  template hipError_t launch_fwd16<D, kBF16, false, kDense>(FwdArgs, hipStream_t);  \
+  template hipError_t launch_fwd16<D, kBF16, true, kDense>(FwdArgs, hipStream_t);   \
+  template hipError_t launch_fwd16<D, kFP16, false, kDense>(FwdArgs, hipStream_t);  \
+  template hipError_t launch_fwd16<D, kFP16, true, kDense>(FwdArgs, hipStream_t);   \
+  template hipError_t launch_fwd16<D, kBF16, false, kVarlen>(FwdArgs, hipStream_t); \
+  template hipError_t launch_fwd16<D, kBF16, true, kVarlen>(FwdArgs, hipStream_t);  \
+  template hipError_t launch_fwd16<D, kFP16, false, kVarlen>(FwdArgs, hipStream_t); \
+  template hipError_t launch_fwd16<D, kFP16, true, kVarlen>(FwdArgs, hipStream_t);  \
+  template hipError_t launch_fwd16<D, kBF16, false, kPaged>(FwdArgs, hipStream_t);  \
+  template hipError_t launch_fwd16<D, kBF16, true, kPaged>(FwdArgs, hipStream_t);   \
+  template hipError_t launch_fwd16<D, kFP16, false, kPaged>(FwdArgs, hipStream_t);  \
+  template hipError_t launch_fwd16<D, kFP16, true, kPaged>(FwdArgs, hipStream_t);
 
 }  // namespace attn

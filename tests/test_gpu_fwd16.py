@@ -56,6 +56,20 @@ def test_shapes_bf16(lib, d, causal, sq, sk):
     assert_close16(o, o_ref, lse, lse_ref, f"d{d} causal={causal} {sq}x{sk}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("sq,sk", [(300, 64), (300, 128), (300, 192), (300, 200), (520, 700), (700, 520),
+                                   (256, 1024)])
+def test_unmasked_tile_runs(lib, d, causal, sq, sk):
+    """Runs of 1, 2, 3 and more unmasked key tiles (odd and even counts),
+    followed by masked tiles or none, with query blocks of 256 rows that are
+    full, partial, or reach past the causal diagonal."""
+    q, k, v = W.qkv_normal(500 + d + sq + sk, (1, sq, 2, d), (1, sk, 2, d))
+    o, lse = _run(lib, q, k, v, causal)
+    o_ref, lse_ref = OA.attention_bshd(q, k, v, 1 / math.sqrt(d), causal)
+    assert_close16(o, o_ref, lse, lse_ref, f"d{d} causal={causal} {sq}x{sk}")
+
+
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
