@@ -91,7 +91,8 @@ def _run_fp8(lib, qp, causal, scale):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("block_rows", [128, 0])
-@pytest.mark.parametrize("sq,sk", [(256, 256), (200, 333), (333, 200), (1, 1), (130, 64)])
+@pytest.mark.parametrize("sq,sk", [(256, 256), (200, 333), (333, 200), (1, 1), (130, 64), (300, 192),
+                                   (260, 1000), (700, 520)])
 def test_fwd_fp8_vs_dequantised_attention(lib, causal, block_rows, sq, sk):
     d = 128
     q, k, v = W.qkv_normal(60 + sq, (2, sq, 2, d), (2, sk, 2, d))
