@@ -229,21 +229,28 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
     chunk = s - key_local * C::VSLOTS;
   };
   // byte offsets of this lane's slots inside a tile for the dense/varlen
-  // layouts (padding slots point out of range and read zeros)
+  // layouts (padding slots point out of range and read zeros).  The slots of
+  // the full rounds (every wave copies one) are kept in registers; the last,
+  // partial round is copied by a few waves only, and its offset is computed
+  // when it is needed, so that it takes no register (spilling it would make
+  // the copy wait for every load in flight)
   constexpr uint32_t kOutOfRange = 0x7ffffff0u;
-  uint32_t k_boff[C::KI_W], v_boff[C::VI_W];
-#pragma unroll
-  for (int ii = 0; ii < C::KI_W; ++ii) {
+  constexpr int KI_FULL = C::KSLOTS / NW, VI_FULL = C::VSLOTS / NW;
+  auto k_off = [&](int ii) {
     int kl, ch;
     k_slot(ii, kl, ch);
-    k_boff[ii] = ch < CPR ? 2u * (uint32_t)(kl * (int)a.k_ss + ch * 8) : kOutOfRange;
-  }
-#pragma unroll
-  for (int ii = 0; ii < C::VI_W; ++ii) {
+    return ch < CPR ? 2u * (uint32_t)(kl * (int)a.k_ss + ch * 8) : kOutOfRange;
+  };
+  auto v_off = [&](int ii) {
     int kl, ch;
     v_slot(ii, kl, ch);
-    v_boff[ii] = ch < CPR ? 2u * (uint32_t)(kl * (int)a.v_ss + ch * 8) : kOutOfRange;
-  }
+    return ch < CPR ? 2u * (uint32_t)(kl * (int)a.v_ss + ch * 8) : kOutOfRange;
+  };
+  uint32_t k_boff[KI_FULL], v_boff[VI_FULL];
+#pragma unroll
+  for (int ii = 0; ii < KI_FULL; ++ii) k_boff[ii] = k_off(ii);
+#pragma unroll
+  for (int ii = 0; ii < VI_FULL; ++ii) v_boff[ii] = v_off(ii);
   auto row_of = [&](int key) -> int64_t {  // element offset of key's row (paged: through the table)
     if constexpr (MODE == kPaged) {
       const int page = a.block_table[(int64_t)b * a.max_pages + (key >> a.page_shift)];
@@ -259,9 +266,12 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   // Smaller pages: each row through the block table; rows past Lk repeat row
   // Lk-1 (finite data, masked out of the scores and multiplied by p = 0).
   const bool contiguous = MODE != kPaged || a.page_shift >= 6;
+  // (the table is read through the constant address space: with a uniform
+  // index that is a scalar load, which the tile copies never wait behind)
+  typedef const __attribute__((address_space(4))) int32_t cint32;
   auto tile_row0 = [&](int key0) -> int64_t {  // element row of key0 (paged: page base + slot)
     if constexpr (MODE == kPaged) {
-      const int page = a.block_table[(int64_t)b * a.max_pages + (key0 >> a.page_shift)];
+      const int page = ((cint32*)a.block_table)[(int64_t)b * a.max_pages + (key0 >> a.page_shift)];
       return ((int64_t)page << a.page_shift) + (key0 & ((1 << a.page_shift) - 1));
     } else {
       return key0;
@@ -269,14 +279,15 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   };
   // (tile ranges are clamped below 2^31; the host limits seq strides to 2^24
   // elements, so a tile's 64 rows always lie inside them)
-  auto dma_k = [&](int key0, auto buf) {
+  // (row0: tile_row0(key0), looked up once per tile by the caller)
+  auto dma_k = [&](int key0, auto buf, int64_t row0) {
     uint16_t* kb = kbuf(buf);
     if (contiguous) {
       const uint64_t kn = 2ull * (uint64_t)(Lk - key0) * (uint64_t)a.k_ss;
-      const i32x4 kr = make_rsrc(kg + tile_row0(key0) * a.k_ss, (uint32_t)min(kn, (uint64_t)0x7fff0000u));
+      const i32x4 kr = make_rsrc(kg + row0 * a.k_ss, (uint32_t)min(kn, (uint64_t)0x7fff0000u));
 #pragma unroll
       for (int ii = 0; ii < C::KI_W; ++ii)
-        if (wave + NW * ii < C::KSLOTS) dma16_buf(kr, k_boff[ii], kb + (wave + NW * ii) * 512);
+        if (wave + NW * ii < C::KSLOTS) dma16_buf(kr, ii < KI_FULL ? k_boff[ii] : k_off(ii), kb + (wave + NW * ii) * 512);
     } else {
 #pragma unroll
       for (int ii = 0; ii < C::KI_W; ++ii) {
@@ -289,14 +300,14 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
       }
     }
   };
-  auto dma_v = [&](int key0, auto buf) {
+  auto dma_v = [&](int key0, auto buf, int64_t row0) {
     uint16_t* vb = vbuf(buf);
     if (contiguous) {
       const uint64_t vn = 2ull * (uint64_t)(Lk - key0) * (uint64_t)a.v_ss;
-      const i32x4 vr = make_rsrc(vg + tile_row0(key0) * a.v_ss, (uint32_t)min(vn, (uint64_t)0x7fff0000u));
+      const i32x4 vr = make_rsrc(vg + row0 * a.v_ss, (uint32_t)min(vn, (uint64_t)0x7fff0000u));
 #pragma unroll
       for (int ii = 0; ii < C::VI_W; ++ii)
-        if (wave + NW * ii < C::VSLOTS) dma16_buf(vr, v_boff[ii], vb + (wave + NW * ii) * 512);
+        if (wave + NW * ii < C::VSLOTS) dma16_buf(vr, ii < VI_FULL ? v_boff[ii] : v_off(ii), vb + (wave + NW * ii) * 512);
     } else {
 #pragma unroll
       for (int ii = 0; ii < C::VI_W; ++ii) {
@@ -310,8 +321,9 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
     }
   };
   auto dma_tile = [&](int key0, int buf) {
-    dma_k(key0, buf);
-    dma_v(key0, buf);
+    const int64_t row0 = contiguous ? tile_row0(key0) : 0;
+    dma_k(key0, buf, row0);
+    dma_v(key0, buf, row0);
   };
 
   // V^T operand addressing for ds_read_b64_tr_b16: lane (group g, index j)
@@ -648,7 +660,9 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   if (j1 > j0) {
     if constexpr (D != 256) {
       int jg = j0;  // first tile of the generic loop below
-      if constexpr (!BIAS) {
+      // (not with a score bias, and not for paged caches, where the registers
+      // of the pipeline and of the page-table copies do not fit together)
+      if constexpr (!BIAS && MODE != kPaged) {
         // Tiles [j0, jm) need no mask for any row of the block.  They run
         // software-pipelined: while the softmax of tile j is on the vector
         // units, the same wave issues the score MFMAs of tile j+1; then P V of
@@ -660,12 +674,15 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
           constexpr std::integral_constant<int, 0> S0{};
           constexpr std::integral_constant<int, 1> S1{};
           f32x16 sa[BC / 32], sb[BC / 32];
-          dma_k(j0 * BC, S0);
-          dma_v(j0 * BC, S0);
-          if (j0 + 1 < j1) dma_k((j0 + 1) * BC, S1);  // (j0 + 1 <= jm)
+          // (no page table on this path: a tile's first row is its first key)
+          dma_k(j0 * BC, S0, j0 * BC);
+          dma_v(j0 * BC, S0, j0 * BC);
+          if (j0 + 1 < j1) dma_k((j0 + 1) * BC, S1, (j0 + 1) * BC);  // (j0 + 1 <= jm)
           wait_vmem();
           __syncthreads();
-          qk_tile(S0, sa);
+          // waves whose rows all lie past the sequence end only copy and
+          // synchronise (with one query row, as in decoding, three of four)
+          if (wave_active) qk_tile(S0, sa);
           // One step with the next tile's scores overlapped (needs j + 1 < jm).
           // The order of the work is fixed by scheduling fences: region A
           // issues the NA score MFMAs of tile j+1, and after each one a share
@@ -673,9 +690,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
           // 24 of the 32 exponentials per lane); region B issues the NB P V
           // MFMAs of tile j, in 16-key chunks, and the last 8 exponentials
           // after its first MFMAs (they feed the last chunk).
-          auto step = [&](int j, auto cur, auto nxt, f32x16 (&sc)[BC / 32], f32x16 (&sn)[BC / 32]) {
-            if (j + 2 <= jm && j + 2 < j1) dma_k((j + 2) * BC, cur);
-            dma_v((j + 1) * BC, nxt);
+          auto step_math = [&](auto cur, auto nxt, f32x16 (&sc)[BC / 32], f32x16 (&sn)[BC / 32]) {
             constexpr int NA = (D / 16) * (BC / 32), NB = (D / 32) * (BC / 16);
             constexpr int KPRE = 3, VPRE = 2;
             const uint16_t* ks = kbuf(nxt) + l32 * KP + 8 * hh;
@@ -752,16 +767,23 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
               if (i == NB / 2 - 1) l_run = fmaf(l_run, alpha, psum);
               __builtin_amdgcn_sched_barrier(0);
             }
+          };
+          auto step = [&](int j, auto cur, auto nxt, f32x16 (&sc)[BC / 32], f32x16 (&sn)[BC / 32]) {
+            if (j + 2 <= jm && j + 2 < j1) dma_k((j + 2) * BC, cur, (j + 2) * BC);
+            dma_v((j + 1) * BC, nxt, (j + 1) * BC);
+            if (wave_active) step_math(cur, nxt, sc, sn);
             wait_vmem();
             __syncthreads();
           };
           // the last pipelined tile: softmax and P V only
           auto last = [&](int j, auto cur, auto nxt, f32x16 (&sc)[BC / 32]) {
-            if (j + 1 < j1) dma_v((j + 1) * BC, nxt);
-            u32x4 pk[BC / 16];
-            float alpha;
-            if (softmax_pack(sc, pk, alpha)) scale_acc(alpha);
-            pv_tile(cur, pk);
+            if (j + 1 < j1) dma_v((j + 1) * BC, nxt, (j + 1) * BC);
+            if (wave_active) {
+              u32x4 pk[BC / 16];
+              float alpha;
+              if (softmax_pack(sc, pk, alpha)) scale_acc(alpha);
+              pv_tile(cur, pk);
+            }
             wait_vmem();
             __syncthreads();
           };
