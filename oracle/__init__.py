@@ -9,9 +9,11 @@ from the pages' description and nothing else:
 * ``fp8``        — the e4m3 codec, the random-sign x Hadamard rotation and the
   block / per-tensor quantisers of the page's "8-bit forward pass" section, plus a
   float64 emulation of the quantised pipeline.
+* ``int8``       — the symmetric int8 codec and quantisers of the int8 path
+  (int8 Q and K, e4m3 V) and its float64 emulation.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The product library never does, and this
 package imports nothing from the product library.
 """
-from . import attention, fp8  # noqa: F401
+from . import attention, fp8, int8  # noqa: F401

@@ -84,3 +84,46 @@ def test_emulation_block_rotation_beats_per_tensor():
     print(f"int8 emulation rmse: block+rotation {r_blk:.3e}, per-tensor {r_pt:.3e}")
     assert r_blk < r_pt
     assert r_blk < 1.2e-2
+
+
+def test_pipeline_formats():
+    """Q and K become int8 codes with int8 scales (amax/127), V keeps the e4m3
+    codes and scales of the 8-bit path."""
+    from oracle import fp8 as F
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((1, 200, 2, 128)).astype(np.float32)
+    qp = I.quantize_pipeline(x, x, x, None, 128)
+    assert qp["q8"].dtype == np.int8 and qp["k8"].dtype == np.int8
+    assert (qp["q8"] == I.quantize(x, 128)[0]).all()
+    v8, vs = F.quantize(x, 128)
+    assert (qp["v8"] == v8).all() and (qp["v_scale"] == vs).all()
+    qd, kd, vd = I.dequantize_pipeline(qp)
+    assert np.abs(qd - x).max() <= 0.5 * qp["q_scale"].max() * (1 + 1e-5)
+    assert np.abs(vd - x).max() <= 0.5 * F.e4m3_ulp(np.abs(x) / vs.min()).max() * vs.max()
+
+
+def test_reading_fixed_point_probabilities_are_too_coarse():
+    """Why the output product keeps e4m3 probabilities: with the same
+    dequantised inputs, probabilities rounded to int8 fixed point (127 = the
+    row maximum) give a far larger attention error on the outlier workload
+    than probabilities rounded to e4m3 (p * 2^6, as the 8-bit path does)."""
+    import workloads as W
+    from oracle import fp8 as F
+    B, S, H, D = 1, 2048, 1, 128
+    q, k, v = W.qkv_outlier(21, (B, S, H, D))
+    signs = W.random_signs(4, D)
+    sc = 1 / math.sqrt(D)
+    rows = np.arange(0, S, 16)
+    ref = A.attention_bshd(q, k, v, sc, rows=rows)[0][0, rows, 0]
+    qd, kd, vd = I.dequantize_pipeline(I.quantize_pipeline(q, k, v, signs, 128))
+    s = qd[0, rows, 0] @ kd[0, :, 0].T * sc
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p_fixed = np.rint(p * 127)
+    p_e4m3 = F.e4m3_decode(F.e4m3_encode((p * 64).astype(np.float32)))
+    err = {}
+    for name, pp in (("fixed", p_fixed), ("e4m3", p_e4m3)):
+        o = (pp @ vd[0, :, 0]) / pp.sum(axis=1, keepdims=True)
+        err[name] = float(np.sqrt(np.mean((o - ref) ** 2)))
+    print(f"rmse: int8 fixed-point P {err['fixed']:.3e}, e4m3 P {err['e4m3']:.3e}")
+    assert err["fixed"] > 4 * err["e4m3"]
+    assert err["e4m3"] < 1.2e-2
