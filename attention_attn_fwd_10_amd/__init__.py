@@ -7,6 +7,8 @@ The entry points mirror the C ABI in ``include/attn.h``:
 * ``fwd``            -> ``attn_fwd``            (bf16 / fp16, optional causal mask)
 * ``fp8_quantize``   -> ``attn_fp8_quantize``   (rotation + e4m3 block quantisation)
 * ``fwd_fp8``        -> ``attn_fwd_fp8``        (e4m3 forward with per-block scales)
+* ``int8_quantize``  -> ``attn_int8_quantize``  (rotation + int8 block quantisation)
+* ``fwd_int8``       -> ``attn_fwd_int8``       (int8 scores, e4m3 V and probabilities)
 * ``fwd_varlen``     -> ``attn_fwd_varlen``     (packed sequences, optional paged KV)
 
 Tensors use the [batch, seq, heads, head_dim] layout (varlen: [tokens, heads,
@@ -19,7 +21,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "fp8_quantize", "fwd_fp8", "fwd_varlen", "lib_path", "AttnError",
+__all__ = ["fwd", "fp8_quantize", "fwd_fp8", "int8_quantize", "fwd_int8", "fwd_varlen", "lib_path", "AttnError",
            "ATTN_BF16", "ATTN_FP16"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -55,6 +57,10 @@ def _load():
     lib.attn_fp8_quantize.restype = I
     lib.attn_fwd_fp8.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, I, F, I, P]
     lib.attn_fwd_fp8.restype = I
+    lib.attn_int8_quantize.argtypes = [P, I64P, P, P, I, I, I, I, I, P, P]
+    lib.attn_int8_quantize.restype = I
+    lib.attn_fwd_int8.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, I, F, I, P]
+    lib.attn_fwd_int8.restype = I
     lib.attn_fwd_varlen.argtypes = [I, P, P, P, P, P, P, I, I, P, P, I, I, I, I, I, I, F, I, P]
     lib.attn_fwd_varlen.restype = I
     SZ = ctypes.c_size_t
@@ -192,25 +198,40 @@ def fwd_bias(q, k, v, bias, softmax_scale=None, causal=False, out=None, lse=None
     return out, lse
 
 
-def fp8_quantize(x, block_rows=128, signs=None, out=None, scales=None, stream=None):
-    """Quantise a bf16 [B, S, H, D] tensor to e4m3 (uint8 codes) with one scale
-    per (b, h, 128-row block) or per tensor (block_rows=0), optionally after the
-    random-sign Hadamard rotation given by ``signs`` (int8 [D] of +-1)."""
+def _quantize(fn, code_dtype, x, block_rows, signs, out, scales, stream):
     import torch
     _require_cuda(x, signs, out, scales)
     if x.dtype != torch.bfloat16:
-        raise TypeError("fp8_quantize expects bf16 input")
+        raise TypeError("the 8-bit quantisers expect bf16 input")
     B, S, H, D = x.shape
     if out is None:
-        out = torch.empty((B, S, H, D), dtype=torch.uint8, device=x.device)
+        out = torch.empty((B, S, H, D), dtype=code_dtype, device=x.device)
+    elif out.dtype != code_dtype or not out.is_contiguous() or out.shape != x.shape:
+        raise ValueError(f"out must be a contiguous {code_dtype} tensor shaped like x")
     if scales is None:
         shape = (B, H, (S + 127) // 128) if block_rows else (1,)
         scales = torch.empty(shape, dtype=torch.float32, device=x.device)
     if signs is not None and (signs.dtype != torch.int8 or signs.numel() != D):
         raise ValueError("signs must be int8 [D]")
-    _check(_lib.attn_fp8_quantize(_ptr(x), _strides(x), _ptr(out), _ptr(scales), B, H, S, D, int(block_rows),
-                                  _ptr(signs), _stream(stream)))
+    _check(fn(_ptr(x), _strides(x), _ptr(out), _ptr(scales), B, H, S, D, int(block_rows), _ptr(signs),
+              _stream(stream)))
     return out, scales
+
+
+def fp8_quantize(x, block_rows=128, signs=None, out=None, scales=None, stream=None):
+    """Quantise a bf16 [B, S, H, D] tensor to e4m3 (uint8 codes) with one scale
+    per (b, h, 128-row block) or per tensor (block_rows=0), optionally after the
+    random-sign Hadamard rotation given by ``signs`` (int8 [D] of +-1)."""
+    import torch
+    return _quantize(_lib.attn_fp8_quantize, torch.uint8, x, block_rows, signs, out, scales, stream)
+
+
+def int8_quantize(x, block_rows=128, signs=None, out=None, scales=None, stream=None):
+    """Quantise a bf16 [B, S, H, D] tensor to symmetric int8 codes (scale =
+    amax / 127) per (b, h, 128-row block) or per tensor, optionally after the
+    random-sign Hadamard rotation."""
+    import torch
+    return _quantize(_lib.attn_int8_quantize, torch.int8, x, block_rows, signs, out, scales, stream)
 
 
 def fwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, block_rows=128, softmax_scale=None, causal=False,
@@ -232,6 +253,29 @@ def fwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, block_rows=128, softmax_scale
     _check(_lib.attn_fwd_fp8(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v8), _ptr(v_scale),
                              int(block_rows), _ptr(out), _ptr(lse), B, H, Sq, Sk, D, scale, int(bool(causal)),
                              _stream(stream)))
+    return out, lse
+
+
+def fwd_int8(q8, q_scale, k8, k_scale, v8, v_scale, block_rows=128, softmax_scale=None, causal=False,
+             out=None, lse=None, stream=None):
+    """Fused forward with int8 scores: q8, k8 int8 codes and v8 e4m3 codes
+    (uint8), all [B, S, H, D] contiguous, with their scales.  Returns
+    (o bf16 [B, Sq, H, D], lse fp32 [B, H, Sq])."""
+    import torch
+    _require_cuda(q8, q_scale, k8, k_scale, v8, v_scale, out, lse)
+    B, Sq, H, D = q8.shape
+    Sk = k8.shape[1]
+    for t, dt in ((q8, torch.int8), (k8, torch.int8), (v8, torch.uint8)):
+        if t.dtype != dt or not t.is_contiguous():
+            raise ValueError("q8, k8 must be contiguous int8 codes and v8 contiguous uint8 e4m3 codes")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, Sq, H, D), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q8.device)
+    _check(_lib.attn_fwd_int8(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v8), _ptr(v_scale),
+                              int(block_rows), _ptr(out), _ptr(lse), B, H, Sq, Sk, D, scale, int(bool(causal)),
+                              _stream(stream)))
     return out, lse
 
 

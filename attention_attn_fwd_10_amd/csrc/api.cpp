@@ -23,6 +23,8 @@ hipError_t launch_fwd16pp(FwdArgs a, hipStream_t s);
 hipError_t launch_fp8_quantize(const QuantArgs& a, int D, hipStream_t s);
 hipError_t launch_splitkv_merge(const MergeArgs& a, int D, int dtype, hipStream_t s);
 hipError_t launch_fwd_fp8(const Fp8Args& a, int D, bool causal, hipStream_t s);
+hipError_t launch_int8_quantize(const QuantArgs& a, int D, hipStream_t s);
+hipError_t launch_fwd_int8(const Fp8Args& a, int D, bool causal, hipStream_t s);
 }  // namespace attn
 
 namespace {
@@ -353,8 +355,11 @@ attn_status_t attn_fwd_splitkv(int dtype, const void* q, const int32_t* cu_seqle
   return hip_status(attn::launch_splitkv_merge(m, D, dtype, (hipStream_t)stream), "attn_fwd_splitkv merge launch");
 }
 
-attn_status_t attn_fp8_quantize(const void* x, const int64_t x_strides[3], uint8_t* x8, float* scales, int B, int H,
-                                int S, int D, int block_rows, const int8_t* signs, void* stream) {
+typedef hipError_t (*quant_launcher_t)(const attn::QuantArgs&, int, hipStream_t);
+
+static attn_status_t quantize_8bit(const char* name, quant_launcher_t launch, const void* x,
+                                   const int64_t x_strides[3], uint8_t* x8, float* scales, int B, int H, int S,
+                                   int D, int block_rows, const int8_t* signs, void* stream) {
   attn_status_t st;
   if (B < 0 || H < 0 || S < 0) return fail(ATTN_ERR_INVALID, "negative size");
   if ((st = check_head_dim(D)) != ATTN_OK) return st;
@@ -369,12 +374,27 @@ attn_status_t attn_fp8_quantize(const void* x, const int64_t x_strides[3], uint8
   a.x_sb = x_strides[0]; a.x_ss = x_strides[1]; a.x_sh = x_strides[2];
   a.x8 = x8; a.scales = scales; a.signs = signs;
   a.B = B; a.H = H; a.S = S; a.block_rows = block_rows;
-  return hip_status(attn::launch_fp8_quantize(a, D, (hipStream_t)stream), "attn_fp8_quantize launch");
+  return hip_status(launch(a, D, (hipStream_t)stream), name);
 }
 
-attn_status_t attn_fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
-                           const uint8_t* v8, const float* v_scale, int block_rows, void* o, float* lse, int B,
-                           int H, int Sq, int Sk, int D, float softmax_scale, int causal, void* stream) {
+attn_status_t attn_fp8_quantize(const void* x, const int64_t x_strides[3], uint8_t* x8, float* scales, int B, int H,
+                                int S, int D, int block_rows, const int8_t* signs, void* stream) {
+  return quantize_8bit("attn_fp8_quantize launch", attn::launch_fp8_quantize, x, x_strides, x8, scales, B, H, S, D,
+                       block_rows, signs, stream);
+}
+
+attn_status_t attn_int8_quantize(const void* x, const int64_t x_strides[3], int8_t* x8, float* scales, int B, int H,
+                                 int S, int D, int block_rows, const int8_t* signs, void* stream) {
+  return quantize_8bit("attn_int8_quantize launch", attn::launch_int8_quantize, x, x_strides, (uint8_t*)x8, scales,
+                       B, H, S, D, block_rows, signs, stream);
+}
+
+typedef hipError_t (*fwd8_launcher_t)(const attn::Fp8Args&, int, bool, hipStream_t);
+
+static attn_status_t fwd_8bit(const char* name, fwd8_launcher_t launch, const uint8_t* q8, const float* q_scale,
+                              const uint8_t* k8, const float* k_scale, const uint8_t* v8, const float* v_scale,
+                              int block_rows, void* o, float* lse, int B, int H, int Sq, int Sk, int D,
+                              float softmax_scale, int causal, void* stream) {
   attn_status_t st;
   if (B < 0 || H < 0 || Sq < 0 || Sk < 0) return fail(ATTN_ERR_INVALID, "negative size");
   if (D <= 0) return fail(ATTN_ERR_INVALID, "head_dim %d must be positive", D);
@@ -397,7 +417,21 @@ attn_status_t attn_fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_
   a.block_rows = block_rows;
   a.scale_log2 = softmax_scale * attn::kLog2e;
   a.n_qblk = (int)n_qblk;
-  return hip_status(attn::launch_fwd_fp8(a, D, causal != 0, (hipStream_t)stream), "attn_fwd_fp8 launch");
+  return hip_status(launch(a, D, causal != 0, (hipStream_t)stream), name);
+}
+
+attn_status_t attn_fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
+                           const uint8_t* v8, const float* v_scale, int block_rows, void* o, float* lse, int B,
+                           int H, int Sq, int Sk, int D, float softmax_scale, int causal, void* stream) {
+  return fwd_8bit("attn_fwd_fp8 launch", attn::launch_fwd_fp8, q8, q_scale, k8, k_scale, v8, v_scale, block_rows, o,
+                  lse, B, H, Sq, Sk, D, softmax_scale, causal, stream);
+}
+
+attn_status_t attn_fwd_int8(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+                            const uint8_t* v8, const float* v_scale, int block_rows, void* o, float* lse, int B,
+                            int H, int Sq, int Sk, int D, float softmax_scale, int causal, void* stream) {
+  return fwd_8bit("attn_fwd_int8 launch", attn::launch_fwd_int8, (const uint8_t*)q8, q_scale, (const uint8_t*)k8,
+                  k_scale, v8, v_scale, block_rows, o, lse, B, H, Sq, Sk, D, softmax_scale, causal, stream);
 }
 
 }  // extern "C"

@@ -109,6 +109,15 @@ __device__ __forceinline__ void dma16_buf(i32x4 rsrc, uint32_t voffset, void* ld
   raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16, (int)voffset, 0, 0, 0);
 }
 
+// 8-bit integer: D(32x32, int32) += A(32x32) * B(32x32), 16 int8 values per
+// lane; lane l supplies row (l % 32) of A / column (l % 32) of B and the
+// k-slice selected by l / 32 (the same (lane, byte) -> k map for A and B).
+// The int32 sums are exact; the accumulator layout is that of the fp32 forms.
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ i32x16 mfma32_i8(i32x4 a, i32x4 b, i32x16 c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
 // wait until every global load (including LDS DMA) issued by this wave is done
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

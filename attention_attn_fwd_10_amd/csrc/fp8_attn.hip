@@ -24,6 +24,14 @@
 //  * the row sum is accumulated from the e4m3-rounded probabilities, the same
 //    values the second GEMM multiplies, so a row dominated by a few keys keeps
 //    its weights consistent.
+//
+// The int8 variant (QK_I8) takes int8 Q and K codes (the case study's int8
+// path; block scales and rotation as above) and computes the scores on
+// v_mfma_i32_32x32x32_i8, whose int32 sums are exact; V and the probabilities
+// stay e4m3.  Its accumulator starts at the bit pattern of 1.5 * 2^23 instead
+// of zero: a score s (|s| <= 128 * 127^2 < 2^22) then lands in the mantissa,
+// and the accumulator read as a float is exactly 1.5 * 2^23 + s, so the
+// conversion costs no instruction — the offset is folded into the exp2 bias.
 #include <type_traits>
 
 #include "common.hpp"
@@ -70,9 +78,11 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
 template <int N>
 using C = std::integral_constant<int, N>;
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool QK_I8>
 __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
   using namespace fp8cfg;
+  // score offset of the int8 form (see the file comment); 0 for e4m3
+  constexpr float kSOff = QK_I8 ? 12582912.0f : 0.0f;
   // two-slot rings (tile j in slot j % 2) as four separate arrays, addressed
   // with compile-time slot numbers: the compiler then sees that a tile's LDS
   // reads never touch the slot the next tile is being copied into, and does
@@ -120,13 +130,17 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
   cfloat* const vs_scale = (cfloat*)(blocked ? a.vs + (int64_t)bh * nbk : a.vs);
   const float qk_scale = sq * a.scale_log2;
 
-  // Q fragments: lane (query l32, half hh) holds q[64kk + 32hh .. +31]
+  // Q fragments: lane (query l32, half hh) holds q[64kk + 32hh .. +31] (e4m3,
+  // one 64-wide k step per qf[kk]) or q[64kk + 16hh .. +15] and
+  // q[64kk + 32 + 16hh .. +15] (int8, two 32-wide k steps per qf[kk])
+  constexpr int kHalfStride = QK_I8 ? 16 : 32;  // bytes between the two lane halves
+  constexpr int kSecond = QK_I8 ? 32 : 16;      // bytes between a lane's two 16-byte runs
   i32x8 qf[2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     if (qi < Lq) {
-      const uint8_t* qp = a.q + qoff + (int64_t)qi * row_q + 64 * kk + 32 * hh;
-      const u32x4 x0 = *(const u32x4*)qp, x1 = *(const u32x4*)(qp + 16);
+      const uint8_t* qp = a.q + qoff + (int64_t)qi * row_q + 64 * kk + kHalfStride * hh;
+      const u32x4 x0 = *(const u32x4*)qp, x1 = *(const u32x4*)(qp + kSecond);
       qf[kk] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
     } else {
       qf[kk] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
@@ -199,22 +213,44 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
     if (CAUSAL && key0 > wave_last_key) return;
     const float c2 = qk_scale * ks_scale[blocked ? key0 >> 7 : 0];
     const float sv = vs_scale[blocked ? key0 >> 7 : 0];
-    // S^T = K Q^T: two 32-key tiles, two 64-wide k steps each
-    const uint8_t* ks = (decltype(buf)::value ? lds_k1 : lds_k0) + l32 * PITCH + 32 * hh;
+    // S^T = K Q^T: two 32-key tiles, two 64-wide k steps each (K operands laid
+    // out like the Q fragments)
+    const uint8_t* ks = (decltype(buf)::value ? lds_k1 : lds_k0) + l32 * PITCH + kHalfStride * hh;
     i32x8 kop[2][2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const u32x4 x0 = *(const u32x4*)(ks + tt * 32 * PITCH + 64 * kk);
-        const u32x4 x1 = *(const u32x4*)(ks + tt * 32 * PITCH + 64 * kk + 16);
+        const u32x4 x1 = *(const u32x4*)(ks + tt * 32 * PITCH + 64 * kk + kSecond);
         kop[tt][kk] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
       }
     f32x16 s[2];
+    if constexpr (QK_I8) {
+      i32x16 acc[2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) s[tt] = mfma32_fp8(kop[tt][0], qf[0], zero16);
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) s[tt] = mfma32_fp8(kop[tt][1], qf[1], s[tt]);
+        for (int r = 0; r < 16; ++r) acc[tt][r] = 0x4B400000;  // the bits of 1.5 * 2^23
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const i32x8& kv = kop[tt][kk];
+            const i32x8& qv = qf[kk];
+            acc[tt] = mfma32_i8(i32x4{kv[4 * half], kv[4 * half + 1], kv[4 * half + 2], kv[4 * half + 3]},
+                                i32x4{qv[4 * half], qv[4 * half + 1], qv[4 * half + 2], qv[4 * half + 3]}, acc[tt]);
+          }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) s[tt] = __builtin_bit_cast(f32x16, acc[tt]);
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) s[tt] = mfma32_fp8(kop[tt][0], qf[0], zero16);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) s[tt] = mfma32_fp8(kop[tt][1], qf[1], s[tt]);
+    }
     // register r of tile tt holds key key0 + 32hh + 16tt + r
     const bool need_mask = (key0 + BC > Lk) || (CAUSAL && key0 + BC - 1 > qw + diag);
     if (need_mask) {
@@ -231,7 +267,7 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
     for (int i = 1; i < 31; i += 2) mx = max3(mx, s[i >> 4][i & 15], s[(i + 1) >> 4][(i + 1) & 15]);
     mx = max3(mx, s[1][15], s[1][15]);
     const auto mxw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    const float mxs = max3(mx, __uint_as_float(mxw[0]), __uint_as_float(mxw[1])) * c2;
+    const float mxs = (max3(mx, __uint_as_float(mxw[0]), __uint_as_float(mxw[1])) - kSOff) * c2;
     // a larger V block scale becomes the accumulator's reference (uniform branch)
     if (sv > sv_ref) {
       const float ratio = sv_ref * __builtin_amdgcn_rcpf(sv);
@@ -256,7 +292,10 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
     // keeps p' = p'' * sv_ref / sv (approximate reciprocals: both factors only
     // need to be consistent to float precision)
     const float vratio = sv * __builtin_amdgcn_rcpf(sv_ref), inv_vratio = sv_ref * __builtin_amdgcn_rcpf(sv);
-    const float bias = m_run == -INFINITY ? 0.f : kMu + __log2f(vratio) - m_run;
+    float bias = m_run == -INFINITY ? 0.f : kMu + __log2f(vratio) - m_run;
+    // the int8 score offset enters once per tile: kSOff * c2 is rounded once,
+    // a shift shared by the whole tile of at most one score unit
+    if constexpr (QK_I8) bias -= kSOff * c2;
     // the row sum adds the e4m3-rounded probabilities, exactly the values the
     // MFMA multiplies, so numerator and denominator share the rounding
     // (the logsumexp keeps the float32 sum)
@@ -333,14 +372,23 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
   }
 }
 
-hipError_t launch_fwd_fp8(const Fp8Args& a, int D, bool causal, hipStream_t s) {
+template <bool QK_I8>
+static hipError_t launch_8bit(const Fp8Args& a, int D, bool causal, hipStream_t s) {
   if (D != fp8cfg::D) return hipErrorNotSupported;
   const int n = a.B * a.H * a.n_qblk;
   if (causal)
-    hipLaunchKernelGGL((fwd_fp8_kernel<true>), dim3(n), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fwd_fp8_kernel<true, QK_I8>), dim3(n), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((fwd_fp8_kernel<false>), dim3(n), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fwd_fp8_kernel<false, QK_I8>), dim3(n), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(const Fp8Args& a, int D, bool causal, hipStream_t s) {
+  return launch_8bit<false>(a, D, causal, s);
+}
+
+hipError_t launch_fwd_int8(const Fp8Args& a, int D, bool causal, hipStream_t s) {
+  return launch_8bit<true>(a, D, causal, s);
 }
 
 }  // namespace attn

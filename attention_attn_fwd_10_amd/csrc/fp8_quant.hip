@@ -5,6 +5,10 @@
 // (or one per tensor for the baseline), scale = amax / 448, code =
 // e4m3fn(x / scale) with round-to-nearest-even and saturation.
 //
+// The int8 form (the case study's int8 path) quantises symmetrically instead:
+// scale = amax / 127, code = x / scale rounded to nearest-even and clamped to
+// [-127, 127].
+//
 // This step streams every element once from HBM and writes a byte back, so it
 // is bandwidth bound; a workgroup owns one 128-row block of one head, holds
 // the whole block in registers (16 values per lane), reduces the block amax
@@ -32,9 +36,20 @@ __device__ __forceinline__ uint32_t e4m3_encode(float x) {
   return ((e << 3) | m) | sign;
 }
 
-enum QuantMode { kQuantBlock = 0, kAmaxOnly = 1, kQuantGlobal = 2 };
+// float32 (already divided by the scale) -> int8 code: nearest-even, clamped
+// to [-127, 127], returned as its byte
+__device__ __forceinline__ uint32_t int8_encode(float y) {
+  const float r = fminf(fmaxf(__builtin_rintf(y), -127.f), 127.f);
+  return (uint32_t)(int32_t)r & 0xffu;
+}
 
-template <int D, int MODE>
+enum QuantMode { kQuantBlock = 0, kAmaxOnly = 1, kQuantGlobal = 2 };
+enum QuantFormat { kE4M3 = 0, kInt8 = 1 };
+
+template <int FMT>
+constexpr float code_max() { return FMT == kInt8 ? 127.f : 448.f; }
+
+template <int D, int MODE, int FMT>
 __global__ void __launch_bounds__(256) fp8_quant_kernel(QuantArgs a) {
   constexpr int LPR = D / 16;          // lanes per row (16 values per lane)
   constexpr int RP = 256 / LPR;        // rows per pass
@@ -113,7 +128,7 @@ __global__ void __launch_bounds__(256) fp8_quant_kernel(QuantArgs a) {
     return;
   }
   if constexpr (MODE == kQuantGlobal) amax = a.scales[0];
-  const float scale = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
+  const float scale = amax > 0.f ? __fdiv_rn(amax, code_max<FMT>()) : 1.f;
   if constexpr (MODE == kQuantBlock)
     if (tid == 0) a.scales[(int64_t)bh * nblk + blk] = scale;
 
@@ -126,7 +141,10 @@ __global__ void __launch_bounds__(256) fp8_quant_kernel(QuantArgs a) {
       for (int wd = 0; wd < 4; ++wd) {
         uint32_t v = 0;
 #pragma unroll
-        for (int by = 0; by < 4; ++by) v |= e4m3_encode(__fdiv_rn(x[p][4 * wd + by], scale)) << (8 * by);
+        for (int by = 0; by < 4; ++by) {
+          const float y = __fdiv_rn(x[p][4 * wd + by], scale);
+          v |= (FMT == kInt8 ? int8_encode(y) : e4m3_encode(y)) << (8 * by);
+        }
         out[wd] = v;
       }
       *(u32x4*)(a.x8 + (((int64_t)b * a.S + row) * a.H + h) * D + 16 * seg) = out;
@@ -136,30 +154,34 @@ __global__ void __launch_bounds__(256) fp8_quant_kernel(QuantArgs a) {
 
 // per-tensor mode helpers: clear the reduction cell, then turn amax into the scale
 __global__ void fp8_fill_kernel(float* p, float v) { *p = v; }
-__global__ void fp8_finalize_scale_kernel(float* p) {
+__global__ void fp8_finalize_scale_kernel(float* p, float code_max) {
   const float amax = *p;
-  *p = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
+  *p = amax > 0.f ? __fdiv_rn(amax, code_max) : 1.f;
 }
 
-template <int D>
+template <int D, int FMT>
 hipError_t launch_quant_d(const QuantArgs& a, hipStream_t s) {
   const int nblk = (a.S + 127) / 128;
   const dim3 grid(a.B * a.H * nblk), block(256);
   if (a.block_rows == 128) {
-    hipLaunchKernelGGL((fp8_quant_kernel<D, kQuantBlock>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((fp8_quant_kernel<D, kQuantBlock, FMT>), grid, block, 0, s, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(fp8_fill_kernel, dim3(1), dim3(1), 0, s, a.scales, 0.f);
-  hipLaunchKernelGGL((fp8_quant_kernel<D, kAmaxOnly>), grid, block, 0, s, a);
-  hipLaunchKernelGGL((fp8_quant_kernel<D, kQuantGlobal>), grid, block, 0, s, a);
-  hipLaunchKernelGGL(fp8_finalize_scale_kernel, dim3(1), dim3(1), 0, s, a.scales);
+  hipLaunchKernelGGL((fp8_quant_kernel<D, kAmaxOnly, FMT>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((fp8_quant_kernel<D, kQuantGlobal, FMT>), grid, block, 0, s, a);
+  hipLaunchKernelGGL(fp8_finalize_scale_kernel, dim3(1), dim3(1), 0, s, a.scales, code_max<FMT>());
   return hipGetLastError();
 }
 
-hipError_t launch_fp8_quantize(const QuantArgs& a, int D, hipStream_t s) {
-  if (D == 64) return launch_quant_d<64>(a, s);
-  if (D == 128) return launch_quant_d<128>(a, s);
-  return launch_quant_d<256>(a, s);
+template <int FMT>
+static hipError_t launch_quant(const QuantArgs& a, int D, hipStream_t s) {
+  if (D == 64) return launch_quant_d<64, FMT>(a, s);
+  if (D == 128) return launch_quant_d<128, FMT>(a, s);
+  return launch_quant_d<256, FMT>(a, s);
 }
+
+hipError_t launch_fp8_quantize(const QuantArgs& a, int D, hipStream_t s) { return launch_quant<kE4M3>(a, D, s); }
+hipError_t launch_int8_quantize(const QuantArgs& a, int D, hipStream_t s) { return launch_quant<kInt8>(a, D, s); }
 
 }  // namespace attn

@@ -74,6 +74,7 @@ def parse():
     p.add_argument("--causal", action="store_true", help="time the causal variant instead")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-fp8", action="store_true")
+    p.add_argument("--no-int8", action="store_true", help="skip the int8-score leg")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--sweep", action="store_true", help="also time the 16384-token seq sweep (extra output)")
     p.add_argument("--no-decode", action="store_true", help="skip the long-cache decoding leg")
@@ -199,6 +200,9 @@ def main():
     if not args.no_fp8:
         result["fp8"] = bench_fp8(A, W, args)
 
+    if not args.no_int8:
+        result["int8"] = bench_int8(A, W, args)
+
     if not args.no_decode:
         result["decode"] = bench_decode(A, W, args)
 
@@ -240,6 +244,33 @@ def bench_fp8(A, W, args):
             "quantize_ms_per_tensor": round(ms_q, 4),
             "quantize_gbs": round(q_bytes / (ms_q * 1e-3) / 1e9, 1),
             "end_to_end_ms": round(ms + 3 * ms_q, 4)}
+
+
+def bench_int8(A, W, args):
+    """int8 Q/K (block scales + rotation), e4m3 V, on the 8-bit workload;
+    int8 and fp8 share the dense 5.0 POP/s peak."""
+    import torch
+    w = W.WORKLOADS["fp8"]
+    qs, _ = w.shapes()
+    qh, kh, vh = W.qkv_outlier(w.seed, qs)
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in (qh, kh, vh))
+    signs = torch.from_numpy(W.random_signs(4, w.head_dim)).cuda()
+    try:
+        q8, qsc = A.int8_quantize(q, 128, signs)
+        k8, ksc = A.int8_quantize(k, 128, signs)
+        v8, vsc = A.fp8_quantize(v, 128, None)
+        o = torch.empty((w.batch, w.seq_q, w.heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((w.batch, w.heads, w.seq_q), dtype=torch.float32, device="cuda")
+        ms = time_launches(lambda: A.fwd_int8(q8, qsc, k8, ksc, v8, vsc, 128, w.scale, False, out=o, lse=lse),
+                           args.steps, args.warmup)
+        ms_q = time_launches(lambda: A.int8_quantize(q, 128, signs, out=q8, scales=qsc), args.steps, 2)
+    except A.AttnError as e:
+        return {"available": False, "reason": str(e)}
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    print(f"[bench] int8 fwd {ms:.3f} ms  {tflops:.1f} TOP/s", file=sys.stderr, flush=True)
+    return {"available": True, "workload": w.name, "ms": round(ms, 4), "tops": round(tflops, 2),
+            "pct_of_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2), "peak": PEAK_FP8_TFLOPS,
+            "quantize_ms_per_tensor": round(ms_q, 4)}
 
 
 def bench_decode(A, W, args):

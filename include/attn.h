@@ -150,6 +150,45 @@ attn_status_t attn_fwd_fp8(const uint8_t* q8, const float* q_scale,
                            float softmax_scale, int causal, void* stream);
 
 /*
+ * attn_int8_quantize — the int8 prologue for Q or K.
+ * (The StreamHPC case study lists an int8 path beside the fp8 one; the
+ * "Fused attention kernel" page, section "8-bit forward pass", gives the block
+ * quantisation and the random-sign Hadamard rotation it shares.)
+ *
+ * Arguments as for attn_fp8_quantize, except:
+ * x8: int8 [B, S, H, D] contiguous; each scale is amax / 127 in float32 (1 for
+ *   an all-zero block) and each code is x' / scale (a correctly rounded
+ *   float32 division) rounded to nearest-even and clamped to [-127, 127].
+ */
+attn_status_t attn_int8_quantize(const void* x, const int64_t x_strides[3],
+                                 int8_t* x8, float* scales,
+                                 int B, int H, int S, int D,
+                                 int block_rows, const int8_t* signs, void* stream);
+
+/*
+ * attn_fwd_int8 — fused forward with int8 scores.
+ * (StreamHPC case study, "Our approach": an int8 path of the fused kernel;
+ * the block scales and the rotation are those of the "Fused attention kernel"
+ * page's 8-bit section.)  Q K^T runs on the int8 matrix cores and sums exactly
+ * in int32; V and the probabilities keep the e4m3 format of attn_fwd_fp8
+ * (a fixed-point int8 probability would round every key below 1/254 of the
+ * row maximum to zero).
+ *
+ * q8: int8 [B, Sq, H, D], k8: int8 [B, Sk, H, D], both from
+ *   attn_int8_quantize with the same `signs` (or none for both);
+ * v8: e4m3 [B, Sk, H, D] from attn_fp8_quantize without rotation;
+ * all contiguous, with scales as for attn_fwd_fp8 (all three with the same
+ * block_rows).  Outputs, errors and D = 128 as for attn_fwd_fp8.
+ */
+attn_status_t attn_fwd_int8(const int8_t* q8, const float* q_scale,
+                            const int8_t* k8, const float* k_scale,
+                            const uint8_t* v8, const float* v_scale,
+                            int block_rows,
+                            void* o, float* lse,
+                            int B, int H, int Sq, int Sk, int D,
+                            float softmax_scale, int causal, void* stream);
+
+/*
  * attn_fwd_varlen — packed variable-length batch, optionally with a paged KV
  * cache.  (The StreamHPC case study lists Paged Attention and Varlen Attention
  * among the features of its fused kernel.)

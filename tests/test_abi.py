@@ -30,6 +30,8 @@ def lib():
     L.attn_fwd.argtypes = [I, P, I64P, P, I64P, P, I64P, P, I64P, P, I, I, I, I, I, F, I, P]
     L.attn_fp8_quantize.argtypes = [P, I64P, P, P, I, I, I, I, I, P, P]
     L.attn_fwd_fp8.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, I, F, I, P]
+    L.attn_int8_quantize.argtypes = [P, I64P, P, P, I, I, I, I, I, P, P]
+    L.attn_fwd_int8.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, I, F, I, P]
     L.attn_fwd_varlen.argtypes = [I, P, P, P, P, P, P, I, I, P, P, I, I, I, I, I, I, F, I, P]
     L.attn_fwd_splitkv.argtypes = [I, P, P, P, P, P, P, I, I, P, P, I, I, I, I, I, I, F, I, I, P,
                                    ctypes.c_size_t, P]
@@ -51,7 +53,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("attn_fwd", "attn_fp8_quantize", "attn_fwd_fp8", "attn_fwd_varlen", "attn_fwd_splitkv",
-              "attn_fwd_splitkv_workspace_bytes", "attn_fwd_bias", "attn_status_string", "attn_last_error"):
+              "attn_fwd_splitkv_workspace_bytes", "attn_fwd_bias", "attn_int8_quantize", "attn_fwd_int8",
+              "attn_status_string", "attn_last_error"):
         assert n in names
 
 
@@ -108,10 +111,12 @@ def test_null_stride_array(lib):
     assert lib.attn_fwd(0, A16, None, A16, GOOD, A16, GOOD, A16, GOOD, None, 1, 1, 1, 1, 128, 0.1, 0, None) == INVALID
 
 
-def test_quantize_validation(lib):
-    q = lambda **k: lib.attn_fp8_quantize(k.get("x", A16), k.get("xs", GOOD), k.get("x8", A16), k.get("sc", A16),
-                                          k.get("B", 1), k.get("H", 1), k.get("S", 1), k.get("D", 128),
-                                          k.get("br", 128), None, None)
+@pytest.mark.parametrize("name", ["attn_fp8_quantize", "attn_int8_quantize"])
+def test_quantize_validation(lib, name):
+    fn = getattr(lib, name)
+    q = lambda **k: fn(k.get("x", A16), k.get("xs", GOOD), k.get("x8", A16), k.get("sc", A16),
+                       k.get("B", 1), k.get("H", 1), k.get("S", 1), k.get("D", 128),
+                       k.get("br", 128), None, None)
     assert q(br=64) == INVALID
     assert q(D=96) == UNSUPPORTED
     assert q(x=None) == INVALID
@@ -120,9 +125,11 @@ def test_quantize_validation(lib):
     assert q(S=0) == OK
 
 
-def test_fp8_fwd_validation(lib):
-    f = lambda **k: lib.attn_fwd_fp8(A16, A16, A16, A16, A16, A16, k.get("br", 128), A16, None, 1, 1, 1, 1,
-                                     k.get("D", 128), k.get("scale", 0.1), k.get("causal", 0), None)
+@pytest.mark.parametrize("name", ["attn_fwd_fp8", "attn_fwd_int8"])
+def test_fp8_fwd_validation(lib, name):
+    fn = getattr(lib, name)
+    f = lambda **k: fn(A16, A16, A16, A16, A16, A16, k.get("br", 128), A16, None, 1, 1, 1, 1,
+                       k.get("D", 128), k.get("scale", 0.1), k.get("causal", 0), None)
     assert f(D=64) == UNSUPPORTED
     assert f(D=-1) == INVALID
     assert f(br=7) == INVALID

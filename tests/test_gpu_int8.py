@@ -1,0 +1,207 @@
+"""GPU parity of the int8 path: the int8 quantiser (attn_int8_quantize) and the
+forward with int8 scores (attn_fwd_int8), against the float64 oracle.
+
+* Quantiser without rotation: codes and scales are bit-exact (scale = amax/127
+  and the code decision are taken in float32 on both sides).  With the
+  rotation the GPU evaluates the Hadamard transform in float32 and the oracle
+  in float64, so a code may differ by one step where the rotated value sits on
+  a rounding boundary.
+* The forward, fed the oracle's own codes (int8 Q, K; e4m3 V), is compared
+  with float64 attention of the dequantised codes.  The scores are exact int32
+  sums; what remains is the e4m3 rounding of the probabilities and float32
+  arithmetic, so the bounds are those of the e4m3 forward: RMSE <= 5e-3,
+  max <= 6e-2, LSE <= 1e-3.
+* On the outlier workload (batch 4, 16 heads, seq 8192, d128, 0.1 % N(0,100)
+  outliers) the pipeline with block scales and the rotation must reach
+  RMSE <= 1.2e-2 against float64 exact attention (the 8-bit bound) and beat
+  the per-tensor int8 baseline built in the same run."""
+import math
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as OA
+from oracle import fp8 as OF
+from oracle import int8 as OI
+from tests.parity import sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import attention_attn_fwd_10_amd as A
+    return A
+
+
+def _dev(x, dt):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=dt)).cuda()
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("s", [128, 300])
+@pytest.mark.parametrize("block_rows", [128, 0])
+def test_quantize_bitexact_without_rotation(lib, d, s, block_rows):
+    import torch
+    x, _, _ = W.qkv_outlier(140 + d + s, (2, s, 3, d))
+    codes, scales = lib.int8_quantize(to_dev(x), block_rows, None)
+    torch.cuda.synchronize()
+    rc, rs = OI.quantize(x, block_rows)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+
+
+def test_quantize_ties_and_zero_block(lib):
+    """Values that sit exactly on half-codes (ties go to even) and an all-zero
+    block (scale 1, codes 0)."""
+    import torch
+    d = 64
+    x = np.zeros((1, 256, 1, d), dtype=np.float32)
+    # block 0: amax 127 -> scale 1, so x / scale is x itself: exact ties
+    half = (np.arange(128 * d).reshape(128, d) % 254 - 127).astype(np.float32) + 0.5
+    half = np.clip(half, -126.5, 126.5)
+    half[0, 0] = 127.0
+    x[0, :128, 0] = half
+    codes, scales = lib.int8_quantize(to_dev(x), 128, None)
+    torch.cuda.synchronize()
+    rc, rs = OI.quantize(x, 128)
+    assert rs[0, 0, 0] == 1.0 and rs[0, 0, 1] == 1.0
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+    assert (rc[0, 128:] == 0).all()
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_quantize_with_rotation_within_one_step(lib, d):
+    import torch
+    x, _, _ = W.qkv_outlier(150 + d, (2, 300, 3, d))
+    signs = W.random_signs(4, d)
+    codes, scales = lib.int8_quantize(to_dev(x), 128, torch.from_numpy(signs).cuda())
+    torch.cuda.synchronize()
+    xr = OF.rotate(x, signs).astype(np.float32)
+    rc, rs = OI.quantize(xr, 128)
+    np.testing.assert_allclose(scales.cpu().numpy(), rs, rtol=1e-5, atol=0)
+    got = codes.cpu().numpy().astype(np.int32)
+    assert np.abs(got - rc.astype(np.int32)).max() <= 1
+    assert (got != rc).mean() < 1e-2
+
+
+def _run_int8(lib, qp, causal, scale):
+    import torch
+    o, lse = lib.fwd_int8(_dev(qp["q8"], np.int8), _dev(qp["q_scale"], np.float32), _dev(qp["k8"], np.int8),
+                          _dev(qp["k_scale"], np.float32), _dev(qp["v8"], np.uint8),
+                          _dev(qp["v_scale"], np.float32), qp["block_rows"], scale, causal)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def _check_vs_dequantised(o, lse, qp, causal, scale):
+    qd, kd, vd = OI.dequantize_pipeline(qp)
+    o_ref, lse_ref = OA.attention_bshd(qd, kd, vd, scale, causal)
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(fin, np.isfinite(lse))
+    if fin.any():
+        assert np.abs(lse[fin] - lse_ref[fin]).max() <= 1e-3
+    err = o - o_ref
+    rmse = float(np.sqrt(np.mean(err ** 2)))
+    assert rmse <= 5e-3, rmse
+    assert np.abs(err).max() <= 6e-2, np.abs(err).max()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("block_rows", [128, 0])
+@pytest.mark.parametrize("sq,sk", [(256, 256), (200, 333), (333, 200), (1, 1), (130, 64), (300, 192),
+                                   (260, 1000), (700, 520)])
+def test_fwd_int8_vs_dequantised_attention(lib, causal, block_rows, sq, sk):
+    d = 128
+    q, k, v = W.qkv_normal(160 + sq, (2, sq, 2, d), (2, sk, 2, d))
+    signs = W.random_signs(4, d)
+    qp = OI.quantize_pipeline(q, k, v, signs, block_rows)
+    o, lse = _run_int8(lib, qp, causal, 1 / math.sqrt(d))
+    _check_vs_dequantised(o, lse, qp, causal, 1 / math.sqrt(d))
+
+
+@pytest.mark.parametrize("ntiles", [3, 8, 16])
+def test_fwd_int8_long_key_ranges(lib, ntiles):
+    """Several 128-row scale blocks and odd/even tile counts of 64 keys."""
+    d = 128
+    sk = 64 * ntiles
+    q, k, v = W.qkv_normal(170 + ntiles, (1, 200, 2, d), (1, sk, 2, d))
+    qp = OI.quantize_pipeline(q, k, v, W.random_signs(4, d), 128)
+    for causal in (False, True):
+        o, lse = _run_int8(lib, qp, causal, 1 / math.sqrt(d))
+        _check_vs_dequantised(o, lse, qp, causal, 1 / math.sqrt(d))
+
+
+def test_fwd_int8_extreme_codes(lib):
+    """Every code at +-127, so the int32 scores reach +-128 * 127^2 (the range
+    the float read of the accumulator relies on)."""
+    d = 128
+    rng = np.random.default_rng(181)
+    sgn = np.where(rng.random((1, 192, 2, d)) < 0.5, -1.0, 1.0).astype(np.float32)
+    q = sgn[:, :128].copy()
+    q[:, 0] = 1.0                              # row 0 matches key 0 at every position
+    k = sgn.copy()
+    k[:, 0] = 1.0
+    v = rng.standard_normal((1, 192, 2, d)).astype(np.float32)
+    qp = OI.quantize_pipeline(q, k, v, None, 128)
+    assert (np.abs(qp["q8"]) == 127).all() and (np.abs(qp["k8"]) == 127).all()
+    scale = 0.05                               # keeps the extreme scores' softmax non-degenerate
+    o, lse = _run_int8(lib, qp, False, scale)
+    _check_vs_dequantised(o, lse, qp, False, scale)
+
+
+def test_fwd_int8_empty_rows_and_determinism(lib):
+    d = 128
+    q, k, v = W.qkv_normal(177, (1, 300, 2, d), (1, 100, 2, d))
+    qp = OI.quantize_pipeline(q, k, v, None, 128)
+    o1, l1 = _run_int8(lib, qp, True, 1 / math.sqrt(d))
+    o2, l2 = _run_int8(lib, qp, True, 1 / math.sqrt(d))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    assert np.all(o1[:, :200] == 0) and np.all(np.isneginf(l1[:, :, :200]))
+
+
+def _rows_ref(q, k, v, scale, rows):
+    B, S, H, D = q.shape
+    o = np.zeros((B, len(rows), H, D))
+    for b in range(B):
+        for h in range(H):
+            oo, _ = OA.naive_head(q[b, rows, h], k[b, :, h], v[b, :, h], scale, False, rows=rows, lq=S)
+            o[b, :, h] = oo
+    return o
+
+
+def test_outlier_workload_accuracy(lib):
+    """batch 4, 16 heads, seq 8192, d128: int8 Q/K with block-128 scales and
+    the random-sign Hadamard rotation vs per-tensor scales, both through the
+    GPU pipeline; the e4m3 forward is reported beside them."""
+    import torch
+    w = W.WORKLOADS["fp8"]
+    qs, _ = w.shapes()
+    q, k, v = W.qkv_outlier(w.seed, qs)
+    signs = torch.from_numpy(W.random_signs(4, w.head_dim)).cuda()
+    tq, tk, tv = to_dev(q), to_dev(k), to_dev(v)
+    rows = sample_rows(w.seq_q, seed=31, n_random=40)
+    o_ref = _rows_ref(q, k, v, w.scale, rows)
+    out = {}
+    for name, br, sg in (("block+hadamard", 128, signs), ("per-tensor", 0, None)):
+        q8, qsc = lib.int8_quantize(tq, br, sg)
+        k8, ksc = lib.int8_quantize(tk, br, sg)
+        v8, vsc = lib.fp8_quantize(tv, br, None)
+        o, _ = lib.fwd_int8(q8, qsc, k8, ksc, v8, vsc, br, w.scale, False)
+        torch.cuda.synchronize()
+        out[name] = OF.rmse(o[:, rows].float().cpu().numpy().astype(np.float64), o_ref)
+    q8, qsc = lib.fp8_quantize(tq, 128, signs)
+    k8, ksc = lib.fp8_quantize(tk, 128, signs)
+    v8, vsc = lib.fp8_quantize(tv, 128, None)
+    o, _ = lib.fwd_fp8(q8, qsc, k8, ksc, v8, vsc, 128, w.scale, False)
+    torch.cuda.synchronize()
+    out["e4m3 block+hadamard"] = OF.rmse(o[:, rows].float().cpu().numpy().astype(np.float64), o_ref)
+    print(out)
+    assert out["block+hadamard"] <= 1.2e-2, out
+    assert out["block+hadamard"] < out["per-tensor"], out
