@@ -10,6 +10,7 @@ The entry points mirror the C ABI in ``include/attn.h``:
 * ``int8_quantize``  -> ``attn_int8_quantize``  (rotation + int8 block quantisation)
 * ``fwd_int8``       -> ``attn_fwd_int8``       (int8 scores, e4m3 V and probabilities)
 * ``fwd_varlen``     -> ``attn_fwd_varlen``     (packed sequences, optional paged KV)
+* ``bwd``            -> ``attn_bwd``            (dq, dk, dv of the dense forward)
 
 Tensors use the [batch, seq, heads, head_dim] layout (varlen: [tokens, heads,
 head_dim]).  If the library has not been built, the first call raises
@@ -21,7 +22,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "fp8_quantize", "fwd_fp8", "int8_quantize", "fwd_int8", "fwd_varlen", "lib_path", "AttnError",
+__all__ = ["fwd", "fp8_quantize", "fwd_fp8", "int8_quantize", "fwd_int8", "fwd_varlen", "bwd", "lib_path", "AttnError",
            "ATTN_BF16", "ATTN_FP16"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -57,6 +58,8 @@ def _load():
     lib.attn_fp8_quantize.restype = I
     lib.attn_fwd_fp8.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, I, F, I, P]
     lib.attn_fwd_fp8.restype = I
+    lib.attn_bwd.argtypes = [I, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, P]
+    lib.attn_bwd.restype = I
     lib.attn_int8_quantize.argtypes = [P, I64P, P, P, I, I, I, I, I, P, P]
     lib.attn_int8_quantize.restype = I
     lib.attn_fwd_int8.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, I, F, I, P]
@@ -366,3 +369,31 @@ def fwd_splitkv(q, cu_seqlens_q, k, v, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                                  _ptr(lse), B, H, D, total_q, int(max_seqlen_q), int(max_seqlen_k), scale,
                                  int(bool(causal)), num_splits, _ptr(workspace), ws_bytes, _stream(stream)))
     return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None, dk=None, dv=None, delta=None,
+        stream=None):
+    """Gradients of ``fwd``: q, o, dout [B, Sq, H, D], k, v [B, Sk, H, D] (bf16
+    or fp16, contiguous), lse fp32 [B, H, Sq] from the forward.  Returns
+    (dq, dk, dv)."""
+    import torch
+    _require_cuda(q, k, v, o, lse, dout, dq, dk, dv, delta)
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    for t in (q, k, v, o, dout):
+        if not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o and dout must be contiguous and share a dtype")
+    if k.shape != (B, Sk, H, D) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("shapes must be q/o/dout [B, Sq, H, D] and k/v [B, Sk, H, D]")
+    if lse.dtype != torch.float32 or lse.shape != (B, H, Sq) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, Sq]")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if delta is None:
+        delta = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _check(_lib.attn_bwd(_dtype_code(q.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), B, H, Sq, Sk, D, scale, int(bool(causal)),
+                         _stream(stream)))
+    return dq, dk, dv

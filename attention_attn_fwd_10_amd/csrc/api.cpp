@@ -4,6 +4,7 @@
 // work was queued and nothing was written.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -13,6 +14,7 @@
 #include <string>
 
 #include "../../include/attn.h"
+#include "bwd.hpp"
 #include "common.hpp"
 
 namespace attn {
@@ -432,6 +434,38 @@ attn_status_t attn_fwd_int8(const int8_t* q8, const float* q_scale, const int8_t
                             int H, int Sq, int Sk, int D, float softmax_scale, int causal, void* stream) {
   return fwd_8bit("attn_fwd_int8 launch", attn::launch_fwd_int8, (const uint8_t*)q8, q_scale, (const uint8_t*)k8,
                   k_scale, v8, v_scale, block_rows, o, lse, B, H, Sq, Sk, D, softmax_scale, causal, stream);
+}
+
+attn_status_t attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int Sq, int Sk,
+                       int D, float softmax_scale, int causal, void* stream) {
+  attn_status_t st;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return fail(ATTN_ERR_INVALID, "dtype %d is not bf16 or fp16", dtype);
+  if (B < 0 || H < 0 || Sq < 0 || Sk < 0) return fail(ATTN_ERR_INVALID, "negative size");
+  if ((st = check_head_dim(D)) != ATTN_OK) return st;
+  if (D == 256) return fail(ATTN_ERR_UNSUPPORTED, "the backward pass supports head_dim 64 and 128 (got 256)");
+  if ((st = check_scale(softmax_scale)) != ATTN_OK) return st;
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID, "causal must be 0 or 1 (got %d)", causal);
+  if (B == 0 || H == 0 || (Sq == 0 && Sk == 0)) return ok();
+  if (Sq > 0 && (q == nullptr || o == nullptr || lse == nullptr || dout == nullptr || dq == nullptr ||
+                 delta == nullptr))
+    return fail(ATTN_ERR_INVALID, "q, o, lse, dout, dq or delta is NULL");
+  if (Sk > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
+    return fail(ATTN_ERR_INVALID, "k, v, dk or dv is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned16(lse) || !aligned16(delta))
+    return fail(ATTN_ERR_INVALID, "every tensor must be 16-byte aligned");
+  if ((int64_t)H * D > kMaxSeqStride) return fail(ATTN_ERR_INVALID, "H * D too large");
+  if ((int64_t)B * H * ((std::max(Sq, Sk) + kBR - 1) / kBR) > INT32_MAX)
+    return fail(ATTN_ERR_INVALID, "problem too large for one launch");
+  attn::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.delta = delta;
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * attn::kLog2e;
+  return hip_status(attn::launch_bwd(a, D, dtype == ATTN_BF16 ? attn::kBF16 : attn::kFP16, causal != 0,
+                                     (hipStream_t)stream), "attn_bwd launch");
 }
 
 }  // extern "C"

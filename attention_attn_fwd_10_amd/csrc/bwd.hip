@@ -1,0 +1,421 @@
+// Backward pass of the fused attention forward for gfx950 (the FlashAttention-3
+// summary page, Key Results: the method has a backward pass; the "Fused
+// attention kernel" page, When to use which: it follows the forward's
+// pattern).  Given dO, the forward's O and its logsumexp, it computes
+//
+//   P  = exp(scale Q K^T - LSE)            (recomputed tile by tile, masked)
+//   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - delta),   delta_i = <dO_i, O_i>
+//   dQ = scale dS K,   dK = scale dS^T Q
+//
+// without ever storing P or dS in HBM.  delta_i equals rowsum(P * dP) because
+// the rows of P sum to one and O = P V.
+//
+// Three kernels, none with atomics (every output element is summed by one
+// wave in a fixed order, so results are run-to-run identical):
+//  * bwd_delta_kernel: delta = rowsum(dO * O) in fp32, [B, H, Sq];
+//  * bwd_dkdv_kernel: a workgroup owns 128 keys of one (b, h) (32 per wave,
+//    their K and V rows in registers) and walks the query tiles of 64 rows,
+//    Q and dO tiles copied asynchronously into a two-stage LDS ring.  Per
+//    32-query sub-tile: S = Q K^T and dP = dO V^T on MFMA (Q and dO rows read
+//    from LDS in a bit-2/3-swapped order, so each lane's 16 results are two runs
+//    of 8 consecutive queries), P and dS in registers, then dV^T += dO^T P and
+//    dK^T += Q^T dS with dO^T and Q^T read through the LDS transposing read;
+//  * bwd_dq_kernel: the forward's layout — a workgroup owns 128 queries (32 per
+//    wave, Q and dO fragments in registers), walks the 64-key K/V tiles, forms
+//    S^T = K Q^T and dP^T = V dO^T, dS^T in registers, and dQ^T += K^T dS^T
+//    with K^T from the transposing read.
+// Masks follow the forward (causal bottom-right, keys past Lk excluded); rows
+// with no allowed key (LSE = -inf) and rows past Lq pass no gradient.
+#include "bwd.hpp"
+#include "common.hpp"
+
+namespace attn {
+
+namespace {
+
+template <int D>
+struct BwdCfg {
+  static constexpr int CPR = D / 8;          // 16-byte chunks per row
+  static constexpr int SLOTS = CPR + 1;      // one pad slot per LDS row
+  static constexpr int P = 8 * SLOTS;        // LDS row pitch in elements
+  static constexpr int TILE = 64 * P;        // elements of a 64-row tile
+};
+
+template <int DT>
+__device__ __forceinline__ float to_f32(uint16_t x) {
+  if constexpr (DT == kBF16) {
+    return __uint_as_float((uint32_t)x << 16);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, x);
+  }
+}
+
+// Asynchronous copy of a 64-row tile (rows of D 16-bit values, `row_elems`
+// apart in memory, starting at g) into LDS with the padded pitch; rows at or
+// past `valid` arrive as zeros without being read.  Slot s of the tile (16
+// bytes) is LDS row s / SLOTS, chunk s % SLOTS; the pad chunk is not copied.
+template <int D>
+__device__ __forceinline__ void copy_tile(const uint16_t* g, int64_t row_elems, int valid, uint16_t* lds,
+                                          int wave, int lane) {
+  using C = BwdCfg<D>;
+  const uint32_t row_bytes = 2u * (uint32_t)row_elems;
+  const uint64_t n = valid > 0 ? (uint64_t)valid * row_bytes : 0;
+  const i32x4 rs = make_rsrc(g, (uint32_t)min(n, (uint64_t)0x7fff0000u));
+#pragma unroll
+  for (int ii = 0; ii < (C::SLOTS + 3) / 4; ++ii) {
+    const int w = wave + 4 * ii;
+    if (w < C::SLOTS) {
+      const int s = 64 * w + lane;
+      const int r = s / C::SLOTS, c = s - r * C::SLOTS;
+      const uint32_t off = c < C::CPR ? (uint32_t)r * row_bytes + 16u * (uint32_t)c : 0x7ffffff0u;
+      dma16_buf(rs, off, (uint8_t*)lds + 1024 * w);
+    }
+  }
+}
+
+__device__ __forceinline__ u32x4 lds16(const uint16_t* p) { return *(const u32x4*)p; }
+
+// Operand A[m][k] (or B[k][n]) = X[k][m] of a row-major LDS tile X with pitch
+// P: two transposing reads give this lane X[k0 + 8(l/32) + e][m0 + l%32],
+// e = 0..7, when p = X + k0 * P + m0 + tr_offset(lane, P).
+__device__ __forceinline__ int tr_offset(int lane, int P) {
+  const int g = lane >> 4, j = lane & 15;
+  return (8 * (g >> 1) + (j >> 2)) * P + 16 * (g & 1) + 4 * (j & 3);
+}
+__device__ __forceinline__ u32x4 lds_tr(const uint16_t* p, int P) {
+  const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * P);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+template <int DT>
+__device__ __forceinline__ u32x4 pack8(const float* x) {
+  return u32x4{pack2<DT>(x[0], x[1]), pack2<DT>(x[2], x[3]), pack2<DT>(x[4], x[5]), pack2<DT>(x[6], x[7])};
+}
+
+// Store an MFMA accumulator of D^T (rows d, column = this lane's row of the
+// output) times `mul`: register 4g + i holds d = 32 dt + 8g + 4hh + i.
+template <int D, int DT>
+__device__ __forceinline__ void store_rows(uint16_t* row, const f32x16 (&acc)[D / 32], float mul, int hh) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x16& x = acc[dt];
+      *(u32x2*)(row + 32 * dt + 8 * g + 4 * hh) =
+          u32x2{pack2<DT>(x[4 * g] * mul, x[4 * g + 1] * mul), pack2<DT>(x[4 * g + 2] * mul, x[4 * g + 3] * mul)};
+    }
+}
+
+}  // namespace
+
+// delta[b, h, i] = sum_d dO[b, i, h, d] * O[b, i, h, d]: D/8 lanes per row.
+template <int D, int DT>
+__global__ void __launch_bounds__(256) bwd_delta_kernel(BwdArgs a) {
+  constexpr int LPR = D / 8, RPW = 256 / LPR;
+  const int tid = threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * RPW + tid / LPR;  // index into [B, Sq, H]
+  const int64_t rows = (int64_t)a.B * a.Sq * a.H;
+  const int c = tid % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 x = *(const u32x4*)((const uint16_t*)a.dout + row * D + 8 * c);
+    const u32x4 y = *(const u32x4*)((const uint16_t*)a.o + row * D + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(to_f32<DT>((uint16_t)(x[e] & 0xffffu)), to_f32<DT>((uint16_t)(y[e] & 0xffffu)), acc);
+      acc = fmaf(to_f32<DT>((uint16_t)(x[e] >> 16)), to_f32<DT>((uint16_t)(y[e] >> 16)), acc);
+    }
+  }
+#pragma unroll
+  for (int s = 1; s < LPR; s <<= 1) acc += __shfl_xor(acc, s);
+  if (row < rows && c == 0) {
+    const int h = (int)(row % a.H);
+    const int64_t bi = row / a.H;
+    const int i = (int)(bi % a.Sq), b = (int)(bi / a.Sq);
+    a.delta[((int64_t)b * a.H + h) * a.Sq + i] = acc;
+  }
+}
+
+template <int D, int DT, bool CAUSAL>
+__global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdArgs a) {
+  using C = BwdCfg<D>;
+  constexpr int P = C::P, BK = 128, BQ = 64;
+  __shared__ __attribute__((aligned(16))) uint16_t sq0[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sq1[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sd0[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sd1[C::TILE];
+  __shared__ __attribute__((aligned(16))) float svec[2][2 * BQ];  // [stage][LSE*log2e (64) | delta (64)]
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int nkb = (a.Sk + BK - 1) / BK;
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = t / nkb, kb = t - bh * nkb;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int Lq = a.Sq, Lk = a.Sk, diag = Lk - Lq;
+  const int64_t rs = (int64_t)a.H * D;
+  const int kw = kb * BK + 32 * wave;  // first key of this wave
+  const int key = kw + l32;            // this lane's key
+  const uint16_t* const qg = (const uint16_t*)a.q + ((int64_t)b * Lq * a.H + h) * D;
+  const uint16_t* const dog = (const uint16_t*)a.dout + ((int64_t)b * Lq * a.H + h) * D;
+  const float c2 = a.scale_log2;
+
+  // K and V rows of this lane's key as B operands (column = key, d-slice 16kk + 8hh)
+  u32x4 kf[D / 16], vf[D / 16];
+  {
+    const int64_t kr = ((int64_t)b * Lk + key) * a.H * D + (int64_t)h * D + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      kf[kk] = key < Lk ? *(const u32x4*)((const uint16_t*)a.k + kr + 16 * kk) : u32x4{0, 0, 0, 0};
+      vf[kk] = key < Lk ? *(const u32x4*)((const uint16_t*)a.v + kr + 16 * kk) : u32x4{0, 0, 0, 0};
+    }
+  }
+  f32x16 dv[D / 32], dk[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dv[dt][r] = dk[dt][r] = 0.f;
+  const f32x16 zero16 = {};
+  const int tro = tr_offset(lane, P);
+
+  // per-row vectors of a query tile: LSE * log2(e) (+inf where the row passes
+  // no gradient, so that its probabilities are exactly 0) and delta
+  const float* const lseg = a.lse + (int64_t)bh * Lq;
+  const float* const delg = a.delta + (int64_t)bh * Lq;
+  auto vec_load = [&](int qt) -> float {
+    const int i = qt * BQ + (tid & (BQ - 1));
+    if (tid < BQ) {
+      const float l = i < Lq ? lseg[i] : -INFINITY;
+      return l == -INFINITY ? INFINITY : l * kLog2e;
+    }
+    return i < Lq ? delg[i] : 0.f;
+  };
+
+  auto compute = [&](int qt, int cur) {
+    if (kw >= Lk) return;  // a wave with no key only copies and synchronises
+    const uint16_t* const Qs = cur ? sq1 : sq0;
+    const uint16_t* const Ds = cur ? sd1 : sd0;
+    const float* const Ls = svec[cur];
+#pragma unroll
+    for (int st = 0; st < BQ / 32; ++st) {
+      const int qa = qt * BQ + 32 * st;  // first query of the sub-tile
+      if (qa >= Lq) break;
+      if (CAUSAL && kw > qa + 31 + diag) continue;  // every pair of the wave is masked
+      f32x16 s = zero16, dp = zero16;
+      const uint16_t* qr = Qs + (32 * st + swz23(l32)) * P + 8 * hh;
+      const uint16_t* dr = Ds + (32 * st + swz23(l32)) * P + 8 * hh;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        s = mfma32<DT>(lds16(qr + 16 * kk), kf[kk], s);
+        dp = mfma32<DT>(lds16(dr + 16 * kk), vf[kk], dp);
+      }
+      // register r: query qa + 16(r/8) + 8hh + r%8 (runs of 8 per lane half)
+      float lv[16], dl[16];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const f32x4* l4 = (const f32x4*)(Ls + 32 * st + 16 * half + 8 * hh);
+        const f32x4* d4 = (const f32x4*)(Ls + BQ + 32 * st + 16 * half + 8 * hh);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const f32x4 x = l4[u], y = d4[u];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lv[8 * half + 4 * u + e] = x[e];
+            dl[8 * half + 4 * u + e] = y[e];
+          }
+        }
+      }
+      float p[16], ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = fast_exp2(fmaf(s[r], c2, -lv[r]));
+        if (CAUSAL) {
+          const int qi = qa + 16 * (r >> 3) + 8 * hh + (r & 7);
+          pr = key > qi + diag ? 0.f : pr;
+        }
+        p[r] = pr;
+        ds[r] = pr * (dp[r] - dl[r]);
+      }
+      const u32x4 pk[2] = {pack8<DT>(p), pack8<DT>(p + 8)};
+      const u32x4 sk[2] = {pack8<DT>(ds), pack8<DT>(ds + 8)};
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const int off = (32 * st + 16 * c) * P + 32 * dt + tro;
+          dv[dt] = mfma32<DT>(lds_tr(Ds + off, P), pk[c], dv[dt]);
+          dk[dt] = mfma32<DT>(lds_tr(Qs + off, P), sk[c], dk[dt]);
+        }
+    }
+  };
+
+  // query tiles that can see this block's keys (causal: i + diag >= first key)
+  const int qt0 = CAUSAL ? max(0, kb * BK - diag) / BQ : 0;
+  const int nqt = (Lq + BQ - 1) / BQ;
+  if (qt0 < nqt) {
+    copy_tile<D>(qg + (int64_t)qt0 * BQ * rs, rs, Lq - qt0 * BQ, sq0, wave, lane);
+    copy_tile<D>(dog + (int64_t)qt0 * BQ * rs, rs, Lq - qt0 * BQ, sd0, wave, lane);
+    if (tid < 2 * BQ) svec[0][tid] = vec_load(qt0);
+    wait_vmem();
+    __syncthreads();
+    for (int qt = qt0; qt < nqt; ++qt) {
+      const int cur = (qt - qt0) & 1;
+      float nv = 0.f;
+      if (qt + 1 < nqt) {
+        const int64_t r0 = (int64_t)(qt + 1) * BQ;
+        copy_tile<D>(qg + r0 * rs, rs, Lq - (int)r0, cur ? sq0 : sq1, wave, lane);
+        copy_tile<D>(dog + r0 * rs, rs, Lq - (int)r0, cur ? sd0 : sd1, wave, lane);
+        if (tid < 2 * BQ) nv = vec_load(qt + 1);
+      }
+      compute(qt, cur);
+      if (qt + 1 < nqt && tid < 2 * BQ) svec[cur ^ 1][tid] = nv;
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+  if (key < Lk) {
+    const int64_t off = ((int64_t)b * Lk + key) * a.H * D + (int64_t)h * D;
+    store_rows<D, DT>((uint16_t*)a.dk + off, dk, a.scale, hh);
+    store_rows<D, DT>((uint16_t*)a.dv + off, dv, 1.f, hh);
+  }
+}
+
+template <int D, int DT, bool CAUSAL>
+__global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
+  using C = BwdCfg<D>;
+  constexpr int P = C::P, BQ = 128, BC = 64;
+  __shared__ __attribute__((aligned(16))) uint16_t sk0[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sk1[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sv0[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sv1[C::TILE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int nqb = (a.Sq + BQ - 1) / BQ;
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = t / nqb;
+  int qb = t - bh * nqb;
+  if (CAUSAL) qb = nqb - 1 - qb;  // longest key ranges first
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int Lq = a.Sq, Lk = a.Sk, diag = Lk - Lq;
+  const int64_t rs = (int64_t)a.H * D;
+  const int q0 = qb * BQ, qw = q0 + 32 * wave, qi = qw + l32;
+  const bool wave_active = qw < Lq;
+  const int wave_last_key = CAUSAL ? min(qw + 31, Lq - 1) + diag : Lk - 1;
+  const uint16_t* const kg = (const uint16_t*)a.k + ((int64_t)b * Lk * a.H + h) * D;
+  const uint16_t* const vg = (const uint16_t*)a.v + ((int64_t)b * Lk * a.H + h) * D;
+  const float c2 = a.scale_log2;
+
+  // Q and dO rows of this lane's query as B operands (column = query)
+  u32x4 qf[D / 16], df[D / 16];
+  {
+    const int64_t qr = ((int64_t)b * Lq + qi) * a.H * D + (int64_t)h * D + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      qf[kk] = qi < Lq ? *(const u32x4*)((const uint16_t*)a.q + qr + 16 * kk) : u32x4{0, 0, 0, 0};
+      df[kk] = qi < Lq ? *(const u32x4*)((const uint16_t*)a.dout + qr + 16 * kk) : u32x4{0, 0, 0, 0};
+    }
+  }
+  float lse2 = INFINITY, del = 0.f;
+  if (qi < Lq) {
+    const float l = a.lse[(int64_t)bh * Lq + qi];
+    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    del = a.delta[(int64_t)bh * Lq + qi];
+  }
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[dt][r] = 0.f;
+  const f32x16 zero16 = {};
+  const int tro = tr_offset(lane, P);
+
+  auto compute = [&](int j, int cur) {
+    const int key0 = j * BC;
+    if (!wave_active || (CAUSAL && key0 > wave_last_key)) return;
+    const uint16_t* const Ks = cur ? sk1 : sk0;
+    const uint16_t* const Vs = cur ? sv1 : sv0;
+    u32x4 dsk[BC / 16];
+#pragma unroll
+    for (int tt = 0; tt < BC / 32; ++tt) {
+      f32x16 s = zero16, dp = zero16;
+      const uint16_t* kr = Ks + (32 * tt + swz23(l32)) * P + 8 * hh;
+      const uint16_t* vr = Vs + (32 * tt + swz23(l32)) * P + 8 * hh;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        s = mfma32<DT>(lds16(kr + 16 * kk), qf[kk], s);
+        dp = mfma32<DT>(lds16(vr + 16 * kk), df[kk], dp);
+      }
+      // register r: key key0 + 32tt + 16(r/8) + 8hh + r%8
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kj = key0 + 32 * tt + 16 * (r >> 3) + 8 * hh + (r & 7);
+        float pr = fast_exp2(fmaf(s[r], c2, -lse2));
+        const bool masked = kj >= Lk || (CAUSAL && kj > qi + diag);
+        pr = masked ? 0.f : pr;
+        ds[r] = pr * (dp[r] - del);
+      }
+      dsk[2 * tt] = pack8<DT>(ds);
+      dsk[2 * tt + 1] = pack8<DT>(ds + 8);
+    }
+#pragma unroll
+    for (int c = 0; c < BC / 16; ++c)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        dq[dt] = mfma32<DT>(lds_tr(Ks + 16 * c * P + 32 * dt + tro, P), dsk[c], dq[dt]);
+  };
+
+  int n_kv = (Lk + BC - 1) / BC;
+  if (CAUSAL) {
+    const int last = min(q0 + BQ, Lq) - 1 + diag;
+    n_kv = last < 0 ? 0 : min(n_kv, last / BC + 1);
+  }
+  if (n_kv > 0) {
+    copy_tile<D>(kg, rs, Lk, sk0, wave, lane);
+    copy_tile<D>(vg, rs, Lk, sv0, wave, lane);
+    wait_vmem();
+    __syncthreads();
+    for (int j = 0; j < n_kv; ++j) {
+      const int cur = j & 1;
+      if (j + 1 < n_kv) {
+        const int64_t r0 = (int64_t)(j + 1) * BC;
+        copy_tile<D>(kg + r0 * rs, rs, Lk - (int)r0, cur ? sk0 : sk1, wave, lane);
+        copy_tile<D>(vg + r0 * rs, rs, Lk - (int)r0, cur ? sv0 : sv1, wave, lane);
+      }
+      compute(j, cur);
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+  if (qi < Lq)
+    store_rows<D, DT>((uint16_t*)a.dq + ((int64_t)b * Lq + qi) * a.H * D + (int64_t)h * D, dq, a.scale, hh);
+}
+
+template <int D, int DT, bool CAUSAL>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
+  const int64_t rows = (int64_t)a.B * a.Sq * a.H;
+  const int rpw = 256 / (D / 8);
+  const int nkb = (a.Sk + 127) / 128, nqb = (a.Sq + 127) / 128;
+  // (with no query every key gradient is zero: the dK/dV kernel then writes zeros)
+  if (rows > 0)
+    hipLaunchKernelGGL((bwd_delta_kernel<D, DT>), dim3((unsigned)((rows + rpw - 1) / rpw)), dim3(256), 0, s, a);
+  if (nkb > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, CAUSAL>), dim3(a.B * a.H * nkb), dim3(256), 0, s, a);
+  if (nqb > 0) hipLaunchKernelGGL((bwd_dq_kernel<D, DT, CAUSAL>), dim3(a.B * a.H * nqb), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D, int DT>
+static hipError_t launch_bwd_c(const BwdArgs& a, bool causal, hipStream_t s) {
+  return causal ? launch_bwd_t<D, DT, true>(a, s) : launch_bwd_t<D, DT, false>(a, s);
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int D, int dtype, bool causal, hipStream_t s) {
+  if (D == 64) return dtype == kBF16 ? launch_bwd_c<64, kBF16>(a, causal, s) : launch_bwd_c<64, kFP16>(a, causal, s);
+  if (D == 128) return dtype == kBF16 ? launch_bwd_c<128, kBF16>(a, causal, s) : launch_bwd_c<128, kFP16>(a, causal, s);
+  return hipErrorNotSupported;
+}
+
+}  // namespace attn

@@ -254,6 +254,31 @@ attn_status_t attn_fwd_splitkv(int dtype,
  * bytes (0 for num_splits <= 1 or an empty problem). */
 size_t attn_fwd_splitkv_workspace_bytes(int total_q, int H, int D, int num_splits);
 
+/*
+ * attn_bwd — gradients of attn_fwd with respect to q, k and v.
+ * (The FlashAttention-3 summary page reports a backward pass beside the
+ * forward one; the "Fused attention kernel" page's "When to use which" says it
+ * follows the same pattern.  The pages do not write it out: this is the chain
+ * rule through O = softmax(scale q k^T [+ causal mask]) v.)
+ *
+ * With P recomputed from the forward's logsumexp, P = exp(scale q k^T - lse):
+ *   dv = P^T dout,  dS = P * (dout v^T - delta),  delta_i = <dout_i, o_i>,
+ *   dq = scale dS k,  dk = scale dS^T q.
+ * q, o, dout, dq: [B, Sq, H, D]; k, v, dk, dv: [B, Sk, H, D]; all contiguous
+ * of `dtype` (bf16 or fp16).  o and lse (float32 [B, H, Sq]) are the outputs of
+ * attn_fwd on the same q, k, v, scale and mask.
+ * delta: float32 [B, H, Sq] scratch owned by the caller (overwritten).
+ * D must be 64 or 128.  Masks as for attn_fwd (causal: bottom-right); rows
+ * with no allowed key pass no gradient; with Sq = 0, dk and dv are zero.
+ * The gradients are written once, with no atomics (run-to-run identical).
+ */
+attn_status_t attn_bwd(int dtype,
+                       const void* q, const void* k, const void* v,
+                       const void* o, const float* lse, const void* dout,
+                       void* dq, void* dk, void* dv, float* delta,
+                       int B, int H, int Sq, int Sk, int D,
+                       float softmax_scale, int causal, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* attn_status_string(int status);
 

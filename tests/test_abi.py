@@ -30,6 +30,7 @@ def lib():
     L.attn_fwd.argtypes = [I, P, I64P, P, I64P, P, I64P, P, I64P, P, I, I, I, I, I, F, I, P]
     L.attn_fp8_quantize.argtypes = [P, I64P, P, P, I, I, I, I, I, P, P]
     L.attn_fwd_fp8.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, I, F, I, P]
+    L.attn_bwd.argtypes = [I, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, P]
     L.attn_int8_quantize.argtypes = [P, I64P, P, P, I, I, I, I, I, P, P]
     L.attn_fwd_int8.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, I, F, I, P]
     L.attn_fwd_varlen.argtypes = [I, P, P, P, P, P, P, I, I, P, P, I, I, I, I, I, I, F, I, P]
@@ -54,7 +55,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("attn_fwd", "attn_fp8_quantize", "attn_fwd_fp8", "attn_fwd_varlen", "attn_fwd_splitkv",
               "attn_fwd_splitkv_workspace_bytes", "attn_fwd_bias", "attn_int8_quantize", "attn_fwd_int8",
-              "attn_status_string", "attn_last_error"):
+              "attn_bwd", "attn_status_string", "attn_last_error"):
         assert n in names
 
 
@@ -194,3 +195,21 @@ def test_bench_refuses_several_gpus():
                        text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_bwd_validation(lib):
+    def f(dtype=0, B=1, H=1, Sq=4, Sk=4, D=128, scale=0.1, causal=0, q=A16, dk=A16, lse=A16):
+        return lib.attn_bwd(dtype, q, A16, A16, A16, lse, A16, A16, dk, A16, A16, B, H, Sq, Sk, D, scale, causal,
+                            None)
+    assert f(D=256) == UNSUPPORTED
+    assert f(D=96) == UNSUPPORTED
+    assert f(D=0) == INVALID
+    assert f(dtype=7) == INVALID
+    assert f(scale=0.0) == INVALID
+    assert f(causal=2) == INVALID
+    assert f(Sq=-1) == INVALID
+    assert f(q=None) == INVALID
+    assert f(lse=None) == INVALID
+    assert f(dk=None) == INVALID
+    assert f(B=0) == OK
+    assert f(Sq=0, Sk=0) == OK
