@@ -136,8 +136,9 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(BwdArgs a) {
   }
 }
 
+// (two workgroups per CU: 256 VGPRs per lane at most)
 template <int D, int DT, bool CAUSAL>
-__global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
   constexpr int P = C::P, BK = 128, BQ = 64;
   __shared__ __attribute__((aligned(16))) uint16_t sq0[C::TILE];
@@ -210,35 +211,29 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdArgs a) {
         s = mfma32<DT>(lds16(qr + 16 * kk), kf[kk], s);
         dp = mfma32<DT>(lds16(dr + 16 * kk), vf[kk], dp);
       }
-      // register r: query qa + 16(r/8) + 8hh + r%8 (runs of 8 per lane half)
-      float lv[16], dl[16];
+      // register r: query qa + 16(r/8) + 8hh + r%8 (runs of 8 per lane half);
+      // the row vectors are read one run at a time
+      u32x4 pk[2], sk[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const f32x4* l4 = (const f32x4*)(Ls + 32 * st + 16 * half + 8 * hh);
-        const f32x4* d4 = (const f32x4*)(Ls + BQ + 32 * st + 16 * half + 8 * hh);
+        const float* lrow = Ls + 32 * st + 16 * half + 8 * hh;
+        const f32x4 l0 = *(const f32x4*)lrow, l1 = *(const f32x4*)(lrow + 4);
+        const f32x4 e0 = *(const f32x4*)(lrow + BQ), e1 = *(const f32x4*)(lrow + BQ + 4);
+        float p[8], ds[8];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const f32x4 x = l4[u], y = d4[u];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            lv[8 * half + 4 * u + e] = x[e];
-            dl[8 * half + 4 * u + e] = y[e];
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * half + e;
+          float pr = fast_exp2(fmaf(s[r], c2, -(e < 4 ? l0[e] : l1[e - 4])));
+          if (CAUSAL) {
+            const int qi = qa + 16 * half + 8 * hh + e;
+            pr = key > qi + diag ? 0.f : pr;
           }
+          p[e] = pr;
+          ds[e] = pr * (dp[r] - (e < 4 ? e0[e] : e1[e - 4]));
         }
+        pk[half] = pack8<DT>(p);
+        sk[half] = pack8<DT>(ds);
       }
-      float p[16], ds[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = fast_exp2(fmaf(s[r], c2, -lv[r]));
-        if (CAUSAL) {
-          const int qi = qa + 16 * (r >> 3) + 8 * hh + (r & 7);
-          pr = key > qi + diag ? 0.f : pr;
-        }
-        p[r] = pr;
-        ds[r] = pr * (dp[r] - dl[r]);
-      }
-      const u32x4 pk[2] = {pack8<DT>(p), pack8<DT>(p + 8)};
-      const u32x4 sk[2] = {pack8<DT>(ds), pack8<DT>(ds + 8)};
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -282,7 +277,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(BwdArgs a) {
 }
 
 template <int D, int DT, bool CAUSAL>
-__global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
   constexpr int P = C::P, BQ = 128, BC = 64;
   __shared__ __attribute__((aligned(16))) uint16_t sk0[C::TILE];
@@ -337,7 +332,6 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
     if (!wave_active || (CAUSAL && key0 > wave_last_key)) return;
     const uint16_t* const Ks = cur ? sk1 : sk0;
     const uint16_t* const Vs = cur ? sv1 : sv0;
-    u32x4 dsk[BC / 16];
 #pragma unroll
     for (int tt = 0; tt < BC / 32; ++tt) {
       f32x16 s = zero16, dp = zero16;
@@ -358,14 +352,14 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(BwdArgs a) {
         pr = masked ? 0.f : pr;
         ds[r] = pr * (dp[r] - del);
       }
-      dsk[2 * tt] = pack8<DT>(ds);
-      dsk[2 * tt + 1] = pack8<DT>(ds + 8);
+      // dQ^T += K^T dS^T for this sub-tile's two 16-key steps
+      const u32x4 dsk[2] = {pack8<DT>(ds), pack8<DT>(ds + 8)};
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          dq[dt] = mfma32<DT>(lds_tr(Ks + (32 * tt + 16 * c) * P + 32 * dt + tro, P), dsk[c], dq[dt]);
     }
-#pragma unroll
-    for (int c = 0; c < BC / 16; ++c)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        dq[dt] = mfma32<DT>(lds_tr(Ks + 16 * c * P + 32 * dt + tro, P), dsk[c], dq[dt]);
   };
 
   int n_kv = (Lk + BC - 1) / BC;

@@ -75,6 +75,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-fp8", action="store_true")
     p.add_argument("--no-int8", action="store_true", help="skip the int8-score leg")
+    p.add_argument("--no-bwd", action="store_true", help="skip the backward-pass leg")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--sweep", action="store_true", help="also time the 16384-token seq sweep (extra output)")
     p.add_argument("--no-decode", action="store_true", help="skip the long-cache decoding leg")
@@ -203,6 +204,9 @@ def main():
     if not args.no_int8:
         result["int8"] = bench_int8(A, W, args)
 
+    if not args.no_bwd:
+        result["bwd"] = bench_bwd(A, W, args, q, k, v, o, lse)
+
     if not args.no_decode:
         result["decode"] = bench_decode(A, W, args)
 
@@ -271,6 +275,26 @@ def bench_int8(A, W, args):
     return {"available": True, "workload": w.name, "ms": round(ms, 4), "tops": round(tflops, 2),
             "pct_of_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2), "peak": PEAK_FP8_TFLOPS,
             "quantize_ms_per_tensor": round(ms_q, 4)}
+
+
+def bench_bwd(A, W, args, q, k, v, o, lse):
+    """attn_bwd on the headline shape (the forward's o and lse as inputs),
+    dO ~ N(0,1); FLOPs = 2.5x the forward's (five Sq x Sk x D products)."""
+    import torch
+    w = W.WORKLOADS["ablation"]
+    dout = torch.randn(q.shape, generator=torch.Generator().manual_seed(w.seed + 1000)).to(torch.bfloat16).cuda()
+    A.fwd(q, k, v, w.scale, False, out=o, lse=lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((w.batch, w.heads, w.seq_q), dtype=torch.float32, device="cuda")
+    steps = max(3, args.steps // 3)
+    ms = time_launches(lambda: A.bwd(q, k, v, o, lse, dout, w.scale, False, dq=dq, dk=dk, dv=dv, delta=delta),
+                       steps, max(2, args.warmup // 3))
+    flops = 2.5 * 4.0 * w.batch * w.heads * w.seq_q * w.seq_k * w.head_dim
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(f"[bench] bwd {ms:.3f} ms  {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    return {"workload": w.name, "causal": False, "ms": round(ms, 4), "tflops": round(tflops, 2),
+            "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+            "flop_convention": "10*B*H*Sq*Sk*D (2.5x the forward)", "steps": steps}
 
 
 def bench_decode(A, W, args):
