@@ -33,13 +33,19 @@ namespace attn {
 
 namespace {
 
-template <int D>
+// LDS tile of 64 rows with PAD pad slots per row.  One pad slot (272-byte
+// rows at d128) suits row reads (ds_read_b128, 16 lanes on 16 bank groups);
+// tiles that are also read through the transposing reads take more
+template <int D, int PAD = 1>
 struct BwdCfg {
   static constexpr int CPR = D / 8;          // 16-byte chunks per row
-  static constexpr int SLOTS = CPR + 1;      // one pad slot per LDS row
+  static constexpr int SLOTS = CPR + PAD;    // pad slots per LDS row
   static constexpr int P = 8 * SLOTS;        // LDS row pitch in elements
   static constexpr int TILE = 64 * P;        // elements of a 64-row tile
 };
+// pad slots of tiles read both ways
+template <int D>
+constexpr int kTrPad = D == 128 ? 3 : 2;
 
 template <int DT>
 __device__ __forceinline__ float to_f32(uint16_t x) {
@@ -54,10 +60,10 @@ __device__ __forceinline__ float to_f32(uint16_t x) {
 // apart in memory, starting at g) into LDS with the padded pitch; rows at or
 // past `valid` arrive as zeros without being read.  Slot s of the tile (16
 // bytes) is LDS row s / SLOTS, chunk s % SLOTS; the pad chunk is not copied.
-template <int D>
+template <int D, int PAD>
 __device__ __forceinline__ void copy_tile(const uint16_t* g, int64_t row_elems, int valid, uint16_t* lds,
                                           int wave, int lane) {
-  using C = BwdCfg<D>;
+  using C = BwdCfg<D, PAD>;
   const uint32_t row_bytes = 2u * (uint32_t)row_elems;
   const uint64_t n = valid > 0 ? (uint64_t)valid * row_bytes : 0;
   const i32x4 rs = make_rsrc(g, (uint32_t)min(n, (uint64_t)0x7fff0000u));
@@ -139,7 +145,8 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(BwdArgs a) {
 // (two workgroups per CU: 256 VGPRs per lane at most)
 template <int D, int DT, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a) {
-  using C = BwdCfg<D>;
+  constexpr int PAD = kTrPad<D>;
+  using C = BwdCfg<D, PAD>;
   constexpr int P = C::P, BK = 128, BQ = 64;
   __shared__ __attribute__((aligned(16))) uint16_t sq0[C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sq1[C::TILE];
@@ -249,8 +256,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a) {
   const int qt0 = CAUSAL ? max(0, kb * BK - diag) / BQ : 0;
   const int nqt = (Lq + BQ - 1) / BQ;
   if (qt0 < nqt) {
-    copy_tile<D>(qg + (int64_t)qt0 * BQ * rs, rs, Lq - qt0 * BQ, sq0, wave, lane);
-    copy_tile<D>(dog + (int64_t)qt0 * BQ * rs, rs, Lq - qt0 * BQ, sd0, wave, lane);
+    copy_tile<D, PAD>(qg + (int64_t)qt0 * BQ * rs, rs, Lq - qt0 * BQ, sq0, wave, lane);
+    copy_tile<D, PAD>(dog + (int64_t)qt0 * BQ * rs, rs, Lq - qt0 * BQ, sd0, wave, lane);
     if (tid < 2 * BQ) svec[0][tid] = vec_load(qt0);
     wait_vmem();
     __syncthreads();
@@ -259,8 +266,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a) {
       float nv = 0.f;
       if (qt + 1 < nqt) {
         const int64_t r0 = (int64_t)(qt + 1) * BQ;
-        copy_tile<D>(qg + r0 * rs, rs, Lq - (int)r0, cur ? sq0 : sq1, wave, lane);
-        copy_tile<D>(dog + r0 * rs, rs, Lq - (int)r0, cur ? sd0 : sd1, wave, lane);
+        copy_tile<D, PAD>(qg + r0 * rs, rs, Lq - (int)r0, cur ? sq0 : sq1, wave, lane);
+        copy_tile<D, PAD>(dog + r0 * rs, rs, Lq - (int)r0, cur ? sd0 : sd1, wave, lane);
         if (tid < 2 * BQ) nv = vec_load(qt + 1);
       }
       compute(qt, cur);
@@ -278,12 +285,14 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a) {
 
 template <int D, int DT, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a) {
-  using C = BwdCfg<D>;
-  constexpr int P = C::P, BQ = 128, BC = 64;
-  __shared__ __attribute__((aligned(16))) uint16_t sk0[C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sk1[C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sv0[C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sv1[C::TILE];
+  // K tiles are read as rows and transposed, V tiles as rows only
+  using CK = BwdCfg<D, kTrPad<D>>;
+  using CV = BwdCfg<D, 1>;
+  constexpr int P = CK::P, PV = CV::P, BQ = 128, BC = 64;
+  __shared__ __attribute__((aligned(16))) uint16_t sk0[CK::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sk1[CK::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sv0[CV::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sv1[CV::TILE];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -336,7 +345,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a) {
     for (int tt = 0; tt < BC / 32; ++tt) {
       f32x16 s = zero16, dp = zero16;
       const uint16_t* kr = Ks + (32 * tt + swz23(l32)) * P + 8 * hh;
-      const uint16_t* vr = Vs + (32 * tt + swz23(l32)) * P + 8 * hh;
+      const uint16_t* vr = Vs + (32 * tt + swz23(l32)) * PV + 8 * hh;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         s = mfma32<DT>(lds16(kr + 16 * kk), qf[kk], s);
@@ -368,16 +377,16 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a) {
     n_kv = last < 0 ? 0 : min(n_kv, last / BC + 1);
   }
   if (n_kv > 0) {
-    copy_tile<D>(kg, rs, Lk, sk0, wave, lane);
-    copy_tile<D>(vg, rs, Lk, sv0, wave, lane);
+    copy_tile<D, kTrPad<D>>(kg, rs, Lk, sk0, wave, lane);
+    copy_tile<D, 1>(vg, rs, Lk, sv0, wave, lane);
     wait_vmem();
     __syncthreads();
     for (int j = 0; j < n_kv; ++j) {
       const int cur = j & 1;
       if (j + 1 < n_kv) {
         const int64_t r0 = (int64_t)(j + 1) * BC;
-        copy_tile<D>(kg + r0 * rs, rs, Lk - (int)r0, cur ? sk0 : sk1, wave, lane);
-        copy_tile<D>(vg + r0 * rs, rs, Lk - (int)r0, cur ? sv0 : sv1, wave, lane);
+        copy_tile<D, kTrPad<D>>(kg + r0 * rs, rs, Lk - (int)r0, cur ? sk0 : sk1, wave, lane);
+        copy_tile<D, 1>(vg + r0 * rs, rs, Lk - (int)r0, cur ? sv0 : sv1, wave, lane);
       }
       compute(j, cur);
       wait_vmem();
