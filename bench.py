@@ -135,9 +135,19 @@ def cpu_baseline(w, q, k, v, target_s):
         if time.perf_counter() - t0 >= target_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": n * flops_head / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n} of {len(pairs)} (batch, head) pairs of {w.name}, all rows, float64 numpy "
-                      f"three-pass, {dt:.1f} s"}
+    out = {"value": n * flops_head / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"{n} of {len(pairs)} (batch, head) pairs of {w.name}, all rows, float64 numpy "
+                     f"three-pass, {dt:.1f} s"}
+    # one (batch, head) on one core, beside the threaded figure
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"):
+            t1 = time.perf_counter()
+            OA.naive_head(q[0, :, 0], k[0, :, 0], v[0, :, 0], w.scale, w.causal)
+            out["single_core_s_per_head"] = round(time.perf_counter() - t1, 3)
+    except Exception as e:  # pragma: no cover
+        out["single_core_s_per_head"] = f"unavailable: {e}"
+    return out
 
 
 def main():
