@@ -690,52 +690,28 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
           // 24 of the 32 exponentials per lane); region B issues the NB P V
           // MFMAs of tile j, in 16-key chunks, and the last 8 exponentials
           // after its first MFMAs (they feed the last chunk).
-          // The exponentials of a pipelined step are taken against the running
-          // max as it stands, with no row max first: a lane's partial sum above
-          // kStepCap (or not finite, e.g. on a row's first tile, where the
-          // running max is -inf) means some probability outgrew the cap, and
-          // only then is the tile's row max formed, the running max moved and
-          // the exponentials taken again.  Probabilities thus stay below
-          // 2^20 between moves; the result is the same rescaling identity.
           auto step_math = [&](auto cur, auto nxt, f32x16 (&sc)[BC / 32], f32x16 (&sn)[BC / 32]) {
             constexpr int NA = (D / 16) * (BC / 32), NB = (D / 32) * (BC / 16);
             constexpr int KPRE = 3, VPRE = 2;
-            constexpr int NXA = 24;           // exponentials in region A (chunks 0..2)
-            constexpr float kStepCap = 1048576.f;  // 2^20
             const uint16_t* ks = kbuf(nxt) + l32 * KP + 8 * hh;
             const uint16_t* vs = vbuf(cur) + vtr_off;
             float p[BC / 2];
             u32x4 pk[BC / 16];
-            float psum_a = 0.f, psum_b = 0.f, m_safe = m_run, alpha = 1.f;
+            float psum = 0.f, mx = 0.f, m_safe = 0.f, alpha = 1.f;
             bool moved = false;
             // exponentials [lo, hi) in chunk-major order (value 8c + e is
             // register 8(c%2) + e of score tile c/2); a chunk is packed as soon
             // as its 8 values exist
-            auto exps = [&](int lo, int hi, float& acc) {
+            auto exps = [&](int lo, int hi) {
 #pragma unroll
               for (int x = lo; x < hi; ++x) {
                 const int c = x >> 3, e = x & 7;
                 p[x] = fast_exp2(fmaf(sc[c >> 1][8 * (c & 1) + e], c2, -m_safe));
-                acc += p[x];
+                psum += p[x];
                 if (e == 7)
                   pk[c] = u32x4{pack2<DT>(p[x - 7], p[x - 6]), pack2<DT>(p[x - 5], p[x - 4]),
                                 pack2<DT>(p[x - 3], p[x - 2]), pack2<DT>(p[x - 1], p[x])};
               }
-            };
-            // (rare) move the running max to this tile's row max; l_run follows
-            // at once, the accumulators when the caller scales them by alpha
-            auto move_max = [&]() {
-              float mx = sc[0][0];
-#pragma unroll
-              for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
-#pragma unroll
-              for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
-              const float m_new = fmaxf(m_run, halfwave_max(mx) * c2);
-              m_safe = m_new == -INFINITY ? 0.f : m_new;
-              alpha = fast_exp2(m_run - m_safe);
-              l_run *= alpha;
-              m_run = m_new;
-              moved = true;
             };
             __builtin_amdgcn_sched_barrier(0);
             u32x4 kop[NA];
@@ -747,13 +723,24 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
               sn[tt] = mfma32<DT>(kop[i], qf[kk], kk == 0 ? zero16 : sn[tt]);
               if (i + KPRE < NA)
                 kop[i + KPRE] = *(const u32x4*)(ks + ((i + KPRE) & 1) * 32 * KP + 16 * ((i + KPRE) >> 1));
-              exps(i * NXA / NA, (i + 1) * NXA / NA, psum_a);
+              if (i == 0) {
+                mx = sc[0][0];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
+              } else if (i == 1) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
+              } else if (i == 2) {
+                const float mxs = halfwave_max(mx) * c2;
+                moved = __builtin_amdgcn_ballot_w64(mxs > m_run + kLazyRescale) != 0;
+                const float m_new = moved ? fmaxf(m_run, mxs) : m_run;
+                m_safe = m_new == -INFINITY ? 0.f : m_new;
+                alpha = fast_exp2(m_run - m_safe);
+                m_run = m_new;
+              } else {
+                exps((i - 3) * 24 / (NA - 3), (i - 2) * 24 / (NA - 3));
+              }
               __builtin_amdgcn_sched_barrier(0);
-            }
-            if (__builtin_amdgcn_ballot_w64(!(psum_a <= kStepCap)) != 0) {
-              move_max();
-              psum_a = 0.f;
-              exps(0, NXA, psum_a);
             }
             // keep P here: otherwise it is sunk past the rescale branch below
 #pragma unroll
@@ -770,29 +757,16 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
               const int c = i / (D / 32), dt = i % (D / 32);
-              if (i == 3 * (D / 32)) {
-                // before the last chunk's products: its exponentials, taken
-                // during the first chunks' products, must be under the cap too;
-                // otherwise chunks 0..2, already in O, move with it
-                if (__builtin_amdgcn_ballot_w64(!(psum_b <= kStepCap)) != 0) {
-                  move_max();
-                  scale_acc(alpha);
-                  psum_a *= alpha;
-                  psum_b = 0.f;
-                  exps(NXA, BC / 2, psum_b);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-              }
               oacc[dt] = mfma32<DT>(u32x4{vop[i][0][0], vop[i][0][1], vop[i][1][0], vop[i][1][1]}, pk[c], oacc[dt]);
               if (i + VPRE < NB) {
                 const uint16_t* vp = vs + 16 * ((i + VPRE) / (D / 32)) * VP + 32 * ((i + VPRE) % (D / 32));
                 vop[i + VPRE][0] = lds_read_tr16(vp);
                 vop[i + VPRE][1] = lds_read_tr16(vp + 4 * VP);
               }
-              if (i < NB / 2) exps(NXA + i * 8 / (NB / 2), NXA + (i + 1) * 8 / (NB / 2), psum_b);
+              if (i < NB / 2) exps(24 + i * 8 / (NB / 2), 24 + (i + 1) * 8 / (NB / 2));
+              if (i == NB / 2 - 1) l_run = fmaf(l_run, alpha, psum);
               __builtin_amdgcn_sched_barrier(0);
             }
-            l_run += psum_a + psum_b;
           };
           auto step = [&](int j, auto cur, auto nxt, f32x16 (&sc)[BC / 32], f32x16 (&sn)[BC / 32]) {
             if (j + 2 <= jm && j + 2 < j1) dma_k((j + 2) * BC, cur, (j + 2) * BC);
