@@ -371,13 +371,13 @@ def fwd_splitkv(q, cu_seqlens_q, k, v, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
     return out, lse
 
 
-def bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None, dk=None, dv=None, delta=None,
+def bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None, dk=None, dv=None, workspace=None,
         stream=None):
     """Gradients of ``fwd``: q, o, dout [B, Sq, H, D], k, v [B, Sk, H, D] (bf16
     or fp16, contiguous), lse fp32 [B, H, Sq] from the forward.  Returns
     (dq, dk, dv)."""
     import torch
-    _require_cuda(q, k, v, o, lse, dout, dq, dk, dv, delta)
+    _require_cuda(q, k, v, o, lse, dout, dq, dk, dv, workspace)
     B, Sq, H, D = q.shape
     Sk = k.shape[1]
     for t in (q, k, v, o, dout):
@@ -391,9 +391,11 @@ def bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None, dk=Non
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    if delta is None:
-        delta = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty((2, B, H, Sq), dtype=torch.float32, device=q.device)
+    elif workspace.dtype != torch.float32 or workspace.numel() < 2 * B * H * Sq or not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous float32 with at least 2 * B * H * Sq elements")
     _check(_lib.attn_bwd(_dtype_code(q.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
-                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), B, H, Sq, Sk, D, scale, int(bool(causal)),
+                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), B, H, Sq, Sk, D, scale, int(bool(causal)),
                          _stream(stream)))
     return dq, dk, dv

@@ -437,7 +437,7 @@ attn_status_t attn_fwd_int8(const int8_t* q8, const float* q_scale, const int8_t
 }
 
 attn_status_t attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o, const float* lse,
-                       const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int Sq, int Sk,
+                       const void* dout, void* dq, void* dk, void* dv, float* workspace, int B, int H, int Sq, int Sk,
                        int D, float softmax_scale, int causal, void* stream) {
   attn_status_t st;
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return fail(ATTN_ERR_INVALID, "dtype %d is not bf16 or fp16", dtype);
@@ -448,19 +448,21 @@ attn_status_t attn_bwd(int dtype, const void* q, const void* k, const void* v, c
   if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID, "causal must be 0 or 1 (got %d)", causal);
   if (B == 0 || H == 0 || (Sq == 0 && Sk == 0)) return ok();
   if (Sq > 0 && (q == nullptr || o == nullptr || lse == nullptr || dout == nullptr || dq == nullptr ||
-                 delta == nullptr))
-    return fail(ATTN_ERR_INVALID, "q, o, lse, dout, dq or delta is NULL");
+                 workspace == nullptr))
+    return fail(ATTN_ERR_INVALID, "q, o, lse, dout, dq or workspace is NULL");
   if (Sk > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
     return fail(ATTN_ERR_INVALID, "k, v, dk or dv is NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
-      !aligned16(dk) || !aligned16(dv) || !aligned16(lse) || !aligned16(delta))
+      !aligned16(dk) || !aligned16(dv) || !aligned16(lse) || !aligned16(workspace))
     return fail(ATTN_ERR_INVALID, "every tensor must be 16-byte aligned");
   if ((int64_t)H * D > kMaxSeqStride) return fail(ATTN_ERR_INVALID, "H * D too large");
   if ((int64_t)B * H * ((std::max(Sq, Sk) + kBR - 1) / kBR) > INT32_MAX)
     return fail(ATTN_ERR_INVALID, "problem too large for one launch");
   attn::BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.delta = delta;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.delta = workspace;
+  a.lse2 = workspace + (size_t)B * H * Sq;
   a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk;
   a.scale = softmax_scale;
   a.scale_log2 = softmax_scale * attn::kLog2e;

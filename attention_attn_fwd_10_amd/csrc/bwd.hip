@@ -12,7 +12,9 @@
 //
 // Three kernels, none with atomics (every output element is summed by one
 // wave in a fixed order, so results are run-to-run identical):
-//  * bwd_delta_kernel: delta = rowsum(dO * O) in fp32, [B, H, Sq];
+//  * bwd_delta_kernel: delta = rowsum(dO * O) in fp32, [B, H, Sq], and the
+//    logsumexp in exp2 units, LSE * log2(e) (+inf for rows with no key, whose
+//    probabilities are then exactly 0), beside it;
 //  * bwd_dkdv_kernel: a workgroup owns 128 keys of one (b, h) (32 per wave,
 //    their K and V rows in registers) and walks the query tiles of 64 rows,
 //    Q and dO tiles copied asynchronously into a two-stage LDS ring.  Per
@@ -26,6 +28,8 @@
 //    with K^T from the transposing read.
 // Masks follow the forward (causal bottom-right, keys past Lk excluded); rows
 // with no allowed key (LSE = -inf) and rows past Lq pass no gradient.
+#include <type_traits>
+
 #include "bwd.hpp"
 #include "common.hpp"
 
@@ -138,7 +142,10 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(BwdArgs a) {
     const int h = (int)(row % a.H);
     const int64_t bi = row / a.H;
     const int i = (int)(bi % a.Sq), b = (int)(bi / a.Sq);
-    a.delta[((int64_t)b * a.H + h) * a.Sq + i] = acc;
+    const int64_t at = ((int64_t)b * a.H + h) * a.Sq + i;
+    a.delta[at] = acc;
+    const float l = a.lse[at];
+    a.lse2[at] = l == -INFINITY ? INFINITY : l * kLog2e;
   }
 }
 
@@ -152,7 +159,9 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sq1[C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sd0[C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sd1[C::TILE];
-  __shared__ __attribute__((aligned(16))) float svec[2][2 * BQ];  // [stage][LSE*log2e (64) | delta (64)]
+  // per-row vectors of each stage: LSE * log2(e) (64 floats), then delta (64)
+  __shared__ __attribute__((aligned(16))) float sv0[2 * BQ];
+  __shared__ __attribute__((aligned(16))) float sv1[2 * BQ];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -187,24 +196,27 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a) {
   const f32x16 zero16 = {};
   const int tro = tr_offset(lane, P);
 
-  // per-row vectors of a query tile: LSE * log2(e) (+inf where the row passes
-  // no gradient, so that its probabilities are exactly 0) and delta
-  const float* const lseg = a.lse + (int64_t)bh * Lq;
-  const float* const delg = a.delta + (int64_t)bh * Lq;
-  auto vec_load = [&](int qt) -> float {
-    const int i = qt * BQ + (tid & (BQ - 1));
-    if (tid < BQ) {
-      const float l = i < Lq ? lseg[i] : -INFINITY;
-      return l == -INFINITY ? INFINITY : l * kLog2e;
+  // per-row vectors of a query tile, copied like the tiles (waves 0 and 1, one
+  // dword per lane; rows past Lq read as 0, harmless: their Q and dO rows are 0)
+  const float* const l2g = a.lse2 + (int64_t)bh * Lq;
+  const float* const dlg = a.delta + (int64_t)bh * Lq;
+  auto copy_vec = [&](int qt, float* dst) {
+    if (wave < 2) {
+      const float* g = (wave == 0 ? l2g : dlg) + (int64_t)qt * BQ;
+      const int valid = Lq - qt * BQ;
+      const i32x4 rs4 = make_rsrc(g, (uint32_t)(4 * min(valid, BQ)));
+      raw_buffer_load_lds(rs4, (__attribute__((address_space(3))) void*)(dst + BQ * wave), 4, 4 * lane, 0, 0, 0);
     }
-    return i < Lq ? delg[i] : 0.f;
   };
 
-  auto compute = [&](int qt, int cur) {
+  // (stages are compile-time constants, so the compiler sees that a stage's
+  // LDS reads never alias the copies into the other one and does not wait for them)
+  auto compute = [&](int qt, auto stage) {
     if (kw >= Lk) return;  // a wave with no key only copies and synchronises
-    const uint16_t* const Qs = cur ? sq1 : sq0;
-    const uint16_t* const Ds = cur ? sd1 : sd0;
-    const float* const Ls = svec[cur];
+    constexpr bool S1 = decltype(stage)::value;
+    const uint16_t* const Qs = S1 ? sq1 : sq0;
+    const uint16_t* const Ds = S1 ? sd1 : sd0;
+    const float* const Ls = S1 ? sv1 : sv0;
 #pragma unroll
     for (int st = 0; st < BQ / 32; ++st) {
       const int qa = qt * BQ + 32 * st;  // first query of the sub-tile
@@ -255,25 +267,31 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a) {
   // query tiles that can see this block's keys (causal: i + diag >= first key)
   const int qt0 = CAUSAL ? max(0, kb * BK - diag) / BQ : 0;
   const int nqt = (Lq + BQ - 1) / BQ;
+  auto load = [&](int qt, auto stage) {
+    constexpr bool S1 = decltype(stage)::value;
+    const int64_t r0 = (int64_t)qt * BQ;
+    copy_tile<D, PAD>(qg + r0 * rs, rs, Lq - (int)r0, S1 ? sq1 : sq0, wave, lane);
+    copy_tile<D, PAD>(dog + r0 * rs, rs, Lq - (int)r0, S1 ? sd1 : sd0, wave, lane);
+    copy_vec(qt, S1 ? sv1 : sv0);
+  };
+  constexpr std::integral_constant<bool, false> T0{};
+  constexpr std::integral_constant<bool, true> T1{};
   if (qt0 < nqt) {
-    copy_tile<D, PAD>(qg + (int64_t)qt0 * BQ * rs, rs, Lq - qt0 * BQ, sq0, wave, lane);
-    copy_tile<D, PAD>(dog + (int64_t)qt0 * BQ * rs, rs, Lq - qt0 * BQ, sd0, wave, lane);
-    if (tid < 2 * BQ) svec[0][tid] = vec_load(qt0);
+    load(qt0, T0);
     wait_vmem();
     __syncthreads();
-    for (int qt = qt0; qt < nqt; ++qt) {
-      const int cur = (qt - qt0) & 1;
-      float nv = 0.f;
-      if (qt + 1 < nqt) {
-        const int64_t r0 = (int64_t)(qt + 1) * BQ;
-        copy_tile<D, PAD>(qg + r0 * rs, rs, Lq - (int)r0, cur ? sq0 : sq1, wave, lane);
-        copy_tile<D, PAD>(dog + r0 * rs, rs, Lq - (int)r0, cur ? sd0 : sd1, wave, lane);
-        if (tid < 2 * BQ) nv = vec_load(qt + 1);
-      }
-      compute(qt, cur);
-      if (qt + 1 < nqt && tid < 2 * BQ) svec[cur ^ 1][tid] = nv;
+    // two tiles per iteration, so that every stage number is a constant
+    for (int qt = qt0; qt < nqt; qt += 2) {
+      if (qt + 1 < nqt) load(qt + 1, T1);
+      compute(qt, T0);
       wait_vmem();
       __syncthreads();
+      if (qt + 1 < nqt) {
+        if (qt + 2 < nqt) load(qt + 2, T0);
+        compute(qt + 1, T1);
+        wait_vmem();
+        __syncthreads();
+      }
     }
   }
   if (key < Lk) {
@@ -324,8 +342,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a) {
   }
   float lse2 = INFINITY, del = 0.f;
   if (qi < Lq) {
-    const float l = a.lse[(int64_t)bh * Lq + qi];
-    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    lse2 = a.lse2[(int64_t)bh * Lq + qi];
     del = a.delta[(int64_t)bh * Lq + qi];
   }
   f32x16 dq[D / 32];
@@ -336,11 +353,12 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a) {
   const f32x16 zero16 = {};
   const int tro = tr_offset(lane, P);
 
-  auto compute = [&](int j, int cur) {
+  auto compute = [&](int j, auto stage) {
     const int key0 = j * BC;
     if (!wave_active || (CAUSAL && key0 > wave_last_key)) return;
-    const uint16_t* const Ks = cur ? sk1 : sk0;
-    const uint16_t* const Vs = cur ? sv1 : sv0;
+    constexpr bool S1 = decltype(stage)::value;
+    const uint16_t* const Ks = S1 ? sk1 : sk0;
+    const uint16_t* const Vs = S1 ? sv1 : sv0;
 #pragma unroll
     for (int tt = 0; tt < BC / 32; ++tt) {
       f32x16 s = zero16, dp = zero16;
@@ -376,21 +394,29 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a) {
     const int last = min(q0 + BQ, Lq) - 1 + diag;
     n_kv = last < 0 ? 0 : min(n_kv, last / BC + 1);
   }
+  auto load = [&](int j, auto stage) {
+    constexpr bool S1 = decltype(stage)::value;
+    const int64_t r0 = (int64_t)j * BC;
+    copy_tile<D, kTrPad<D>>(kg + r0 * rs, rs, Lk - (int)r0, S1 ? sk1 : sk0, wave, lane);
+    copy_tile<D, 1>(vg + r0 * rs, rs, Lk - (int)r0, S1 ? sv1 : sv0, wave, lane);
+  };
+  constexpr std::integral_constant<bool, false> T0{};
+  constexpr std::integral_constant<bool, true> T1{};
   if (n_kv > 0) {
-    copy_tile<D, kTrPad<D>>(kg, rs, Lk, sk0, wave, lane);
-    copy_tile<D, 1>(vg, rs, Lk, sv0, wave, lane);
+    load(0, T0);
     wait_vmem();
     __syncthreads();
-    for (int j = 0; j < n_kv; ++j) {
-      const int cur = j & 1;
-      if (j + 1 < n_kv) {
-        const int64_t r0 = (int64_t)(j + 1) * BC;
-        copy_tile<D, kTrPad<D>>(kg + r0 * rs, rs, Lk - (int)r0, cur ? sk0 : sk1, wave, lane);
-        copy_tile<D, 1>(vg + r0 * rs, rs, Lk - (int)r0, cur ? sv0 : sv1, wave, lane);
-      }
-      compute(j, cur);
+    for (int j = 0; j < n_kv; j += 2) {
+      if (j + 1 < n_kv) load(j + 1, T1);
+      compute(j, T0);
       wait_vmem();
       __syncthreads();
+      if (j + 1 < n_kv) {
+        if (j + 2 < n_kv) load(j + 2, T0);
+        compute(j + 1, T1);
+        wait_vmem();
+        __syncthreads();
+      }
     }
   }
   if (qi < Lq)

@@ -17,6 +17,7 @@ struct BwdArgs {
   void* dk;           // [B, Sk, H, D]
   void* dv;           // [B, Sk, H, D]
   float* delta;       // [B, H, Sq] scratch: rowsum(dO * O)
+  float* lse2;        // [B, H, Sq] scratch: lse * log2(e), +inf for rows with no key
   int B, H, Sq, Sk;
   float scale;        // softmax scale
   float scale_log2;   // scale * log2(e)

@@ -295,9 +295,9 @@ def bench_bwd(A, W, args, q, k, v, o, lse):
     dout = torch.randn(q.shape, generator=torch.Generator().manual_seed(w.seed + 1000)).to(torch.bfloat16).cuda()
     A.fwd(q, k, v, w.scale, False, out=o, lse=lse)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    delta = torch.empty((w.batch, w.heads, w.seq_q), dtype=torch.float32, device="cuda")
+    ws = torch.empty((2, w.batch, w.heads, w.seq_q), dtype=torch.float32, device="cuda")
     steps = max(3, args.steps // 3)
-    ms = time_launches(lambda: A.bwd(q, k, v, o, lse, dout, w.scale, False, dq=dq, dk=dk, dv=dv, delta=delta),
+    ms = time_launches(lambda: A.bwd(q, k, v, o, lse, dout, w.scale, False, dq=dq, dk=dk, dv=dv, workspace=ws),
                        steps, max(2, args.warmup // 3))
     flops = 2.5 * 4.0 * w.batch * w.heads * w.seq_q * w.seq_k * w.head_dim
     tflops = flops / (ms * 1e-3) / 1e12

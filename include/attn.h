@@ -267,7 +267,8 @@ size_t attn_fwd_splitkv_workspace_bytes(int total_q, int H, int D, int num_split
  * q, o, dout, dq: [B, Sq, H, D]; k, v, dk, dv: [B, Sk, H, D]; all contiguous
  * of `dtype` (bf16 or fp16).  o and lse (float32 [B, H, Sq]) are the outputs of
  * attn_fwd on the same q, k, v, scale and mask.
- * delta: float32 [B, H, Sq] scratch owned by the caller (overwritten).
+ * workspace: float32 [2, B, H, Sq] scratch owned by the caller, 16-byte
+ *   aligned, overwritten (delta, then lse * log2(e)).
  * D must be 64 or 128.  Masks as for attn_fwd (causal: bottom-right); rows
  * with no allowed key pass no gradient; with Sq = 0, dk and dv are zero.
  * The gradients are written once, with no atomics (run-to-run identical).
@@ -275,7 +276,7 @@ size_t attn_fwd_splitkv_workspace_bytes(int total_q, int H, int D, int num_split
 attn_status_t attn_bwd(int dtype,
                        const void* q, const void* k, const void* v,
                        const void* o, const float* lse, const void* dout,
-                       void* dq, void* dk, void* dv, float* delta,
+                       void* dq, void* dk, void* dv, float* workspace,
                        int B, int H, int Sq, int Sk, int D,
                        float softmax_scale, int causal, void* stream);
 
