@@ -301,10 +301,18 @@ def bench_bwd(A, W, args, q, k, v, o, lse):
                        steps, max(2, args.warmup // 3))
     flops = 2.5 * 4.0 * w.batch * w.heads * w.seq_q * w.seq_k * w.head_dim
     tflops = flops / (ms * 1e-3) / 1e12
-    print(f"[bench] bwd {ms:.3f} ms  {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    # the causal backward beside it (its own forward outputs; FLOPs halved)
+    oc, lc = torch.empty_like(o), torch.empty_like(lse)
+    A.fwd(q, k, v, w.scale, True, out=oc, lse=lc)
+    ms_c = time_launches(lambda: A.bwd(q, k, v, oc, lc, dout, w.scale, True, dq=dq, dk=dk, dv=dv, workspace=ws),
+                         steps, max(2, args.warmup // 3))
+    tflops_c = flops / 2 / (ms_c * 1e-3) / 1e12
+    print(f"[bench] bwd {ms:.3f} ms  {tflops:.1f} TFLOP/s; causal {ms_c:.3f} ms  {tflops_c:.1f} TFLOP/s",
+          file=sys.stderr, flush=True)
     return {"workload": w.name, "causal": False, "ms": round(ms, 4), "tflops": round(tflops, 2),
             "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-            "flop_convention": "10*B*H*Sq*Sk*D (2.5x the forward)", "steps": steps}
+            "ms_causal": round(ms_c, 4), "tflops_causal": round(tflops_c, 2),
+            "flop_convention": "10*B*H*Sq*Sk*D (2.5x the forward), halved for causal", "steps": steps}
 
 
 def bench_decode(A, W, args):
