@@ -328,7 +328,7 @@ def splitkv_num_splits(n_work, max_seqlen_k, target=2048, min_tiles=4, max_split
     want = max(1, -(-int(target) // max(1, int(n_work))))
     per = max(1, -(-tiles // want))
     per = max(int(min_tiles), 1 << (per.bit_length() - 1))
-    return int(max(1, min(-(-tiles // per), max_splits)))
+    return int(max(1, min(-(-tiles // per), tiles // int(min_tiles), max_splits)))
 
 
 def fwd_splitkv(q, cu_seqlens_q, k, v, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale=None,

@@ -213,3 +213,21 @@ def test_bwd_validation(lib):
     assert f(dk=None) == INVALID
     assert f(B=0) == OK
     assert f(Sq=0, Sk=0) == OK
+
+
+def test_splitkv_num_splits_bounds():
+    """The split-count rule: between 1 and 16 splits, at least 4 tiles of 64 keys
+    in every split the kernel forms (ceil(tiles / splits) each), and no fewer
+    splits for fewer work items."""
+    import attention_attn_fwd_10_amd as A
+    for n_work in (1, 32, 160, 544, 5000):
+        for lk in (1, 64, 255, 300, 4096, 32768, 131072, 1 << 20):
+            s = A.splitkv_num_splits(n_work, lk)
+            tiles = (lk + 63) // 64
+            assert 1 <= s <= 16
+            per = -(-tiles // s)
+            if s > 1:
+                assert per >= 4 and tiles - (s - 1) * per >= 1, (n_work, lk, s)
+    assert A.splitkv_num_splits(160, 32768) == 16
+    assert A.splitkv_num_splits(544, 8192) == 4
+    assert A.splitkv_num_splits(32, 131072) >= A.splitkv_num_splits(5000, 131072)
