@@ -683,6 +683,10 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
           // waves whose rows all lie past the sequence end only copy and
           // synchronise (with one query row, as in decoding, three of four)
           if (wave_active) qk_tile(S0, sa);
+          // the first step copies K(j0 + 2) into stage 0: every wave must have
+          // read K(j0) from it first (waves with no rows skip the read and
+          // would otherwise overwrite the stage while it is still being read)
+          __syncthreads();
           // One step with the next tile's scores overlapped (needs j + 1 < jm).
           // The order of the work is fixed by scheduling fences: region A
           // issues the NA score MFMAs of tile j+1, and after each one a share
