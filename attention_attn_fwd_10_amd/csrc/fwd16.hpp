@@ -320,6 +320,24 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
       }
     }
   };
+  // the same copies for callers that know the tile is contiguous (no per-row
+  // table path compiled in)
+  auto dma_k_c = [&](int key0, auto buf, int64_t row0) {
+    uint16_t* kb = kbuf(buf);
+    const uint64_t kn = 2ull * (uint64_t)(Lk - key0) * (uint64_t)a.k_ss;
+    const i32x4 kr = make_rsrc(kg + row0 * a.k_ss, (uint32_t)min(kn, (uint64_t)0x7fff0000u));
+#pragma unroll
+    for (int ii = 0; ii < C::KI_W; ++ii)
+      if (wave + NW * ii < C::KSLOTS) dma16_buf(kr, ii < KI_FULL ? k_boff[ii] : k_off(ii), kb + (wave + NW * ii) * 512);
+  };
+  auto dma_v_c = [&](int key0, auto buf, int64_t row0) {
+    uint16_t* vb = vbuf(buf);
+    const uint64_t vn = 2ull * (uint64_t)(Lk - key0) * (uint64_t)a.v_ss;
+    const i32x4 vr = make_rsrc(vg + row0 * a.v_ss, (uint32_t)min(vn, (uint64_t)0x7fff0000u));
+#pragma unroll
+    for (int ii = 0; ii < C::VI_W; ++ii)
+      if (wave + NW * ii < C::VSLOTS) dma16_buf(vr, ii < VI_FULL ? v_boff[ii] : v_off(ii), vb + (wave + NW * ii) * 512);
+  };
   auto dma_tile = [&](int key0, int buf) {
     const int64_t row0 = contiguous ? tile_row0(key0) : 0;
     dma_k(key0, buf, row0);
@@ -660,9 +678,10 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   if (j1 > j0) {
     if constexpr (D != 256) {
       int jg = j0;  // first tile of the generic loop below
-      // (not with a score bias, and not for paged caches, where the registers
-      // of the pipeline and of the page-table copies do not fit together)
-      if constexpr (!BIAS && MODE != kPaged) {
+      // (not with a score bias, and for paged caches only with pages of >= 64
+      // tokens, whose tiles are copied like contiguous ones: the registers of
+      // the pipeline and of the per-row page-table copies do not fit together)
+      if (!BIAS && contiguous) {
         // Tiles [j0, jm) need no mask for any row of the block.  They run
         // software-pipelined: while the softmax of tile j is on the vector
         // units, the same wave issues the score MFMAs of tile j+1; then P V of
@@ -674,10 +693,11 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
           constexpr std::integral_constant<int, 0> S0{};
           constexpr std::integral_constant<int, 1> S1{};
           f32x16 sa[BC / 32], sb[BC / 32];
-          // (no page table on this path: a tile's first row is its first key)
-          dma_k(j0 * BC, S0, j0 * BC);
-          dma_v(j0 * BC, S0, j0 * BC);
-          if (j0 + 1 < j1) dma_k((j0 + 1) * BC, S1, (j0 + 1) * BC);  // (j0 + 1 <= jm)
+          // (a tile's first row: its first key, or for a paged cache its
+          // page's base plus the slot, one table read per copied tile)
+          dma_k_c(j0 * BC, S0, tile_row0(j0 * BC));
+          dma_v_c(j0 * BC, S0, tile_row0(j0 * BC));
+          if (j0 + 1 < j1) dma_k_c((j0 + 1) * BC, S1, tile_row0((j0 + 1) * BC));  // (j0 + 1 <= jm)
           wait_vmem();
           __syncthreads();
           // waves whose rows all lie past the sequence end only copy and
@@ -773,15 +793,15 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
             }
           };
           auto step = [&](int j, auto cur, auto nxt, f32x16 (&sc)[BC / 32], f32x16 (&sn)[BC / 32]) {
-            if (j + 2 <= jm && j + 2 < j1) dma_k((j + 2) * BC, cur, (j + 2) * BC);
-            dma_v((j + 1) * BC, nxt, (j + 1) * BC);
+            if (j + 2 <= jm && j + 2 < j1) dma_k_c((j + 2) * BC, cur, tile_row0((j + 2) * BC));
+            dma_v_c((j + 1) * BC, nxt, tile_row0((j + 1) * BC));
             if (wave_active) step_math(cur, nxt, sc, sn);
             wait_vmem();
             __syncthreads();
           };
           // the last pipelined tile: softmax and P V only
           auto last = [&](int j, auto cur, auto nxt, f32x16 (&sc)[BC / 32]) {
-            if (j + 1 < j1) dma_v((j + 1) * BC, nxt, (j + 1) * BC);
+            if (j + 1 < j1) dma_v_c((j + 1) * BC, nxt, tile_row0((j + 1) * BC));
             if (wave_active) {
               u32x4 pk[BC / 16];
               float alpha;
