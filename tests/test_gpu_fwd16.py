@@ -193,3 +193,35 @@ def test_seq_sweep_sampled(lib, d, h, s, causal):
     lse = lse[bsel][:, :, rows].cpu().numpy().astype(np.float64)
     o_ref, lse_ref = _rows_ref(q[bsel], k[bsel], v[bsel], 1 / math.sqrt(d), causal, rows)
     assert_close16(o, o_ref, lse, lse_ref, f"sweep s{s} d{d} causal={causal}")
+
+
+def test_pingpong_schedule_in_child_process(lib):
+    """The opt-in ping-pong schedule (ATTN_FWD16_SCHEDULE=pingpong, read once per
+    process) against the oracle, in a child process: d64 and d128, causal and
+    not, several key tiles and a ragged tail."""
+    import subprocess
+    import sys
+    root = __import__("os").path.dirname(__import__("os").path.dirname(__import__("os").path.abspath(__file__)))
+    code = r'''
+import math, sys
+import numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+import attention_attn_fwd_10_amd as A, workloads as W
+from oracle import attention as OA
+from tests.parity import assert_close16
+for d in (64, 128):
+    for causal in (False, True):
+        q, k, v = W.qkv_normal(900 + d, (2, 300, 2, d), (2, 333, 2, d))
+        dev = [torch.from_numpy(x).to(torch.bfloat16).cuda() for x in (q, k, v)]
+        o, lse = A.fwd(*dev, 1 / math.sqrt(d), causal)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = OA.attention_bshd(q, k, v, 1 / math.sqrt(d), causal)
+        oh = o.float().cpu().numpy().astype(np.float64)
+        lh = lse.cpu().numpy().astype(np.float64)
+        print(d, causal, float(np.abs(oh - o_ref).max()), flush=True)
+        assert_close16(oh, o_ref, lh, lse_ref, f"pingpong d{d} causal={causal}")
+'''
+    env = dict(__import__("os").environ, ATTN_FWD16_SCHEDULE="pingpong")
+    r = subprocess.run([sys.executable, "-c", code, root], env=env, capture_output=True, text=True, timeout=120)
+    print(r.stdout)
+    assert r.returncode == 0, r.stdout + r.stderr
