@@ -225,3 +225,18 @@ for d in (64, 128):
     r = subprocess.run([sys.executable, "-c", code, root], env=env, capture_output=True, text=True, timeout=120)
     print(r.stdout)
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("d,h", [(64, 32), (128, 16), (256, 8)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_seq_sweep_s512_full_tensors(lib, d, h, causal):
+    """The seq-512 points of the 16384-token sweep (batch 32, hidden 2048),
+    compared on every batch, head and row."""
+    import torch
+    s, B = 512, 32
+    q, k, v = W.qkv_normal(2000 + s + d, (B, s, h, d))
+    o, lse = lib.fwd(to_dev(q), to_dev(k), to_dev(v), causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = OA.attention_bshd(q, k, v, 1 / math.sqrt(d), causal)
+    assert_close16(o.float().cpu().numpy().astype(np.float64), o_ref,
+                   lse.cpu().numpy().astype(np.float64), lse_ref, f"sweep s512 d{d} causal={causal} (full)")
