@@ -205,3 +205,34 @@ def test_outlier_workload_accuracy(lib):
     print(out)
     assert out["block+hadamard"] <= 1.2e-2, out
     assert out["block+hadamard"] < out["per-tensor"], out
+
+
+def test_outlier_sensitivity_sigma_100(lib):
+    """The other reading of the outlier law, N(0, 100) as sigma = 100 (the
+    default reading is sigma = 10): the same GPU pipelines (e4m3 and int8
+    scores, block-128 + rotation vs per-tensor) on batch 4, 16 heads, seq 8192,
+    d128.  Reported, with the ordering the pages claim (block scales with
+    incoherent processing beat one scale per tensor) checked; the 1.2e-2 bound
+    belongs to the default reading."""
+    import torch
+    w = W.WORKLOADS["fp8"]
+    qs, _ = w.shapes()
+    q, k, v = W.qkv_outlier(w.seed, qs, sigma=100.0)
+    signs = torch.from_numpy(W.random_signs(4, w.head_dim)).cuda()
+    tq, tk, tv = to_dev(q), to_dev(k), to_dev(v)
+    rows = sample_rows(w.seq_q, seed=37, n_random=24)
+    o_ref = _rows_ref(q, k, v, w.scale, rows)
+    out = {}
+    for fmt in ("e4m3", "int8"):
+        quant = lib.fp8_quantize if fmt == "e4m3" else lib.int8_quantize
+        fwd = lib.fwd_fp8 if fmt == "e4m3" else lib.fwd_int8
+        for name, br, sg in (("block+hadamard", 128, signs), ("per-tensor", 0, None)):
+            q8, qsc = quant(tq, br, sg)
+            k8, ksc = quant(tk, br, sg)
+            v8, vsc = lib.fp8_quantize(tv, br, None)
+            o, _ = fwd(q8, qsc, k8, ksc, v8, vsc, br, w.scale, False)
+            torch.cuda.synchronize()
+            out[f"{fmt} {name}"] = OF.rmse(o[:, rows].float().cpu().numpy().astype(np.float64), o_ref)
+    print("sigma=100:", out)
+    for fmt in ("e4m3", "int8"):
+        assert out[f"{fmt} block+hadamard"] < out[f"{fmt} per-tensor"], out
