@@ -17,25 +17,6 @@
 
 namespace attn {
 
-// float32 -> e4m3fn (OCP): nearest-even, saturating to +-448, NaN -> 0x7F.
-// Built from the bit layout: normal results keep 3 mantissa bits of the
-// float32 (bias 127 -> 7); below 2^-6 the spacing is the fixed 2^-9.
-__device__ __forceinline__ uint32_t e4m3_encode(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return 0x7fu;               // NaN
-  if (a >= 0x43e00000u) return 0x7eu | sign;       // >= 448 (and inf): saturate
-  if (a < 0x3c800000u) {                           // < 2^-6: multiples of 2^-9
-    const float f = __uint_as_float(a) * 512.f;    // exact power-of-two scaling
-    return (uint32_t)__builtin_rintf(f) | sign;    // 0..8 (8 = smallest normal)
-  }
-  const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);  // round mantissa to 3 bits
-  const uint32_t e = (r >> 23) - 127u + 7u;
-  const uint32_t m = (r >> 20) & 7u;
-  return ((e << 3) | m) | sign;
-}
-
 // float32 (already divided by the scale) -> int8 code: nearest-even, clamped
 // to [-127, 127], returned as its byte
 __device__ __forceinline__ uint32_t int8_encode(float y) {
@@ -139,13 +120,22 @@ __global__ void __launch_bounds__(256) fp8_quant_kernel(QuantArgs a) {
       u32x4 out;
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
-        uint32_t v = 0;
+        float y[4];
 #pragma unroll
-        for (int by = 0; by < 4; ++by) {
-          const float y = __fdiv_rn(x[p][4 * wd + by], scale);
-          v |= (FMT == kInt8 ? int8_encode(y) : e4m3_encode(y)) << (8 * by);
+        for (int by = 0; by < 4; ++by) y[by] = __fdiv_rn(x[p][4 * wd + by], scale);
+        if constexpr (FMT == kInt8) {
+          uint32_t v = 0;
+#pragma unroll
+          for (int by = 0; by < 4; ++by) v |= int8_encode(y[by]) << (8 * by);
+          out[wd] = v;
+        } else {
+          // the hardware converter rounds to nearest-even into e4m3fn but does
+          // not saturate: clamp to +-448 first (one v_med3 per value)
+#pragma unroll
+          for (int by = 0; by < 4; ++by) y[by] = __builtin_amdgcn_fmed3f(y[by], -448.f, 448.f);
+          const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+          out[wd] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
         }
-        out[wd] = v;
       }
       *(u32x4*)(a.x8 + (((int64_t)b * a.S + row) * a.H + h) * D + 16 * seg) = out;
     }

@@ -57,6 +57,36 @@ def test_quantize_bitexact_without_rotation(lib, d, s, block_rows):
     np.testing.assert_array_equal(codes.cpu().numpy(), rc)
 
 
+def _e4m3_boundary_values(rng, shape):
+    """Values whose quotient by the scale falls on every e4m3 code, on every
+    rounding tie between neighbouring codes (normal and subnormal), one bf16
+    step either side of each tie, and below half the smallest subnormal (which
+    must give a signed zero), in both signs.  Every (batch, head, 128-row block)
+    holds +-28, so its scale is 28 / 448 = 2^-4 and the division is exact."""
+    vals = OF.e4m3_decode(np.arange(127, dtype=np.uint8))
+    mids = (vals[:-1] + vals[1:]) / 2
+    step = 2.0 ** (np.floor(np.log2(np.abs(mids))) - 7)     # one bf16 step
+    y = np.concatenate([vals, mids, mids + step, mids - step, [2.0 ** -11, 2.0 ** -13]])
+    y = np.concatenate([y, -y]) / 16.0
+    x = rng.permutation(np.resize(y, int(np.prod(shape)))).reshape(shape)
+    x[:, ::128, :, 0] = 28.0
+    x[:, 1::128, :, 1] = -28.0
+    return x
+
+
+@pytest.mark.parametrize("block_rows", [128, 0])
+def test_quantize_rounding_ties_bitexact(lib, block_rows):
+    import torch
+    x = _e4m3_boundary_values(np.random.default_rng(7), (2, 300, 2, 64))
+    assert np.array_equal(to_dev(x).float().cpu().numpy(), x)   # bf16-exact inputs
+    codes, scales = lib.fp8_quantize(to_dev(x), block_rows, None)
+    torch.cuda.synchronize()
+    rc, rs = OF.quantize(x, block_rows)
+    assert np.all(rs == np.float32(2.0 ** -4))
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+
+
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_quantize_with_rotation_within_one_step(lib, d):
     import torch
