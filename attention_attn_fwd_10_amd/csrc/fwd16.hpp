@@ -58,20 +58,26 @@ struct Fwd16Cfg {
   static constexpr int BR = 32 * NW;              // query rows per workgroup
   static constexpr int BC = 64;                   // keys per tile
   static constexpr int CPR = D / 8;               // 16-byte chunks per row
-  // LDS row pitches in 16-byte slots.  K: one pad slot, so the 16 rows read by
-  // 16 consecutive lanes with ds_read_b128 start in 16 different bank groups.
-  // V: the transposing reads fetch 4 rows x 32 bytes per 16 lanes; the pitch
-  // puts those 4 rows in distinct 32-byte bank groups.
-  static constexpr int KSLOTS = CPR + 1;
-  static constexpr int VSLOTS = D == 64 ? 10 : (D == 128 ? 19 : 34);
-  static constexpr int KP = 8 * KSLOTS;           // pitches in elements
-  static constexpr int VP = 8 * VSLOTS;
-  static constexpr int K_ELEMS = BC * KP;
-  static constexpr int V_ELEMS = BC * VP;
-  // a tile is copied by KSLOTS (VSLOTS) wave instructions of 64 x 16 bytes,
-  // dealt round-robin to the NW waves
-  static constexpr int KI_W = (KSLOTS + NW - 1) / NW;
-  static constexpr int VI_W = (VSLOTS + NW - 1) / NW;
+  // LDS layout of a 64-row tile.  A tile is copied by CPR wave instructions of
+  // 64 lanes x 16 bytes, each writing 1 KB of whole rows: instruction m holds
+  // the rows R with R % CPR == m (lane l: row m + CPR * (l / CPR), chunk
+  // l % CPR).  The instructions sit 1 KB plus a gap apart, and the gap spreads
+  // the rows that one LDS read instruction touches together over the banks:
+  // 16 bytes for K, whose 16 rows read by 16 consecutive lanes (ds_read_b128)
+  // then start in 16 different 16-byte bank groups; 64 bytes for V, whose
+  // transposing reads fetch, per 32 lanes, 4 consecutive rows x 2 x 32 bytes
+  // (the 4 rows then start 64 bytes apart in the banks).  Row R
+  // starts at element row(R) = (R % CPR) * GRP + (R / CPR) * D; row() is
+  // additive over index bits, so fixed row offsets fold into immediates.
+  static constexpr int KGRP = 512 + 8;            // instruction pitches in elements
+  static constexpr int VGRP = 512 + 32;
+  static constexpr int K_ELEMS = CPR * KGRP;
+  static constexpr int V_ELEMS = CPR * VGRP;
+  static constexpr int krow(int r) { return (r % CPR) * KGRP + (r / CPR) * D; }
+  static constexpr int vrow(int r) { return (r % CPR) * VGRP + (r / CPR) * D; }
+  // each wave copies CPR / NW instructions of each of K and V per tile
+  static_assert(CPR % NW == 0, "the copy instructions of a tile are dealt evenly to the waves");
+  static constexpr int CI_W = CPR / NW;
   // waves per SIMD: two at head dims up to 128 (one workgroup of 8 waves or
   // two of 4 per CU), one at 256
   static constexpr int WAVES_PER_EU = D <= 128 ? 2 : 1;
@@ -86,7 +92,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
     fwd16_kernel(FwdArgs a) {
   constexpr int NW = fwd16_waves(D, MODE, CAUSAL);
   using C = Fwd16Cfg<D, NW>;
-  constexpr int BR = C::BR, BC = C::BC, KP = C::KP, VP = C::VP, CPR = C::CPR;
+  constexpr int BR = C::BR, BC = C::BC, CPR = C::CPR;
   constexpr bool DENSE = MODE == kDense || MODE == kDenseBias;
   constexpr bool BIAS = MODE == kDenseBias;
   static_assert(!BIAS || D <= 128, "the score bias is supported up to head dim 128");
@@ -200,9 +206,8 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   }
 
   // ---- K/V tiles: asynchronous global -> LDS copies --------------------------
-  // Slot s of a tile (16 bytes) holds LDS row s / SLOTS, column chunk s % SLOTS;
-  // chunks >= CPR are padding and are not copied.  K rows are stored with the
-  // rows of each 32-row group in swz23 order, V rows in natural order.
+  // LDS row R of a K tile holds key (R & ~31) | swz23(R & 31), i.e. the rows of
+  // each 32-row group in swz23 order; row R of a V tile holds key R.
   // score bias: one buffer resource over this (b, h) plane (rows of bias_ss
   // elements, the last one readable up to a multiple of 8 elements, so that no
   // 16-byte read straddles the range end; reads past it return zeros), and
@@ -217,40 +222,32 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   }
   const uint16_t* const kg = (const uint16_t*)a.k + koff;
   const uint16_t* const vg = (const uint16_t*)a.v + voff;
+  // the key and 16-byte chunk this lane copies in its copy round ii (wave
+  // instruction wave + NW * ii of the tile)
   auto k_slot = [&](int ii, int& key_local, int& chunk) {
-    const int s = 64 * (wave + NW * ii) + lane;
-    const int r = s / C::KSLOTS;
-    chunk = s - r * C::KSLOTS;
+    const int r = wave + NW * ii + CPR * (lane / CPR);
+    chunk = lane % CPR;
     key_local = (r & ~31) | swz23(r & 31);
   };
   auto v_slot = [&](int ii, int& key_local, int& chunk) {
-    const int s = 64 * (wave + NW * ii) + lane;
-    key_local = s / C::VSLOTS;
-    chunk = s - key_local * C::VSLOTS;
+    key_local = wave + NW * ii + CPR * (lane / CPR);
+    chunk = lane % CPR;
   };
-  // byte offsets of this lane's slots inside a tile for the dense/varlen
-  // layouts (padding slots point out of range and read zeros).  The slots of
-  // the full rounds (every wave copies one) are kept in registers; the last,
-  // partial round is copied by a few waves only, and its offset is computed
-  // when it is needed, so that it takes no register (spilling it would make
-  // the copy wait for every load in flight)
-  constexpr uint32_t kOutOfRange = 0x7ffffff0u;
-  constexpr int KI_FULL = C::KSLOTS / NW, VI_FULL = C::VSLOTS / NW;
-  auto k_off = [&](int ii) {
+  // From one round to the next only the instruction index moves, by NW, in
+  // index bits that no other term of the row uses; the key therefore moves by
+  // a compile-time amount (swz23(NW * ii) for K, NW * ii for V) and the lane's
+  // byte offset inside the tile is that of round 0 plus a scalar, so one
+  // register per operand holds the offsets of every round.
+  auto k_key_shift = [](int ii) { return swz23(NW * ii); };
+  auto v_key_shift = [](int ii) { return NW * ii; };
+  uint32_t k_boff, v_boff;
+  {
     int kl, ch;
-    k_slot(ii, kl, ch);
-    return ch < CPR ? 2u * (uint32_t)(kl * (int)a.k_ss + ch * 8) : kOutOfRange;
-  };
-  auto v_off = [&](int ii) {
-    int kl, ch;
-    v_slot(ii, kl, ch);
-    return ch < CPR ? 2u * (uint32_t)(kl * (int)a.v_ss + ch * 8) : kOutOfRange;
-  };
-  uint32_t k_boff[KI_FULL], v_boff[VI_FULL];
-#pragma unroll
-  for (int ii = 0; ii < KI_FULL; ++ii) k_boff[ii] = k_off(ii);
-#pragma unroll
-  for (int ii = 0; ii < VI_FULL; ++ii) v_boff[ii] = v_off(ii);
+    k_slot(0, kl, ch);
+    k_boff = 2u * (uint32_t)(kl * (int)a.k_ss + ch * 8);
+    v_slot(0, kl, ch);
+    v_boff = 2u * (uint32_t)(kl * (int)a.v_ss + ch * 8);
+  }
   auto row_of = [&](int key) -> int64_t {  // element offset of key's row (paged: through the table)
     if constexpr (MODE == kPaged) {
       const int page = a.block_table[(int64_t)b * a.max_pages + (key >> a.page_shift)];
@@ -261,10 +258,9 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   };
   // A 64-key tile is contiguous in memory for the dense and varlen layouts,
   // and inside one page of a paged cache whose pages hold >= 64 tokens.  Then
-  // one buffer resource per tile covers rows key0 .. Lk-1 (rows past the
-  // sequence end read as zeros) and every copy is a single buffer load.
-  // Smaller pages: each row through the block table; rows past Lk repeat row
-  // Lk-1 (finite data, masked out of the scores and multiplied by p = 0).
+  // every copy is a single buffer load whose resource ends at row Lk (rows
+  // past the sequence end read as zeros).  Smaller pages: each row through
+  // the block table.
   const bool contiguous = MODE != kPaged || a.page_shift >= 6;
   // (the table is read through the constant address space: with a uniform
   // index that is a scalar load, which the tile copies never wait behind)
@@ -280,63 +276,55 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   // (tile ranges are clamped below 2^31; the host limits seq strides to 2^24
   // elements, so a tile's 64 rows always lie inside them)
   // (row0: tile_row0(key0), looked up once per tile by the caller)
+  // Copies of a tile whose rows are contiguous: one buffer resource from the
+  // tile's first row to row Lk (rows past the sequence end read as zeros);
+  // round ii adds the byte offset of its key shift to the lane's round-0
+  // offset (a scalar, below 2^31 since the shift is < 64 rows).
+  auto dma_k_c = [&](int key0, auto buf, int64_t row0) {
+    uint16_t* kb = kbuf(buf) + wave * C::KGRP;
+    const uint64_t kn = 2ull * (uint64_t)(Lk - key0) * (uint64_t)a.k_ss;
+    const i32x4 kr = make_rsrc(kg + row0 * a.k_ss, (uint32_t)min(kn, (uint64_t)0x7fff0000u));
+#pragma unroll
+    for (int ii = 0; ii < C::CI_W; ++ii)
+      dma16_buf(kr, k_boff + 2u * (uint32_t)k_key_shift(ii) * (uint32_t)a.k_ss, kb + NW * ii * C::KGRP);
+  };
+  auto dma_v_c = [&](int key0, auto buf, int64_t row0) {
+    uint16_t* vb = vbuf(buf) + wave * C::VGRP;
+    const uint64_t vn = 2ull * (uint64_t)(Lk - key0) * (uint64_t)a.v_ss;
+    const i32x4 vr = make_rsrc(vg + row0 * a.v_ss, (uint32_t)min(vn, (uint64_t)0x7fff0000u));
+#pragma unroll
+    for (int ii = 0; ii < C::CI_W; ++ii)
+      dma16_buf(vr, v_boff + 2u * (uint32_t)v_key_shift(ii) * (uint32_t)a.v_ss, vb + NW * ii * C::VGRP);
+  };
+  // Copies for any layout: contiguous tiles as above; otherwise (pages of
+  // fewer than 64 tokens) each row through the block table, rows past Lk
+  // repeating row Lk-1 (finite data, masked out of the scores and multiplied
+  // by p = 0).
   auto dma_k = [&](int key0, auto buf, int64_t row0) {
-    uint16_t* kb = kbuf(buf);
     if (contiguous) {
-      const uint64_t kn = 2ull * (uint64_t)(Lk - key0) * (uint64_t)a.k_ss;
-      const i32x4 kr = make_rsrc(kg + row0 * a.k_ss, (uint32_t)min(kn, (uint64_t)0x7fff0000u));
-#pragma unroll
-      for (int ii = 0; ii < C::KI_W; ++ii)
-        if (wave + NW * ii < C::KSLOTS) dma16_buf(kr, ii < KI_FULL ? k_boff[ii] : k_off(ii), kb + (wave + NW * ii) * 512);
+      dma_k_c(key0, buf, row0);
     } else {
+      uint16_t* kb = kbuf(buf) + wave * C::KGRP;
 #pragma unroll
-      for (int ii = 0; ii < C::KI_W; ++ii) {
-        const int i = wave + NW * ii;
-        if (i < C::KSLOTS) {
-          int kl, ch;
-          k_slot(ii, kl, ch);
-          if (ch < CPR) dma16(kg + row_of(min(key0 + kl, Lk - 1)) * a.k_ss + ch * 8, kb + i * 512);
-        }
+      for (int ii = 0; ii < C::CI_W; ++ii) {
+        int kl, ch;
+        k_slot(ii, kl, ch);
+        dma16(kg + row_of(min(key0 + kl, Lk - 1)) * a.k_ss + ch * 8, kb + NW * ii * C::KGRP);
       }
     }
   };
   auto dma_v = [&](int key0, auto buf, int64_t row0) {
-    uint16_t* vb = vbuf(buf);
     if (contiguous) {
-      const uint64_t vn = 2ull * (uint64_t)(Lk - key0) * (uint64_t)a.v_ss;
-      const i32x4 vr = make_rsrc(vg + row0 * a.v_ss, (uint32_t)min(vn, (uint64_t)0x7fff0000u));
-#pragma unroll
-      for (int ii = 0; ii < C::VI_W; ++ii)
-        if (wave + NW * ii < C::VSLOTS) dma16_buf(vr, ii < VI_FULL ? v_boff[ii] : v_off(ii), vb + (wave + NW * ii) * 512);
+      dma_v_c(key0, buf, row0);
     } else {
+      uint16_t* vb = vbuf(buf) + wave * C::VGRP;
 #pragma unroll
-      for (int ii = 0; ii < C::VI_W; ++ii) {
-        const int i = wave + NW * ii;
-        if (i < C::VSLOTS) {
-          int kl, ch;
-          v_slot(ii, kl, ch);
-          if (ch < CPR) dma16(vg + row_of(min(key0 + kl, Lk - 1)) * a.v_ss + ch * 8, vb + i * 512);
-        }
+      for (int ii = 0; ii < C::CI_W; ++ii) {
+        int kl, ch;
+        v_slot(ii, kl, ch);
+        dma16(vg + row_of(min(key0 + kl, Lk - 1)) * a.v_ss + ch * 8, vb + NW * ii * C::VGRP);
       }
     }
-  };
-  // the same copies for callers that know the tile is contiguous (no per-row
-  // table path compiled in)
-  auto dma_k_c = [&](int key0, auto buf, int64_t row0) {
-    uint16_t* kb = kbuf(buf);
-    const uint64_t kn = 2ull * (uint64_t)(Lk - key0) * (uint64_t)a.k_ss;
-    const i32x4 kr = make_rsrc(kg + row0 * a.k_ss, (uint32_t)min(kn, (uint64_t)0x7fff0000u));
-#pragma unroll
-    for (int ii = 0; ii < C::KI_W; ++ii)
-      if (wave + NW * ii < C::KSLOTS) dma16_buf(kr, ii < KI_FULL ? k_boff[ii] : k_off(ii), kb + (wave + NW * ii) * 512);
-  };
-  auto dma_v_c = [&](int key0, auto buf, int64_t row0) {
-    uint16_t* vb = vbuf(buf);
-    const uint64_t vn = 2ull * (uint64_t)(Lk - key0) * (uint64_t)a.v_ss;
-    const i32x4 vr = make_rsrc(vg + row0 * a.v_ss, (uint32_t)min(vn, (uint64_t)0x7fff0000u));
-#pragma unroll
-    for (int ii = 0; ii < C::VI_W; ++ii)
-      if (wave + NW * ii < C::VSLOTS) dma16_buf(vr, ii < VI_FULL ? v_boff[ii] : v_off(ii), vb + (wave + NW * ii) * 512);
   };
   auto dma_tile = [&](int key0, int buf) {
     const int64_t row0 = contiguous ? tile_row0(key0) : 0;
@@ -349,7 +337,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   // 16*(g%2) + 4*swap(j%4), so that after the transpose lane l holds
   // V[key 8*(l/32) + e][d = swz23(l % 32)] for e = 0..7.
   const int vg_grp = lane >> 4, vg_j = lane & 15;
-  const int vtr_off = (8 * (vg_grp >> 1) + (vg_j >> 2)) * VP + 16 * (vg_grp & 1) +
+  const int vtr_off = C::vrow(8 * (vg_grp >> 1) + (vg_j >> 2)) + 16 * (vg_grp & 1) +
                       4 * (((vg_j & 1) << 1) | ((vg_j >> 1) & 1));
 
   // ---- running state ---------------------------------------------------------
@@ -417,7 +405,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
     if (!wave_active) return;
     if (CAUSAL && key0 > wave_last_key) return;  // tile fully masked for this wave
     // S^T = K Q^T
-    const uint16_t* ks = kbuf(buf) + l32 * KP + 8 * hh;
+    const uint16_t* ks = kbuf(buf) + C::krow(l32) + 8 * hh;
     f32x16 s[BC / 32];
     {
       // the K operands of the tile are read before the first MFMA so that the
@@ -432,7 +420,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
 #pragma unroll
         for (int kk = 0; kk < KG; ++kk)
 #pragma unroll
-          for (int tt = 0; tt < BC / 32; ++tt) kop[tt][kk] = *(const u32x4*)(ks + tt * 32 * KP + 16 * (g * KG + kk));
+          for (int tt = 0; tt < BC / 32; ++tt) kop[tt][kk] = *(const u32x4*)(ks + C::krow(32 * tt) + 16 * (g * KG + kk));
         __builtin_amdgcn_sched_barrier(0);  // keep the group's reads ahead of its MFMAs
         __builtin_amdgcn_s_setprio(1);       // favour this wave while it feeds the matrix core
 #pragma unroll
@@ -503,8 +491,8 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
                         pack2<DT>(p[6], p[7])};
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const uint16_t* vp = vs + 16 * c * VP + 32 * dt;
-        const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * VP);
+        const uint16_t* vp = vs + C::vrow(16 * c) + 32 * dt;
+        const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + C::vrow(4));
         oacc[dt] = mfma32<DT>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pk, oacc[dt]);
       }
     }
@@ -518,7 +506,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   auto tile_active = [&](int key0) { return wave_active && !(CAUSAL && key0 > wave_last_key); };
   // S^T = K Q^T, masking and the row max; true when the running max must move
   auto scores_max = [&](int key0, int buf) -> bool {
-    const uint16_t* ks = kbuf(buf) + l32 * KP + 8 * hh;
+    const uint16_t* ks = kbuf(buf) + C::krow(l32) + 8 * hh;
     {
       // the K operands of the tile are read before the first MFMA so that the
       // LDS latency is paid once (at D = 256 in quarters, which keeps them
@@ -532,7 +520,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
 #pragma unroll
         for (int kk = 0; kk < KG; ++kk)
 #pragma unroll
-          for (int tt = 0; tt < BC / 32; ++tt) kop[tt][kk] = *(const u32x4*)(ks + tt * 32 * KP + 16 * (g * KG + kk));
+          for (int tt = 0; tt < BC / 32; ++tt) kop[tt][kk] = *(const u32x4*)(ks + C::krow(32 * tt) + 16 * (g * KG + kk));
         __builtin_amdgcn_sched_barrier(0);  // keep the group's reads ahead of its MFMAs
         __builtin_amdgcn_s_setprio(1);       // favour this wave while it feeds the matrix core
 #pragma unroll
@@ -606,8 +594,8 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
                         pack2<DT>(p[6], p[7])};
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const uint16_t* vp = vs + 16 * c * VP + 32 * dt;
-        const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * VP);
+        const uint16_t* vp = vs + C::vrow(16 * c) + 32 * dt;
+        const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + C::vrow(4));
         oacc[dt] = mfma32<DT>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pk, oacc[dt]);
       }
     }
@@ -617,12 +605,12 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   // ---- software-pipelined pieces (head dims up to 128, tiles needing no mask)
   // S^T = K Q^T of one tile
   auto qk_tile = [&](auto buf, f32x16 (&sc)[BC / 32]) {
-    const uint16_t* ks = kbuf(buf) + l32 * KP + 8 * hh;
+    const uint16_t* ks = kbuf(buf) + C::krow(l32) + 8 * hh;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
       for (int tt = 0; tt < BC / 32; ++tt) {
-        const u32x4 kop = *(const u32x4*)(ks + tt * 32 * KP + 16 * kk);
+        const u32x4 kop = *(const u32x4*)(ks + C::krow(32 * tt) + 16 * kk);
         sc[tt] = mfma32<DT>(kop, qf[kk], kk == 0 ? zero16 : sc[tt]);
       }
   };
@@ -669,8 +657,8 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
     for (int c = 0; c < BC / 16; ++c)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const uint16_t* vp = vs + 16 * c * VP + 32 * dt;
-        const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * VP);
+        const uint16_t* vp = vs + C::vrow(16 * c) + 32 * dt;
+        const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + C::vrow(4));
         oacc[dt] = mfma32<DT>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pk[c], oacc[dt]);
       }
   };
@@ -717,7 +705,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
           auto step_math = [&](auto cur, auto nxt, f32x16 (&sc)[BC / 32], f32x16 (&sn)[BC / 32]) {
             constexpr int NA = (D / 16) * (BC / 32), NB = (D / 32) * (BC / 16);
             constexpr int KPRE = 3, VPRE = 2;
-            const uint16_t* ks = kbuf(nxt) + l32 * KP + 8 * hh;
+            const uint16_t* ks = kbuf(nxt) + C::krow(l32) + 8 * hh;
             const uint16_t* vs = vbuf(cur) + vtr_off;
             float p[BC / 2];
             u32x4 pk[BC / 16];
@@ -740,13 +728,13 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
             __builtin_amdgcn_sched_barrier(0);
             u32x4 kop[NA];
 #pragma unroll
-            for (int i = 0; i < KPRE; ++i) kop[i] = *(const u32x4*)(ks + (i & 1) * 32 * KP + 16 * (i >> 1));
+            for (int i = 0; i < KPRE; ++i) kop[i] = *(const u32x4*)(ks + C::krow(32 * (i & 1)) + 16 * (i >> 1));
 #pragma unroll
             for (int i = 0; i < NA; ++i) {
               const int kk = i >> 1, tt = i & 1;
               sn[tt] = mfma32<DT>(kop[i], qf[kk], kk == 0 ? zero16 : sn[tt]);
               if (i + KPRE < NA)
-                kop[i + KPRE] = *(const u32x4*)(ks + ((i + KPRE) & 1) * 32 * KP + 16 * ((i + KPRE) >> 1));
+                kop[i + KPRE] = *(const u32x4*)(ks + C::krow(32 * ((i + KPRE) & 1)) + 16 * ((i + KPRE) >> 1));
               if (i == 0) {
                 mx = sc[0][0];
 #pragma unroll
@@ -774,18 +762,18 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
             u32x2 vop[NB][2];
 #pragma unroll
             for (int i = 0; i < VPRE; ++i) {
-              const uint16_t* vp = vs + 16 * (i / (D / 32)) * VP + 32 * (i % (D / 32));
+              const uint16_t* vp = vs + C::vrow(16 * (i / (D / 32))) + 32 * (i % (D / 32));
               vop[i][0] = lds_read_tr16(vp);
-              vop[i][1] = lds_read_tr16(vp + 4 * VP);
+              vop[i][1] = lds_read_tr16(vp + C::vrow(4));
             }
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
               const int c = i / (D / 32), dt = i % (D / 32);
               oacc[dt] = mfma32<DT>(u32x4{vop[i][0][0], vop[i][0][1], vop[i][1][0], vop[i][1][1]}, pk[c], oacc[dt]);
               if (i + VPRE < NB) {
-                const uint16_t* vp = vs + 16 * ((i + VPRE) / (D / 32)) * VP + 32 * ((i + VPRE) % (D / 32));
+                const uint16_t* vp = vs + C::vrow(16 * ((i + VPRE) / (D / 32))) + 32 * ((i + VPRE) % (D / 32));
                 vop[i + VPRE][0] = lds_read_tr16(vp);
-                vop[i + VPRE][1] = lds_read_tr16(vp + 4 * VP);
+                vop[i + VPRE][1] = lds_read_tr16(vp + C::vrow(4));
               }
               if (i < NB / 2) exps(24 + i * 8 / (NB / 2), 24 + (i + 1) * 8 / (NB / 2));
               if (i == NB / 2 - 1) l_run = fmaf(l_run, alpha, psum);

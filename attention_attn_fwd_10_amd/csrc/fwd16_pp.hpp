@@ -30,8 +30,11 @@ struct PPCfg {
   static constexpr int BR = 32 * NW;               // query rows per workgroup
   static constexpr int BC = 64;                    // keys per tile
   static constexpr int CPR = D / 8;
-  static constexpr int KSLOTS = Fwd16Cfg<D>::KSLOTS;
-  static constexpr int VSLOTS = Fwd16Cfg<D>::VSLOTS;
+  // LDS row pitches in 16-byte slots: one pad slot for K (16 rows read by 16
+  // lanes with ds_read_b128 start in distinct bank groups); for V a pitch that
+  // puts the 4 rows of a transposing read in distinct 32-byte bank groups
+  static constexpr int KSLOTS = CPR + 1;
+  static constexpr int VSLOTS = D == 64 ? 10 : (D == 128 ? 19 : 34);
   static constexpr int KP = 8 * KSLOTS;
   static constexpr int VP = 8 * VSLOTS;
   static constexpr int K_ELEMS = BC * KP;
