@@ -42,10 +42,23 @@ namespace fp8cfg {
 constexpr int D = 128;
 constexpr int BR = 128;            // query rows per workgroup
 constexpr int BC = 64;             // keys per tile
-constexpr int SLOTS = D / 16 + 1;  // 16-byte slots per LDS row (one pad slot): pitch 144 bytes
-constexpr int PITCH = 16 * SLOTS;  // bytes
-constexpr int TILE_BYTES = BC * PITCH;
-constexpr int I_W = (SLOTS + 3) / 4;  // copy instructions per wave per tile (max)
+// LDS layout of a 64-row tile (rows of D bytes, CPR 16-byte chunks).  The
+// tile is copied by CPR wave instructions of 64 lanes x 16 bytes; instruction
+// m writes 1 KB holding the rows R with R % CPR == m (lane l: row m + CPR *
+// (l / CPR), chunk l % CPR).  Instructions sit 1 KB plus a gap apart; the gap
+// spreads what one read instruction touches over the banks: 16 bytes for K
+// (16 rows read by 16 lanes with ds_read_b128 start in 16 distinct 16-byte
+// bank groups), 32 bytes for V (the 8 rows x 32 bytes of a 32-lane
+// transposing read fall in 8 distinct 32-byte groups).  Row R starts at byte
+// row(R) = (R % CPR) * GRP + (R / CPR) * D, additive over index bits.
+constexpr int CPR = D / 16;
+constexpr int KGRP = 1024 + 16;  // bytes
+constexpr int VGRP = 1024 + 32;
+constexpr int K_BYTES = CPR * KGRP;
+constexpr int V_BYTES = CPR * VGRP;
+constexpr int CI_W = CPR / 4;      // copy instructions per wave per tile and operand
+constexpr int krow(int r) { return (r % CPR) * KGRP + (r / CPR) * D; }
+constexpr int vrow(int r) { return (r % CPR) * VGRP + (r / CPR) * D; }
 constexpr float kMu = 6.0f;        // probabilities are quantised as p * 2^kMu
 constexpr float kTau = 2.0f;       // the running max may lag by 2^kTau
 }  // namespace fp8cfg
@@ -87,10 +100,10 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
   // with compile-time slot numbers: the compiler then sees that a tile's LDS
   // reads never touch the slot the next tile is being copied into, and does
   // not make them wait for that copy
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k0[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k1[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v0[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k0[K_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k1[K_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v0[V_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v1[V_BYTES];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
@@ -157,39 +170,38 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
   };
   const uint8_t* const kg = a.k + koff;
   const uint8_t* const vg = a.v + koff;
-  // byte offsets of this lane's slots inside a tile (padding slots point out of
-  // range and read zeros)
-  constexpr uint32_t kOutOfRange = 0x7ffffff0u;
-  uint32_t k_boff[I_W], v_boff[I_W];
-#pragma unroll
-  for (int ii = 0; ii < I_W; ++ii) {
-    const int s = 64 * (wave + 4 * ii) + lane;
-    const int R = s / SLOTS, c = s - R * SLOTS;
-    k_boff[ii] = c < SLOTS - 1 ? (uint32_t)(k_row_key(R) * (int)row_q + 16 * c) : kOutOfRange;
-    v_boff[ii] = c < SLOTS - 1 ? (uint32_t)(R * (int)row_q + 16 * c) : kOutOfRange;
+  // Byte offsets of this lane's copy in round 0 (wave instruction `wave`).
+  // Round ii copies instruction wave + 4 * ii: only row bit 2 moves, which
+  // k_row_key maps to key bit 5 (32 keys) and V's identity map to 4 keys, so
+  // each round's offset is the round-0 offset plus a scalar.
+  uint32_t k_boff, v_boff;
+  {
+    const int R = wave + CPR * (lane / CPR), c = lane % CPR;
+    k_boff = (uint32_t)(k_row_key(R) * (int)row_q + 16 * c);
+    v_boff = (uint32_t)(R * (int)row_q + 16 * c);
   }
+  static_assert(CI_W == 2, "two copy rounds per wave: the round shift is one row bit");
   // one buffer resource per tile covers rows key0 .. Lk-1: rows past the
   // sequence end read as zeros
   auto dma_tile = [&](int key0, auto buf) {
-    uint8_t* kb = decltype(buf)::value ? lds_k1 : lds_k0;
-    uint8_t* vb = decltype(buf)::value ? lds_v1 : lds_v0;
+    uint8_t* kb = (decltype(buf)::value ? lds_k1 : lds_k0) + wave * KGRP;
+    uint8_t* vb = (decltype(buf)::value ? lds_v1 : lds_v0) + wave * VGRP;
     const uint64_t n = (uint64_t)(Lk - key0) * (uint64_t)row_q;
     const uint32_t nb = (uint32_t)min(n, (uint64_t)0x7fff0000u);
     const i32x4 kr = make_rsrc(kg + (int64_t)key0 * row_q, nb);
     const i32x4 vr = make_rsrc(vg + (int64_t)key0 * row_q, nb);
 #pragma unroll
-    for (int ii = 0; ii < I_W; ++ii)
-      if (wave + 4 * ii < SLOTS) {
-        dma16_buf(kr, k_boff[ii], kb + (wave + 4 * ii) * 1024);
-        dma16_buf(vr, v_boff[ii], vb + (wave + 4 * ii) * 1024);
-      }
+    for (int ii = 0; ii < CI_W; ++ii) {
+      dma16_buf(kr, k_boff + (uint32_t)(k_row_key(4 * ii) * (int)row_q), kb + 4 * ii * KGRP);
+      dma16_buf(vr, v_boff + (uint32_t)(4 * ii * (int)row_q), vb + 4 * ii * VGRP);
+    }
   };
 
   // V^T operand: lane (group g, index j) addresses row 32(g/2) + 8u + j/2 and
   // columns 32dt + 16(g%2) + 8(j%2); after the byte transpose lane l holds
   // V[32(l/32) + 8u + t][32dt + l%32] as its elements 8u + t.
   const int vgrp = lane >> 4, vj = lane & 15;
-  const int vtr_off = (32 * (vgrp >> 1) + (vj >> 1)) * PITCH + 16 * (vgrp & 1) + 8 * (vj & 1);
+  const int vtr_off = vrow(32 * (vgrp >> 1) + (vj >> 1)) + 16 * (vgrp & 1) + 8 * (vj & 1);
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -215,14 +227,14 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
     const float sv = vs_scale[blocked ? key0 >> 7 : 0];
     // S^T = K Q^T: two 32-key tiles, two 64-wide k steps each (K operands laid
     // out like the Q fragments)
-    const uint8_t* ks = (decltype(buf)::value ? lds_k1 : lds_k0) + l32 * PITCH + kHalfStride * hh;
+    const uint8_t* ks = (decltype(buf)::value ? lds_k1 : lds_k0) + krow(l32) + kHalfStride * hh;
     i32x8 kop[2][2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const u32x4 x0 = *(const u32x4*)(ks + tt * 32 * PITCH + 64 * kk);
-        const u32x4 x1 = *(const u32x4*)(ks + tt * 32 * PITCH + 64 * kk + kSecond);
+        const u32x4 x0 = *(const u32x4*)(ks + krow(32 * tt) + 64 * kk);
+        const u32x4 x1 = *(const u32x4*)(ks + krow(32 * tt) + 64 * kk + kSecond);
         kop[tt][kk] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
       }
     f32x16 s[2];
@@ -322,7 +334,7 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
     for (int dt = 0; dt < D / 32; ++dt) {
       u32x2 r[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) r[u] = lds_read_tr8(vs + 8 * u * PITCH + 32 * dt);
+      for (int u = 0; u < 4; ++u) r[u] = lds_read_tr8(vs + vrow(8 * u) + 32 * dt);
       const i32x8 vop = {(int)r[0][0], (int)r[0][1], (int)r[1][0], (int)r[1][1],
                          (int)r[2][0], (int)r[2][1], (int)r[3][0], (int)r[3][1]};
       oacc[dt] = mfma32_fp8(vop, pk, oacc[dt]);
