@@ -39,17 +39,42 @@ namespace {
 
 // LDS tile of 64 rows with PAD pad slots per row.  One pad slot (272-byte
 // rows at d128) suits row reads (ds_read_b128, 16 lanes on 16 bank groups);
-// tiles that are also read through the transposing reads take more
+// tiles that are also read through the transposing reads take more.  Row r
+// starts at element row(r).
 template <int D, int PAD = 1>
 struct BwdCfg {
+  static constexpr bool GROUPED = false;
   static constexpr int CPR = D / 8;          // 16-byte chunks per row
   static constexpr int SLOTS = CPR + PAD;    // pad slots per LDS row
   static constexpr int P = 8 * SLOTS;        // LDS row pitch in elements
   static constexpr int TILE = 64 * P;        // elements of a 64-row tile
+  static constexpr int row(int r) { return r * P; }
 };
-// pad slots of tiles read both ways
+// pad slots of padded tiles read both ways
+constexpr int kTrPad = 2;
+
+// Grouped tile at head dim 128 (16 chunks of 16 bytes per row).  The tile is
+// copied by 16 wave instructions; instruction m writes 1 KB holding rows m,
+// m + 16, m + 32, m + 48 and starts at byte 1088 (m % 4) + 4368 (m / 4), so
+// row r starts at bank offset 64 (r % 4) + 16 ((r / 4) % 4) (mod 256 bytes):
+//  * the 16 rows of a 16-lane ds_read_b128 (any 16 consecutive row indices
+//    modulo 16) start in 16 distinct 16-byte bank groups, and
+//  * the 4 consecutive rows x 64 bytes of a 32-lane transposing read fill the
+//    256 bytes of the banks once.
+// row() is additive over the index bit fields (bits 0-1, 2-3, 4-5), so fixed
+// row offsets fold into immediates, and a wave's copy round ii moves its
+// global offset by 4 ii rows and its LDS destination by row(4 ii).
 template <int D>
-constexpr int kTrPad = D == 128 ? 3 : 2;
+struct BwdGrp {
+  static_assert(D == 128, "the grouped backward tile is laid out for head dim 128");
+  static constexpr bool GROUPED = true;
+  static constexpr int CPR = D / 8;
+  static constexpr int row(int r) { return 544 * (r & 3) + 2184 * ((r >> 2) & 3) + D * (r >> 4); }
+  static constexpr int TILE = row(15) + 512;  // the last instruction's 1 KB
+};
+// layout of the tiles at head dim D (PAD: pad slots of the padded layout)
+template <int D, int PAD>
+using BwdTile = std::conditional_t<D == 128, BwdGrp<D>, BwdCfg<D, PAD>>;
 
 template <int DT>
 __device__ __forceinline__ float to_f32(uint16_t x) {
@@ -61,39 +86,49 @@ __device__ __forceinline__ float to_f32(uint16_t x) {
 }
 
 // Asynchronous copy of a 64-row tile (rows of D 16-bit values, `row_elems`
-// apart in memory, starting at g) into LDS with the padded pitch; rows at or
-// past `valid` arrive as zeros without being read.  Slot s of the tile (16
-// bytes) is LDS row s / SLOTS, chunk s % SLOTS; the pad chunk is not copied.
-template <int D, int PAD>
+// apart in memory, starting at g) into LDS in layout C; rows at or past
+// `valid` arrive as zeros without being read.  Padded layout: slot s of the
+// tile (16 bytes) is LDS row s / SLOTS, chunk s % SLOTS, and the pad chunk is
+// not copied.  Grouped layout: wave instruction i writes rows i + 16 q, q =
+// lane / 16, chunk lane % 16.
+template <class C>
 __device__ __forceinline__ void copy_tile(const uint16_t* g, int64_t row_elems, int valid, uint16_t* lds,
                                           int wave, int lane) {
-  using C = BwdCfg<D, PAD>;
   const uint32_t row_bytes = 2u * (uint32_t)row_elems;
   const uint64_t n = valid > 0 ? (uint64_t)valid * row_bytes : 0;
   const i32x4 rs = make_rsrc(g, (uint32_t)min(n, (uint64_t)0x7fff0000u));
+  if constexpr (C::GROUPED) {
+    const uint32_t off = (uint32_t)(wave + 16 * (lane >> 4)) * row_bytes + 16u * (uint32_t)(lane & 15);
 #pragma unroll
-  for (int ii = 0; ii < (C::SLOTS + 3) / 4; ++ii) {
-    const int w = wave + 4 * ii;
-    if (w < C::SLOTS) {
-      const int s = 64 * w + lane;
-      const int r = s / C::SLOTS, c = s - r * C::SLOTS;
-      const uint32_t off = c < C::CPR ? (uint32_t)r * row_bytes + 16u * (uint32_t)c : 0x7ffffff0u;
-      dma16_buf(rs, off, (uint8_t*)lds + 1024 * w);
+    for (int ii = 0; ii < C::CPR / 4; ++ii)
+      dma16_buf(rs, off + 4u * (uint32_t)ii * row_bytes, lds + C::row(wave) + C::row(4 * ii));
+  } else {
+#pragma unroll
+    for (int ii = 0; ii < (C::SLOTS + 3) / 4; ++ii) {
+      const int w = wave + 4 * ii;
+      if (w < C::SLOTS) {
+        const int s = 64 * w + lane;
+        const int r = s / C::SLOTS, c = s - r * C::SLOTS;
+        const uint32_t off = c < C::CPR ? (uint32_t)r * row_bytes + 16u * (uint32_t)c : 0x7ffffff0u;
+        dma16_buf(rs, off, (uint8_t*)lds + 1024 * w);
+      }
     }
   }
 }
 
 __device__ __forceinline__ u32x4 lds16(const uint16_t* p) { return *(const u32x4*)p; }
 
-// Operand A[m][k] (or B[k][n]) = X[k][m] of a row-major LDS tile X with pitch
-// P: two transposing reads give this lane X[k0 + 8(l/32) + e][m0 + l%32],
-// e = 0..7, when p = X + k0 * P + m0 + tr_offset(lane, P).
-__device__ __forceinline__ int tr_offset(int lane, int P) {
+// Operand A[m][k] (or B[k][n]) = X[k][m] of a row-major LDS tile X in layout
+// C: two transposing reads give this lane X[k0 + 8(l/32) + e][m0 + l%32],
+// e = 0..7, when p = X + C::row(k0) + m0 + tr_offset<C>(lane).
+template <class C>
+__device__ __forceinline__ int tr_offset(int lane) {
   const int g = lane >> 4, j = lane & 15;
-  return (8 * (g >> 1) + (j >> 2)) * P + 16 * (g & 1) + 4 * (j & 3);
+  return C::row(8 * (g >> 1) + (j >> 2)) + 16 * (g & 1) + 4 * (j & 3);
 }
-__device__ __forceinline__ u32x4 lds_tr(const uint16_t* p, int P) {
-  const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * P);
+template <class C>
+__device__ __forceinline__ u32x4 lds_tr(const uint16_t* p) {
+  const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + C::row(4));
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
@@ -152,9 +187,8 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(BwdArgs a) {
 // (two workgroups per CU: 256 VGPRs per lane at most)
 template <int D, int DT, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int PAD = kTrPad<D>;
-  using C = BwdCfg<D, PAD>;
-  constexpr int P = C::P, BK = 128, BQ = 64;
+  using C = BwdTile<D, kTrPad>;  // Q and dO tiles are read as rows and transposed
+  constexpr int BK = 128, BQ = 64;
   __shared__ __attribute__((aligned(16))) uint16_t sq0[C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sq1[C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sd0[C::TILE];
@@ -194,7 +228,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dv[dt][r] = dk[dt][r] = 0.f;
   const f32x16 zero16 = {};
-  const int tro = tr_offset(lane, P);
+  const int tro = tr_offset<C>(lane);
 
   // per-row vectors of a query tile, copied like the tiles (waves 0 and 1, one
   // dword per lane; rows past Lq read as 0, harmless: their Q and dO rows are 0)
@@ -223,8 +257,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a) {
       if (qa >= Lq) break;
       if (CAUSAL && kw > qa + 31 + diag) continue;  // every pair of the wave is masked
       f32x16 s = zero16, dp = zero16;
-      const uint16_t* qr = Qs + (32 * st + swz23(l32)) * P + 8 * hh;
-      const uint16_t* dr = Ds + (32 * st + swz23(l32)) * P + 8 * hh;
+      const uint16_t* qr = Qs + C::row(32 * st + swz23(l32)) + 8 * hh;
+      const uint16_t* dr = Ds + C::row(32 * st + swz23(l32)) + 8 * hh;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         s = mfma32<DT>(lds16(qr + 16 * kk), kf[kk], s);
@@ -257,9 +291,9 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a) {
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          const int off = (32 * st + 16 * c) * P + 32 * dt + tro;
-          dv[dt] = mfma32<DT>(lds_tr(Ds + off, P), pk[c], dv[dt]);
-          dk[dt] = mfma32<DT>(lds_tr(Qs + off, P), sk[c], dk[dt]);
+          const int off = C::row(32 * st + 16 * c) + 32 * dt + tro;
+          dv[dt] = mfma32<DT>(lds_tr<C>(Ds + off), pk[c], dv[dt]);
+          dk[dt] = mfma32<DT>(lds_tr<C>(Qs + off), sk[c], dk[dt]);
         }
     }
   };
@@ -270,8 +304,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a) {
   auto load = [&](int qt, auto stage) {
     constexpr bool S1 = decltype(stage)::value;
     const int64_t r0 = (int64_t)qt * BQ;
-    copy_tile<D, PAD>(qg + r0 * rs, rs, Lq - (int)r0, S1 ? sq1 : sq0, wave, lane);
-    copy_tile<D, PAD>(dog + r0 * rs, rs, Lq - (int)r0, S1 ? sd1 : sd0, wave, lane);
+    copy_tile<C>(qg + r0 * rs, rs, Lq - (int)r0, S1 ? sq1 : sq0, wave, lane);
+    copy_tile<C>(dog + r0 * rs, rs, Lq - (int)r0, S1 ? sd1 : sd0, wave, lane);
     copy_vec(qt, S1 ? sv1 : sv0);
   };
   constexpr std::integral_constant<bool, false> T0{};
@@ -304,9 +338,9 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(BwdArgs a) {
 template <int D, int DT, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a) {
   // K tiles are read as rows and transposed, V tiles as rows only
-  using CK = BwdCfg<D, kTrPad<D>>;
-  using CV = BwdCfg<D, 1>;
-  constexpr int P = CK::P, PV = CV::P, BQ = 128, BC = 64;
+  using CK = BwdTile<D, kTrPad>;
+  using CV = BwdTile<D, 1>;
+  constexpr int BQ = 128, BC = 64;
   __shared__ __attribute__((aligned(16))) uint16_t sk0[CK::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sk1[CK::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sv0[CV::TILE];
@@ -351,7 +385,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[dt][r] = 0.f;
   const f32x16 zero16 = {};
-  const int tro = tr_offset(lane, P);
+  const int tro = tr_offset<CK>(lane);
 
   auto compute = [&](int j, auto stage) {
     const int key0 = j * BC;
@@ -362,8 +396,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int tt = 0; tt < BC / 32; ++tt) {
       f32x16 s = zero16, dp = zero16;
-      const uint16_t* kr = Ks + (32 * tt + swz23(l32)) * P + 8 * hh;
-      const uint16_t* vr = Vs + (32 * tt + swz23(l32)) * PV + 8 * hh;
+      const uint16_t* kr = Ks + CK::row(32 * tt + swz23(l32)) + 8 * hh;
+      const uint16_t* vr = Vs + CV::row(32 * tt + swz23(l32)) + 8 * hh;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         s = mfma32<DT>(lds16(kr + 16 * kk), qf[kk], s);
@@ -385,7 +419,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a) {
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
-          dq[dt] = mfma32<DT>(lds_tr(Ks + (32 * tt + 16 * c) * P + 32 * dt + tro, P), dsk[c], dq[dt]);
+          dq[dt] = mfma32<DT>(lds_tr<CK>(Ks + CK::row(32 * tt + 16 * c) + 32 * dt + tro), dsk[c], dq[dt]);
     }
   };
 
@@ -397,8 +431,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdArgs a) {
   auto load = [&](int j, auto stage) {
     constexpr bool S1 = decltype(stage)::value;
     const int64_t r0 = (int64_t)j * BC;
-    copy_tile<D, kTrPad<D>>(kg + r0 * rs, rs, Lk - (int)r0, S1 ? sk1 : sk0, wave, lane);
-    copy_tile<D, 1>(vg + r0 * rs, rs, Lk - (int)r0, S1 ? sv1 : sv0, wave, lane);
+    copy_tile<CK>(kg + r0 * rs, rs, Lk - (int)r0, S1 ? sk1 : sk0, wave, lane);
+    copy_tile<CV>(vg + r0 * rs, rs, Lk - (int)r0, S1 ? sv1 : sv0, wave, lane);
   };
   constexpr std::integral_constant<bool, false> T0{};
   constexpr std::integral_constant<bool, true> T1{};
