@@ -125,7 +125,7 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // (or head-dim row d) at LDS row swz(k) and reading row m = lane % 32 makes
 // accumulator register r of lane half hh correspond to index
 // 16*(r/8) + 8*hh + r%8, i.e. runs of 8 consecutive keys (or d) per lane.
-__device__ __forceinline__ int swz23(int m) {
+__host__ __device__ constexpr int swz23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 

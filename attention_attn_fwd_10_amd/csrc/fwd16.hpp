@@ -78,11 +78,82 @@ struct Fwd16Cfg {
   // each wave copies CPR / NW instructions of each of K and V per tile
   static_assert(CPR % NW == 0, "the copy instructions of a tile are dealt evenly to the waves");
   static constexpr int CI_W = CPR / NW;
+  // copy round ii of a wave is tile instruction wave + NW * ii; lane l copies
+  // 16-byte chunk copy_chunk(l) of LDS row copy_row(wave, ii, l) to element
+  // (wave + NW * ii) * GRP + 8 l of the stage
+  static constexpr int copy_row(int wave, int ii, int lane) { return wave + NW * ii + CPR * (lane / CPR); }
+  static constexpr int copy_chunk(int lane) { return lane % CPR; }
+  // key held by LDS row r of a K tile (each 32-row group in swz23 order); V
+  // row r holds key r
+  static constexpr int k_key(int r) { return (r & ~31) | swz23(r & 31); }
   // waves per SIMD: two at head dims up to 128 (one workgroup of 8 waves or
   // two of 4 per CU), one at 256
   static constexpr int WAVES_PER_EU = D <= 128 ? 2 : 1;
   static constexpr int MIN_BLOCKS = WAVES_PER_EU * 4 / NW;
 };
+
+// Compile-time check of a tile layout against the kernel's addressing:
+//  * the copies (every wave, round and lane) fill each element of the tile's
+//    64 rows exactly once, inside the stage, at row(R) + column;
+//  * a round's key is the round-0 key plus the compile-time shift the copies
+//    add (k_key(NW ii) for K, NW ii for V);
+//  * the K operand reads (row 32 tt + swz23(l), 8 elements at 16 kk + 8 hh)
+//    find key 32 tt + swz23(l), and the 16 rows of 16 consecutive lanes start
+//    in 16 distinct 16-byte bank groups (of 256 bytes);
+//  * the transposing V reads of 32 lanes touch 32 distinct 8-byte pieces of
+//    the 256 bytes of banks.
+template <class C>
+constexpr bool fwd16_layout_ok() {
+  constexpr int D = C::CPR * 8;
+  bool kseen[C::K_ELEMS / 8] = {}, vseen[C::V_ELEMS / 8] = {};
+  int kkey[C::K_ELEMS / 8] = {}, vkey[C::V_ELEMS / 8] = {};
+  for (int w = 0; w < C::BR / 32; ++w)
+    for (int ii = 0; ii < C::CI_W; ++ii)
+      for (int l = 0; l < 64; ++l) {
+        const int r = C::copy_row(w, ii, l), ch = C::copy_chunk(l);
+        const int kd = (w + (C::BR / 32) * ii) * C::KGRP + 8 * l, vd = (w + (C::BR / 32) * ii) * C::VGRP + 8 * l;
+        if (r < 0 || r >= 64 || kd + 8 > C::K_ELEMS || vd + 8 > C::V_ELEMS) return false;
+        if (kd != C::krow(r) + 8 * ch || vd != C::vrow(r) + 8 * ch) return false;
+        if (kseen[kd / 8] || vseen[vd / 8]) return false;
+        kseen[kd / 8] = vseen[vd / 8] = true;
+        kkey[kd / 8] = C::k_key(r) * 64 + ch;
+        vkey[vd / 8] = r * 64 + ch;
+        if (C::k_key(r) != C::k_key(C::copy_row(w, 0, l)) + C::k_key((C::BR / 32) * ii)) return false;
+        if (r != C::copy_row(w, 0, l) + (C::BR / 32) * ii) return false;
+      }
+  for (int l = 0; l < 64; ++l)
+    for (int tt = 0; tt < 2; ++tt)
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const int e = C::krow(32 * tt + l % 32) + 8 * (l / 32) + 16 * kk;
+        if (e % 8 || !kseen[e / 8] || kkey[e / 8] != (32 * tt + swz23(l % 32)) * 64 + 2 * kk + l / 32) return false;
+      }
+  for (int tt = 0; tt < 2; ++tt)
+    for (int hh = 0; hh < 2; ++hh)
+      for (int kk = 0; kk < D / 16; ++kk) {
+        unsigned seen = 0;
+        for (int l = 0; l < 16; ++l) seen |= 1u << (((C::krow(32 * tt + l) + 8 * hh + 16 * kk) * 2 / 16) % 16);
+        if (seen != 0xffffu) return false;
+      }
+  for (int half = 0; half < 2; ++half)
+    for (int hi = 0; hi < 2; ++hi)
+      for (int c = 0; c < 4; ++c)
+        for (int dt = 0; dt < D / 32; ++dt) {
+          unsigned seen = 0;
+          for (int l = 32 * half; l < 32 * half + 32; ++l) {
+            const int g = l >> 4, j = l & 15;
+            const int row = 8 * (g >> 1) + (j >> 2) + 16 * c + 4 * hi;
+            const int col = 32 * dt + 16 * (g & 1) + 4 * (((j & 1) << 1) | ((j >> 1) & 1));
+            const int e = C::vrow(row) + col;
+            if (!vseen[e / 8] || vkey[e / 8] != row * 64 + col / 8) return false;
+            seen |= 1u << ((e * 2 / 8) % 32);
+          }
+          if (seen != 0xffffffffu) return false;
+        }
+  return true;
+}
+static_assert(fwd16_layout_ok<Fwd16Cfg<64, 4>>() && fwd16_layout_ok<Fwd16Cfg<64, 8>>(), "fwd16 tile layout, head dim 64");
+static_assert(fwd16_layout_ok<Fwd16Cfg<128, 4>>() && fwd16_layout_ok<Fwd16Cfg<128, 8>>(), "fwd16 tile layout, head dim 128");
+static_assert(fwd16_layout_ok<Fwd16Cfg<256, 4>>(), "fwd16 tile layout, head dim 256");
 
 // Probabilities may grow to 2^kLazyRescale before the running max is moved.
 constexpr float kLazyRescale = 8.0f;
@@ -225,20 +296,19 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   // the key and 16-byte chunk this lane copies in its copy round ii (wave
   // instruction wave + NW * ii of the tile)
   auto k_slot = [&](int ii, int& key_local, int& chunk) {
-    const int r = wave + NW * ii + CPR * (lane / CPR);
-    chunk = lane % CPR;
-    key_local = (r & ~31) | swz23(r & 31);
+    key_local = C::k_key(C::copy_row(wave, ii, lane));
+    chunk = C::copy_chunk(lane);
   };
   auto v_slot = [&](int ii, int& key_local, int& chunk) {
-    key_local = wave + NW * ii + CPR * (lane / CPR);
-    chunk = lane % CPR;
+    key_local = C::copy_row(wave, ii, lane);
+    chunk = C::copy_chunk(lane);
   };
   // From one round to the next only the instruction index moves, by NW, in
   // index bits that no other term of the row uses; the key therefore moves by
   // a compile-time amount (swz23(NW * ii) for K, NW * ii for V) and the lane's
   // byte offset inside the tile is that of round 0 plus a scalar, so one
   // register per operand holds the offsets of every round.
-  auto k_key_shift = [](int ii) { return swz23(NW * ii); };
+  auto k_key_shift = [](int ii) { return C::k_key(NW * ii); };
   auto v_key_shift = [](int ii) { return NW * ii; };
   uint32_t k_boff, v_boff;
   {
