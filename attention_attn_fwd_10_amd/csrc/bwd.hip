@@ -122,7 +122,7 @@ __device__ __forceinline__ u32x4 lds16(const uint16_t* p) { return *(const u32x4
 // C: two transposing reads give this lane X[k0 + 8(l/32) + e][m0 + l%32],
 // e = 0..7, when p = X + C::row(k0) + m0 + tr_offset<C>(lane).
 template <class C>
-__device__ __forceinline__ int tr_offset(int lane) {
+__host__ __device__ constexpr int tr_offset(int lane) {
   const int g = lane >> 4, j = lane & 15;
   return C::row(8 * (g >> 1) + (j >> 2)) + 16 * (g & 1) + 4 * (j & 3);
 }
@@ -131,6 +131,61 @@ __device__ __forceinline__ u32x4 lds_tr(const uint16_t* p) {
   const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + C::row(4));
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
+
+// Compile-time check of the grouped tile against the kernels' addressing: the
+// copies (every wave, round and lane) fill each element of the 64 rows once,
+// at row(R) + column; the row reads (row 32 st + swz23(l), 8 elements at
+// 16 kk + 8 hh) find their rows and start the 16 rows of 16 lanes in 16
+// distinct 16-byte bank groups; the transposing reads (tr_offset) find
+// theirs and touch 32 distinct 8-byte pieces of the 256 bytes of banks per
+// 32 lanes.
+template <class C>
+constexpr bool bwd_grouped_ok() {
+  constexpr int D = C::CPR * 8;
+  bool seen[C::TILE / 8] = {};
+  int key[C::TILE / 8] = {};
+  for (int w = 0; w < 4; ++w)
+    for (int ii = 0; ii < C::CPR / 4; ++ii)
+      for (int l = 0; l < 64; ++l) {
+        const int r = w + 4 * ii + 16 * (l >> 4), ch = l & 15;
+        const int d = C::row(w) + C::row(4 * ii) + 8 * l;
+        if (d + 8 > C::TILE || d != C::row(r) + 8 * ch || seen[d / 8]) return false;
+        seen[d / 8] = true;
+        key[d / 8] = r * 16 + ch;
+      }
+  for (int l = 0; l < 64; ++l)
+    for (int st = 0; st < 2; ++st)
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const int r = 32 * st + swz23(l % 32);
+        const int e = C::row(r) + 8 * (l / 32) + 16 * kk;
+        if (e % 8 || key[e / 8] != r * 16 + 2 * kk + l / 32) return false;
+      }
+  for (int st = 0; st < 2; ++st)
+    for (int hh = 0; hh < 2; ++hh)
+      for (int kk = 0; kk < D / 16; ++kk) {
+        unsigned g16 = 0;
+        for (int l = 0; l < 16; ++l) g16 |= 1u << (((C::row(32 * st + swz23(l)) + 8 * hh + 16 * kk) * 2 / 16) % 16);
+        if (g16 != 0xffffu) return false;
+      }
+  for (int half = 0; half < 2; ++half)
+    for (int st = 0; st < 2; ++st)
+      for (int c = 0; c < 2; ++c)
+        for (int dt = 0; dt < D / 32; ++dt)
+          for (int hi = 0; hi < 2; ++hi) {
+            unsigned pieces = 0;
+            for (int l = 32 * half; l < 32 * half + 32; ++l) {
+              const int g = l >> 4, j = l & 15;
+              const int r = 8 * (g >> 1) + (j >> 2) + 32 * st + 16 * c + 4 * hi;
+              const int col = 32 * dt + 16 * (g & 1) + 4 * (j & 3);
+              const int e = tr_offset<C>(l) + C::row(32 * st + 16 * c) + 32 * dt + (hi ? C::row(4) : 0);
+              if (key[e / 8] != r * 16 + col / 8 || e % 8 != col % 8) return false;
+              pieces |= 1u << ((e * 2 / 8) % 32);
+            }
+            if (pieces != 0xffffffffu) return false;
+          }
+  return true;
+}
+static_assert(bwd_grouped_ok<BwdGrp<128>>(), "grouped backward tile layout");
 
 template <int DT>
 __device__ __forceinline__ u32x4 pack8(const float* x) {

@@ -59,8 +59,75 @@ constexpr int V_BYTES = CPR * VGRP;
 constexpr int CI_W = CPR / 4;      // copy instructions per wave per tile and operand
 constexpr int krow(int r) { return (r % CPR) * KGRP + (r / CPR) * D; }
 constexpr int vrow(int r) { return (r % CPR) * VGRP + (r / CPR) * D; }
+// LDS row R of a K tile holds key 32((m>>2)&1) + 16(R/32) + 4(m>>3) + (m&3),
+// m = R % 32: then score register r of tile tt in lane half hh belongs to key
+// 32hh + 16tt + r, so each lane's 32 probabilities are 32 consecutive keys.
+// V row R holds key R.
+constexpr int k_row_key(int R) {
+  return 32 * (((R & 31) >> 2) & 1) + 16 * (R >> 5) + 4 * ((R & 31) >> 3) + (R & 3);
+}
+// copy round ii of wave w is tile instruction w + 4 ii; lane l copies chunk
+// copy_chunk(l) of LDS row copy_row(w, ii, l) to byte (w + 4 ii) * GRP + 16 l
+constexpr int copy_row(int w, int ii, int l) { return w + 4 * ii + CPR * (l / CPR); }
+constexpr int copy_chunk(int l) { return l % CPR; }
 constexpr float kMu = 6.0f;        // probabilities are quantised as p * 2^kMu
 constexpr float kTau = 2.0f;       // the running max may lag by 2^kTau
+
+// Compile-time check of the tile layout against the kernel's addressing: the
+// copies fill each byte of the 64 rows once, at row(R) + column; a round's
+// key is the round-0 key plus the shift the copies add; the K reads (both
+// operand layouts) find their keys and start 16 rows of 16 lanes in 16
+// distinct 16-byte bank groups; the transposing V reads of 32 lanes touch 32
+// distinct 8-byte pieces of the 256 bytes of banks.
+constexpr bool layout_ok() {
+  bool kseen[K_BYTES / 16] = {}, vseen[V_BYTES / 16] = {};
+  int kkey[K_BYTES / 16] = {}, vkey[V_BYTES / 16] = {};
+  for (int w = 0; w < 4; ++w)
+    for (int ii = 0; ii < CI_W; ++ii)
+      for (int l = 0; l < 64; ++l) {
+        const int r = copy_row(w, ii, l), ch = copy_chunk(l);
+        const int kd = (w + 4 * ii) * KGRP + 16 * l, vd = (w + 4 * ii) * VGRP + 16 * l;
+        if (r >= 64 || kd + 16 > K_BYTES || vd + 16 > V_BYTES) return false;
+        if (kd != krow(r) + 16 * ch || vd != vrow(r) + 16 * ch || kseen[kd / 16] || vseen[vd / 16]) return false;
+        kseen[kd / 16] = vseen[vd / 16] = true;
+        kkey[kd / 16] = k_row_key(r) * 8 + ch;
+        vkey[vd / 16] = r * 8 + ch;
+        if (k_row_key(r) != k_row_key(copy_row(w, 0, l)) + k_row_key(4 * ii)) return false;
+      }
+  for (int i8 = 0; i8 < 2; ++i8) {
+    const int hs = i8 ? 16 : 32, sec = i8 ? 32 : 16;
+    for (int l = 0; l < 64; ++l)
+      for (int tt = 0; tt < 2; ++tt)
+        for (int kk = 0; kk < 2; ++kk)
+          for (int x = 0; x <= sec; x += sec) {
+            const int b = krow(l % 32) + hs * (l / 32) + krow(32 * tt) + 64 * kk + x;
+            const int colb = 64 * kk + hs * (l / 32) + x;
+            if (b % 16 || kkey[b / 16] != k_row_key(32 * tt + l % 32) * 8 + colb / 16) return false;
+          }
+    for (int tt = 0; tt < 2; ++tt)
+      for (int hh = 0; hh < 2; ++hh)
+        for (int kk = 0; kk < 2; ++kk) {
+          unsigned seen = 0;
+          for (int l = 0; l < 16; ++l) seen |= 1u << (((krow(32 * tt + l) + hs * hh + 64 * kk) / 16) % 16);
+          if (seen != 0xffffu) return false;
+        }
+  }
+  for (int half = 0; half < 2; ++half)
+    for (int u = 0; u < 4; ++u)
+      for (int dt = 0; dt < D / 32; ++dt) {
+        unsigned seen = 0;
+        for (int l = 32 * half; l < 32 * half + 32; ++l) {
+          const int g = l >> 4, j = l & 15;
+          const int row = 32 * (g >> 1) + (j >> 1) + 8 * u, col = 32 * dt + 16 * (g & 1) + 8 * (j & 1);
+          const int b = vrow(32 * (g >> 1) + (j >> 1)) + 16 * (g & 1) + 8 * (j & 1) + vrow(8 * u) + 32 * dt;
+          if (vkey[b / 16] != row * 8 + col / 16 || b % 16 != col % 16) return false;
+          seen |= 1u << ((b / 8) % 32);
+        }
+        if (seen != 0xffffffffu) return false;
+      }
+  return true;
+}
+static_assert(layout_ok(), "8-bit forward tile layout");
 }  // namespace fp8cfg
 
 // two floats -> two e4m3 bytes (nearest-even; values above 464 would become NaN)
@@ -161,13 +228,6 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
   }
 
   // ---- asynchronous tile copies ----------------------------------------------
-  // LDS row R of a K tile holds key 32((m>>2)&1) + 16(R/32) + 4(m>>3) + (m&3),
-  // m = R % 32: then score register r of tile tt in lane half hh belongs to key
-  // 32hh + 16tt + r, so each lane's 32 probabilities are 32 consecutive keys.
-  auto k_row_key = [](int R) {
-    const int m = R & 31;
-    return 32 * ((m >> 2) & 1) + 16 * (R >> 5) + 4 * (m >> 3) + (m & 3);
-  };
   const uint8_t* const kg = a.k + koff;
   const uint8_t* const vg = a.v + koff;
   // Byte offsets of this lane's copy in round 0 (wave instruction `wave`).
@@ -176,7 +236,7 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
   // each round's offset is the round-0 offset plus a scalar.
   uint32_t k_boff, v_boff;
   {
-    const int R = wave + CPR * (lane / CPR), c = lane % CPR;
+    const int R = copy_row(wave, 0, lane), c = copy_chunk(lane);
     k_boff = (uint32_t)(k_row_key(R) * (int)row_q + 16 * c);
     v_boff = (uint32_t)(R * (int)row_q + 16 * c);
   }
