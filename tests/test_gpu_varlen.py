@@ -108,12 +108,15 @@ def test_varlen_paged_workload(lib):
     assert_close16(og, o_ref, lg, lse_ref, "varlen+paged workload")
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("page", [16, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_varlen_equals_dense_per_sequence(lib, page, causal):
+def test_varlen_equals_dense_per_sequence(lib, page, causal, d):
+    # every head dim through both tile-copy paths (pages of 16 tokens: one row
+    # at a time through the table; 64 and 128: whole tiles)
     import torch
     lens = np.array([1, 130, 0, 77, 64, 300, 129], dtype=np.int64)
-    H, D = 3, 128
+    H, D = 3, d
     q, k, v, cu_q, cu_k = _pack(lens, lens, H, D, 5)
     o_pk, lse_pk = _run(lib, q, k, v, cu_q, cu_k, lens, lens, causal)
     kp, vp, table = _paginate(k, v, cu_k, lens, page, 8)
