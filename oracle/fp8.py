@@ -79,10 +79,12 @@ def e4m3_encode(x) -> np.ndarray:
 
 
 def e4m3_ulp(x) -> np.ndarray:
-    """Spacing of e4m3 values at magnitude |x| (for tolerance statements)."""
+    """Spacing of e4m3 values at magnitude |x| (for tolerance statements):
+    2^(e-3) in the binade [2^e, 2^(e+1)) for e >= -6, and the subnormal
+    spacing 2^-9 below 2^-6, zero included."""
     a = np.abs(np.asarray(x, dtype=np.float64))
     with np.errstate(divide="ignore"):
-        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+        e = np.floor(np.log2(np.where(a > 0, a, 2.0 ** -9)))
     e = np.maximum(e, -6.0)
     return np.exp2(e - 3.0)
 

@@ -155,3 +155,48 @@ def test_emulation_prediction_block_rotation_beats_per_tensor():
     r_blk, r_pt = F.rmse(blk, ref), F.rmse(pt, ref)
     assert r_blk < r_pt
     assert r_blk < 1.2e-2
+
+
+def test_rmse_golden():
+    """The pass measure of the 8-bit configs, against hand-derived values."""
+    with open(os.path.join(GOLDEN, "oracle_measures.json")) as f:
+        g = json.load(f)
+    for c in g["rmse"]:
+        assert F.rmse(np.array(c["a"], float), np.array(c["b"], float)) == pytest.approx(c["value"], abs=1e-15), c
+        assert F.rmse(np.array(c["b"], float), np.array(c["a"], float)) == pytest.approx(c["value"], abs=1e-15), c
+
+
+def test_e4m3_ulp_golden():
+    with open(os.path.join(GOLDEN, "oracle_measures.json")) as f:
+        g = json.load(f)
+    for c in g["e4m3_ulp"]:
+        assert float(F.e4m3_ulp(np.float64(c["x"]))) == c["value"], c
+
+
+def test_e4m3_ulp_is_the_spacing_of_adjacent_codes():
+    """For every non-negative finite code but the largest, the step to the next
+    code (decoded by the codec pinned above) is e4m3_ulp of the code's value."""
+    codes = np.arange(0, 126, dtype=np.uint8)
+    lo = F.e4m3_decode(codes)
+    hi = F.e4m3_decode(codes + 1)
+    assert np.array_equal(hi - lo, F.e4m3_ulp(lo))
+    assert np.array_equal(F.e4m3_ulp(-lo), F.e4m3_ulp(lo))
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp16"])
+def test_half_ulp_of_16bit_outputs(fmt):
+    """The rounding allowance of the 16-bit parity tests: twice half_ulp(x) is
+    the step from x to the next representable value, for values across the
+    normal range of each format (bit patterns stepped by one)."""
+    from tests.parity import half_ulp
+    rng = np.random.default_rng(3)
+    if fmt == "bf16":
+        bits = rng.integers(0x0080, 0x7F7F, size=5000).astype(np.uint32)
+        x = (bits << 16).view(np.float32).astype(np.float64)
+        nxt = ((bits + 1) << 16).view(np.float32).astype(np.float64)
+    else:
+        bits = rng.integers(0x0400, 0x7BFF, size=5000).astype(np.uint16)
+        x = bits.view(np.float16).astype(np.float64)
+        nxt = (bits + 1).astype(np.uint16).view(np.float16).astype(np.float64)
+    assert np.array_equal(2 * half_ulp(x, fmt), nxt - x)
+    assert half_ulp(1.0, fmt) == (2.0 ** -8 if fmt == "bf16" else 2.0 ** -11)
