@@ -134,6 +134,21 @@ def _require_cuda(*ts):
             raise ValueError("all tensors must live on the GPU")
 
 
+def _require(t, name, shape, dtype, contiguous=True):
+    """The C ABI sees only pointers: a tensor of another shape, dtype or
+    layout would be misread on the device, so it is refused here."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _scale_shape(B, H, S, block_rows):
+    return (B, H, (S + 127) // 128) if block_rows else (1,)
+
+
 def fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None, return_lse=True, stream=None):
     """Fused attention forward.  q [B, Sq, H, D], k/v [B, Sk, H, D] (bf16 or
     fp16, head_dim contiguous).  Returns (o [B, Sq, H, D], lse [B, H, Sq] fp32)."""
@@ -149,10 +164,12 @@ def fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None, return_ls
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format) if not q.is_contiguous() \
             else torch.empty_like(q)
+    else:
+        _require(out, "out", (B, Sq, H, D), q.dtype, contiguous=False)
     if lse is None and return_lse:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (B, H, Sq)):
-        raise ValueError("lse must be contiguous float32 [B, H, Sq]")
+    if lse is not None:
+        _require(lse, "lse", (B, H, Sq), torch.float32)
     _check(_lib.attn_fwd(_dtype_code(q.dtype), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
                          _ptr(out), _strides(out), _ptr(lse), B, H, Sq, Sk, D, scale, int(bool(causal)),
                          _stream(stream)))
@@ -193,8 +210,12 @@ def fwd_bias(q, k, v, bias, softmax_scale=None, causal=False, out=None, lse=None
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format) if not q.is_contiguous() \
             else torch.empty_like(q)
+    else:
+        _require(out, "out", (B, Sq, H, D), q.dtype, contiguous=False)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    else:
+        _require(lse, "lse", (B, H, Sq), torch.float32)
     _check(_lib.attn_fwd_bias(_dtype_code(q.dtype), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
                               _strides(v), _ptr(bias), (ctypes.c_int64 * 3)(*bst), _ptr(out), _strides(out),
                               _ptr(lse), B, H, Sq, Sk, D, scale, int(bool(causal)), _stream(stream)))
@@ -212,8 +233,9 @@ def _quantize(fn, code_dtype, x, block_rows, signs, out, scales, stream):
     elif out.dtype != code_dtype or not out.is_contiguous() or out.shape != x.shape:
         raise ValueError(f"out must be a contiguous {code_dtype} tensor shaped like x")
     if scales is None:
-        shape = (B, H, (S + 127) // 128) if block_rows else (1,)
-        scales = torch.empty(shape, dtype=torch.float32, device=x.device)
+        scales = torch.empty(_scale_shape(B, H, S, block_rows), dtype=torch.float32, device=x.device)
+    else:
+        _require(scales, "scales", _scale_shape(B, H, S, block_rows), torch.float32)
     if signs is not None and (signs.dtype != torch.int8 or signs.numel() != D):
         raise ValueError("signs must be int8 [D]")
     _check(fn(_ptr(x), _strides(x), _ptr(out), _ptr(scales), B, H, S, D, int(block_rows), _ptr(signs),
@@ -237,6 +259,27 @@ def int8_quantize(x, block_rows=128, signs=None, out=None, scales=None, stream=N
     return _quantize(_lib.attn_int8_quantize, torch.int8, x, block_rows, signs, out, scales, stream)
 
 
+def _check_8bit(q8, q_scale, k8, k_scale, v8, v_scale, block_rows, out, lse, qk_dtype):
+    """Shapes, dtypes and layouts of the 8-bit forward's operands: q8 and k8
+    codes of qk_dtype, v8 e4m3 codes (uint8), all contiguous [B, S, H, D];
+    float32 scales [B, H, ceil(S/128)] (block_rows 128) or [1] (0)."""
+    import torch
+    if block_rows not in (0, 128):
+        raise ValueError("block_rows must be 128 or 0")
+    B, Sq, H, D = q8.shape
+    Sk = k8.shape[1]
+    _require(q8, "q8", (B, Sq, H, D), qk_dtype)
+    _require(k8, "k8", (B, Sk, H, D), qk_dtype)
+    _require(v8, "v8", (B, Sk, H, D), torch.uint8)
+    _require(q_scale, "q_scale", _scale_shape(B, H, Sq, block_rows), torch.float32)
+    _require(k_scale, "k_scale", _scale_shape(B, H, Sk, block_rows), torch.float32)
+    _require(v_scale, "v_scale", _scale_shape(B, H, Sk, block_rows), torch.float32)
+    if out is not None:
+        _require(out, "out", (B, Sq, H, D), torch.bfloat16)
+    if lse is not None:
+        _require(lse, "lse", (B, H, Sq), torch.float32)
+
+
 def fwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, block_rows=128, softmax_scale=None, causal=False,
             out=None, lse=None, stream=None):
     """8-bit fused forward on e4m3 codes (uint8 [B, S, H, D], contiguous) and
@@ -245,9 +288,7 @@ def fwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, block_rows=128, softmax_scale
     _require_cuda(q8, q_scale, k8, k_scale, v8, v_scale, out, lse)
     B, Sq, H, D = q8.shape
     Sk = k8.shape[1]
-    for t in (q8, k8, v8):
-        if t.dtype != torch.uint8 or not t.is_contiguous():
-            raise ValueError("q8, k8, v8 must be contiguous uint8 e4m3 codes")
+    _check_8bit(q8, q_scale, k8, k_scale, v8, v_scale, block_rows, out, lse, torch.uint8)
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     if out is None:
         out = torch.empty((B, Sq, H, D), dtype=torch.bfloat16, device=q8.device)
@@ -268,9 +309,7 @@ def fwd_int8(q8, q_scale, k8, k_scale, v8, v_scale, block_rows=128, softmax_scal
     _require_cuda(q8, q_scale, k8, k_scale, v8, v_scale, out, lse)
     B, Sq, H, D = q8.shape
     Sk = k8.shape[1]
-    for t, dt in ((q8, torch.int8), (k8, torch.int8), (v8, torch.uint8)):
-        if t.dtype != dt or not t.is_contiguous():
-            raise ValueError("q8, k8 must be contiguous int8 codes and v8 contiguous uint8 e4m3 codes")
+    _check_8bit(q8, q_scale, k8, k_scale, v8, v_scale, block_rows, out, lse, torch.int8)
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     if out is None:
         out = torch.empty((B, Sq, H, D), dtype=torch.bfloat16, device=q8.device)
@@ -282,6 +321,44 @@ def fwd_int8(q8, q_scale, k8, k_scale, v8, v_scale, block_rows=128, softmax_scal
     return out, lse
 
 
+def _check_varlen(q, cu_seqlens_q, k, v, cu_seqlens_k, block_table, page_size, out, lse):
+    """Operands of the packed / paged forward: q [total_q, H, D]; k, v of q's
+    dtype, packed [total_k, H, D] or paged [num_pages, page_size, H, D]; int32
+    cu_seqlens [B+1] and block table [B, max_pages]; out and lse shaped like
+    the results.  Returns B and max_pages."""
+    import torch
+    total_q, H, D = q.shape
+    B = cu_seqlens_q.numel() - 1
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("varlen tensors must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share a dtype")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    for t in (cu_seqlens_q, cu_seqlens_k):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+            raise TypeError("cu_seqlens must be contiguous 1-d int32")
+    if cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have B + 1 entries")
+    max_pages = 0
+    if block_table is not None:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
+            raise ValueError("block_table must be contiguous int32 [B, max_pages]")
+        if block_table.shape[0] != B:
+            raise ValueError("block_table must have one row per sequence")
+        max_pages = block_table.shape[1]
+        if k.dim() != 4 or k.shape[1] != page_size or tuple(k.shape[2:]) != (H, D):
+            raise ValueError("paged k/v must be [num_pages, page_size, H, D]")
+    elif k.dim() != 3 or tuple(k.shape[1:]) != (H, D):
+        raise ValueError("packed k/v must be [total_k, H, D]")
+    if out is not None:
+        _require(out, "out", (total_q, H, D), q.dtype)
+    if lse is not None:
+        _require(lse, "lse", (H, total_q), torch.float32)
+    return B, max_pages
+
+
 def fwd_varlen(q, cu_seqlens_q, k, v, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale=None,
                causal=False, block_table=None, page_size=0, out=None, lse=None, stream=None):
     """Packed variable-length forward.  q [total_q, H, D]; cu_seqlens int32
@@ -291,20 +368,7 @@ def fwd_varlen(q, cu_seqlens_q, k, v, cu_seqlens_k, max_seqlen_q, max_seqlen_k, 
     import torch
     _require_cuda(q, cu_seqlens_q, k, v, cu_seqlens_k, block_table, out, lse)
     total_q, H, D = q.shape
-    B = cu_seqlens_q.numel() - 1
-    for t in (q, k, v):
-        if not t.is_contiguous():
-            raise ValueError("varlen tensors must be contiguous")
-    for t in (cu_seqlens_q, cu_seqlens_k):
-        if t.dtype != torch.int32:
-            raise TypeError("cu_seqlens must be int32")
-    max_pages = 0
-    if block_table is not None:
-        if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
-            raise ValueError("block_table must be contiguous int32 [B, max_pages]")
-        max_pages = block_table.shape[1]
-        if k.shape[1] != page_size:
-            raise ValueError("paged k/v must be [num_pages, page_size, H, D]")
+    B, max_pages = _check_varlen(q, cu_seqlens_q, k, v, cu_seqlens_k, block_table, page_size, out, lse)
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     if out is None:
         out = torch.empty_like(q)
@@ -342,20 +406,7 @@ def fwd_splitkv(q, cu_seqlens_q, k, v, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
     import torch
     _require_cuda(q, cu_seqlens_q, k, v, cu_seqlens_k, block_table, out, lse, workspace)
     total_q, H, D = q.shape
-    B = cu_seqlens_q.numel() - 1
-    for t in (q, k, v):
-        if not t.is_contiguous():
-            raise ValueError("varlen tensors must be contiguous")
-    for t in (cu_seqlens_q, cu_seqlens_k):
-        if t.dtype != torch.int32:
-            raise TypeError("cu_seqlens must be int32")
-    max_pages = 0
-    if block_table is not None:
-        if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
-            raise ValueError("block_table must be contiguous int32 [B, max_pages]")
-        max_pages = block_table.shape[1]
-        if k.shape[1] != page_size:
-            raise ValueError("paged k/v must be [num_pages, page_size, H, D]")
+    B, max_pages = _check_varlen(q, cu_seqlens_q, k, v, cu_seqlens_k, block_table, page_size, out, lse)
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     if num_splits is None:
         n_work = H * (-(-int(total_q) // 128) + B)
@@ -396,6 +447,9 @@ def bwd(q, k, v, o, lse, dout, softmax_scale=None, causal=False, dq=None, dk=Non
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _require(dq, "dq", q.shape, q.dtype)
+    _require(dk, "dk", k.shape, q.dtype)
+    _require(dv, "dv", v.shape, q.dtype)
     if workspace is None:
         workspace = torch.empty((2, B, H, Sq), dtype=torch.float32, device=q.device)
     elif workspace.dtype != torch.float32 or workspace.numel() < 2 * B * H * Sq or not workspace.is_contiguous():

@@ -20,8 +20,6 @@
 namespace attn {
 template <int D, int DT, bool CAUSAL, int MODE>
 hipError_t launch_fwd16(FwdArgs a, hipStream_t s);
-template <int D, int DT, bool CAUSAL, int MODE>
-hipError_t launch_fwd16pp(FwdArgs a, hipStream_t s);
 hipError_t launch_fp8_quantize(const QuantArgs& a, int D, hipStream_t s);
 hipError_t launch_splitkv_merge(const MergeArgs& a, int D, int dtype, hipStream_t s);
 hipError_t launch_fwd_fp8(const Fp8Args& a, int D, bool causal, hipStream_t s);
@@ -80,25 +78,8 @@ attn_status_t check_head_dim(int D) {
   return ATTN_OK;
 }
 
-// Schedule of the 16-bit kernels for head_dim 64/128: "pairs" (4 waves, two
-// independent workgroups per CU; the default, measured faster) or "pingpong"
-// (8 waves, two groups alternating matrix and softmax phases).  Read once from
-// ATTN_FWD16_SCHEDULE; head_dim 256 always uses the 4-wave kernel.
-bool use_pingpong() {
-  static const bool pp = [] {
-    const char* e = std::getenv("ATTN_FWD16_SCHEDULE");
-    return e != nullptr && std::strcmp(e, "pingpong") == 0;
-  }();
-  return pp;
-}
-
 template <int D, int DT, bool CAUSAL, int MODE>
 hipError_t launch_one(const attn::FwdArgs& a, hipStream_t s) {
-  if constexpr (D <= 128) {
-    // (the ping-pong kernel has no split-key or bias form)
-    if constexpr (MODE != attn::kDenseBias)
-      if (use_pingpong() && a.n_split <= 1) return attn::launch_fwd16pp<D, DT, CAUSAL, MODE>(a, s);
-  }
   return attn::launch_fwd16<D, DT, CAUSAL, MODE>(a, s);
 }
 

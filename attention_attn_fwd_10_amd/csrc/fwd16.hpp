@@ -521,11 +521,13 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tt][r]);
     const float mxs = halfwave_max(mx) * c2k;
-    // move the running max only when some row's new max exceeds it by > 2^8
+    // move the running max only when some row's new max exceeds it by > 2^8;
+    // the row sum takes alpha in the same fused update as the pipelined tiles
+    // (l = fma(l, alpha, psum)), so every path rounds it identically
+    float alpha = 1.f;
     if (__builtin_amdgcn_ballot_w64(mxs > m_run + kLazyRescale) != 0) {
       const float m_new = fmaxf(m_run, mxs);
-      const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
-      l_run *= alpha;
+      alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -566,7 +568,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
         oacc[dt] = mfma32<DT>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pk, oacc[dt]);
       }
     }
-    l_run += psum;
+    l_run = fmaf(l_run, alpha, psum);
   };
 
   // ---- one key tile in three pieces (head dim 256) ---------------------------
@@ -623,11 +625,13 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
     // move the running max only when some row's new max exceeds it by > 2^8
     return __builtin_amdgcn_ballot_w64(mxs > m_run + kLazyRescale) != 0;
   };
-  // move the running max and rescale the sums and accumulators
+  // move the running max and rescale the accumulators; the row sum takes
+  // alpha in softmax_pv's fused update
+  float alpha_pend = 1.f;
   auto rescale = [&]() {
     const float m_new = fmaxf(m_run, mxs);
     const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
-    l_run *= alpha;
+    alpha_pend = alpha;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -669,7 +673,8 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
         oacc[dt] = mfma32<DT>(u32x4{lo[0], lo[1], hi[0], hi[1]}, pk, oacc[dt]);
       }
     }
-    l_run += psum;
+    l_run = fmaf(l_run, alpha_pend, psum);
+    alpha_pend = 1.f;
   };
 
   // ---- software-pipelined pieces (head dims up to 128, tiles needing no mask)

@@ -1,8 +1,7 @@
 // Instantiations of the 16-bit forward kernels for head_dim 128.
-#include "fwd16_pp.hpp"
+#include "fwd16.hpp"
 
 namespace attn {
 ATTN_INSTANTIATE_FWD16(128)
 ATTN_INSTANTIATE_FWD16_BIAS(128)
-ATTN_INSTANTIATE_FWD16PP(128)
 }  // namespace attn

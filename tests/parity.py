@@ -5,13 +5,19 @@ from __future__ import annotations
 import numpy as np
 
 # 16-bit path: max |O - O_ref| <= 1e-2, RMSE(O) <= 2e-3, max |LSE - LSE_ref| <= 1e-3.
-# The max-abs budget applies to the computed value; the output's own rounding
-# to its 16-bit storage type (half an ulp of the stored value) comes on top,
-# since no 16-bit output can be closer than that to the float64 result (at
-# |O| >= 4 half an ulp of bf16 already exceeds 1e-2).
+# The max-abs bound is asserted twice: literally, on every entry whose
+# reference magnitude is below LITERAL_BELOW, and on all entries for the
+# computed value with the output's own rounding to its 16-bit storage type
+# (half an ulp of the stored value) allowed on top, since no 16-bit output can
+# be closer than that to the float64 result (at |O| >= 4 half an ulp of bf16
+# already exceeds 1e-2).
 MAX_ABS = 1e-2
 RMSE = 2e-3
 LSE_TOL = 1e-3
+# Where the reference output is below this magnitude, half an ulp of the
+# stored value is at most 2^-8 (bf16) and the literal bound max |O - O_ref| <=
+# 1e-2 is attainable, so it is asserted there as stated, with no allowance.
+LITERAL_BELOW = 2.0
 
 
 def half_ulp(x, dtype="bf16"):
@@ -42,7 +48,10 @@ def errors(o, o_ref, lse=None, lse_ref=None, dtype="bf16"):
     sel = ~np.isnan(o_ref)
     d = o[sel] - o_ref[sel]
     beyond = np.abs(d) - half_ulp(o[sel], dtype)
+    small = np.abs(o_ref[sel]) < LITERAL_BELOW
     out = {"max_abs": float(np.abs(d).max()) if d.size else 0.0,
+           "max_abs_where_attainable": float(np.abs(d[small]).max()) if small.any() else 0.0,
+           "frac_attainable": float(small.mean()) if d.size else 1.0,
            "max_abs_beyond_rounding": float(beyond.max()) if d.size else 0.0,
            "rmse": float(np.sqrt(np.mean(d * d))) if d.size else 0.0,
            "nan_in_out": bool(np.isnan(o[sel]).any())}
@@ -57,6 +66,7 @@ def errors(o, o_ref, lse=None, lse_ref=None, dtype="bf16"):
 def assert_close16(o, o_ref, lse=None, lse_ref=None, what="", dtype="bf16"):
     e = errors(o, o_ref, lse, lse_ref, dtype)
     assert not e["nan_in_out"], f"{what}: NaN in output {e}"
+    assert e["max_abs_where_attainable"] <= MAX_ABS, f"{what}: {e}"
     assert e["max_abs_beyond_rounding"] <= MAX_ABS, f"{what}: {e}"
     assert e["rmse"] <= RMSE, f"{what}: {e}"
     if lse is not None:

@@ -178,10 +178,12 @@ def _rows_ref(q, k, v, scale, causal, rows):
 
 
 @pytest.mark.parametrize("d,h", [(64, 32), (128, 16), (256, 8)])
-@pytest.mark.parametrize("s", [512, 2048, 16384])
+@pytest.mark.parametrize("s", [512, 1024, 2048, 4096, 8192, 16384])
 @pytest.mark.parametrize("causal", [False, True])
 def test_seq_sweep_sampled(lib, d, h, s, causal):
-    """16384 tokens per batch, hidden 2048: seq s, batch 16384/s, heads 2048/d."""
+    """16384 tokens per batch, hidden 2048: seq s, batch 16384/s, heads 2048/d.
+    All 36 points of the sweep; s 8192 at d128 (batch 2, 16 heads, non-causal)
+    is the d128 / seq-8k headline point."""
     import torch
     B = 16384 // s
     q, k, v = W.qkv_normal(2000 + s + d, (B, s, h, d))
@@ -192,39 +194,7 @@ def test_seq_sweep_sampled(lib, d, h, s, causal):
     o = o[bsel][:, rows].float().cpu().numpy().astype(np.float64)
     lse = lse[bsel][:, :, rows].cpu().numpy().astype(np.float64)
     o_ref, lse_ref = _rows_ref(q[bsel], k[bsel], v[bsel], 1 / math.sqrt(d), causal, rows)
-    assert_close16(o, o_ref, lse, lse_ref, f"sweep s{s} d{d} causal={causal}")
-
-
-def test_pingpong_schedule_in_child_process(lib):
-    """The opt-in ping-pong schedule (ATTN_FWD16_SCHEDULE=pingpong, read once per
-    process) against the oracle, in a child process: d64 and d128, causal and
-    not, several key tiles and a ragged tail."""
-    import subprocess
-    import sys
-    root = __import__("os").path.dirname(__import__("os").path.dirname(__import__("os").path.abspath(__file__)))
-    code = r'''
-import math, sys
-import numpy as np, torch
-sys.path.insert(0, sys.argv[1])
-import attention_attn_fwd_10_amd as A, workloads as W
-from oracle import attention as OA
-from tests.parity import assert_close16
-for d in (64, 128):
-    for causal in (False, True):
-        q, k, v = W.qkv_normal(900 + d, (2, 300, 2, d), (2, 333, 2, d))
-        dev = [torch.from_numpy(x).to(torch.bfloat16).cuda() for x in (q, k, v)]
-        o, lse = A.fwd(*dev, 1 / math.sqrt(d), causal)
-        torch.cuda.synchronize()
-        o_ref, lse_ref = OA.attention_bshd(q, k, v, 1 / math.sqrt(d), causal)
-        oh = o.float().cpu().numpy().astype(np.float64)
-        lh = lse.cpu().numpy().astype(np.float64)
-        print(d, causal, float(np.abs(oh - o_ref).max()), flush=True)
-        assert_close16(oh, o_ref, lh, lse_ref, f"pingpong d{d} causal={causal}")
-'''
-    env = dict(__import__("os").environ, ATTN_FWD16_SCHEDULE="pingpong")
-    r = subprocess.run([sys.executable, "-c", code, root], env=env, capture_output=True, text=True, timeout=120)
-    print(r.stdout)
-    assert r.returncode == 0, r.stdout + r.stderr
+    print(f"sweep s{s} d{d} causal={causal}:", assert_close16(o, o_ref, lse, lse_ref, f"sweep s{s} d{d} causal={causal}"))
 
 
 @pytest.mark.parametrize("d,h", [(64, 32), (128, 16), (256, 8)])

@@ -196,3 +196,48 @@ def test_partial_blocks_repeatable(lib):
         assert torch.equal(o0, o1) and torch.equal(l0, l1)
         o2, l2 = _run(lib, q, kp, vp, cu_q, cu_k, lens, lens, True, table, 64)
         assert torch.equal(o0, o2) and torch.equal(l0, l2)
+
+
+def _growing_scores(q, k, cu_k, lens_k, d):
+    """Scores that grow by about 12 (natural units, > 2^8 in exp2 terms) from
+    one 64-key tile of a sequence to the next, so the running max moves and the
+    row sum and accumulators are rescaled on every tile."""
+    w = np.zeros(d, dtype=np.float32)
+    w[::2] = 1.0
+    w /= np.linalg.norm(w)
+    q = q + 4.0 * w
+    k = k.copy()
+    for b, n in enumerate(lens_k):
+        tile = (np.arange(int(n)) // 64).astype(np.float32)
+        k[cu_k[b]:cu_k[b] + n] += (3.0 * math.sqrt(d) * tile)[:, None, None] * w
+    return (W.bf16_bits_to_f32(W.bf16_round(x)) for x in (q, k))
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bit_identity_when_running_max_moves(lib, d, causal):
+    """Paged with 16-token pages (every tile one at a time), paged with 64-token
+    pages and packed (unmasked tiles software-pipelined) and per-sequence dense
+    runs (causal: 256-row query blocks at d <= 128, so other tiles take the
+    pipelined path) give bit-identical O and LSE while the running max moves on
+    every tile: every path rescales the row sum with the same fused update."""
+    import torch
+    lens = np.array([1, 130, 77, 300, 129, 520, 64], dtype=np.int64)
+    H = 2
+    q, k, v, cu_q, cu_k = _pack(lens, lens, H, d, 40 + d)
+    q, k = _growing_scores(q, k, cu_k, lens, d)
+    o_pk, lse_pk = _run(lib, q, k, v, cu_q, cu_k, lens, lens, causal)
+    assert float(lse_pk.max()) > 60.0  # the scores really span several moves of the max
+    for page in (16, 64):
+        kp, vp, table = _paginate(k, v, cu_k, lens, page, 41)
+        o_pg, lse_pg = _run(lib, q, kp, vp, cu_q, cu_k, lens, lens, causal, table, page)
+        assert torch.equal(o_pg, o_pk) and torch.equal(lse_pg, lse_pk), page
+    for b, n in enumerate(lens):
+        sl = slice(int(cu_q[b]), int(cu_q[b + 1]))
+        od, ld = lib.fwd(to_dev(q[None, sl]), to_dev(k[None, sl]), to_dev(v[None, sl]), causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(od[0], o_pk[sl]), b
+        assert torch.equal(ld[0], lse_pk[:, sl]), b
+    rows, o_ref, lse_ref = _sample_rows_ref(q, k, v, cu_q, cu_k, lens, lens, causal, heads=[0, 1], seed=43)
+    og, lg = _gather(o_pk, lse_pk, rows)
+    assert_close16(og, o_ref, lg, lse_ref, f"growing scores d{d} causal={causal}")
