@@ -10,6 +10,8 @@ The entry points mirror the C ABI in ``include/attn.h``:
 * ``int8_quantize``  -> ``attn_int8_quantize``  (rotation + int8 block quantisation)
 * ``fwd_int8``       -> ``attn_fwd_int8``       (int8 scores, e4m3 V and probabilities)
 * ``fwd_varlen``     -> ``attn_fwd_varlen``     (packed sequences, optional paged KV)
+* ``fwd_splitkv``    -> ``attn_fwd_splitkv``    (keys cut into ranges, merged through the LSEs)
+* ``fwd_splitkv_noalloc`` -> ``attn_fwd_splitkv_noalloc`` (the same with the library's own scratch)
 * ``bwd``            -> ``attn_bwd``            (dq, dk, dv of the dense forward)
 
 Tensors use the [batch, seq, heads, head_dim] layout (varlen: [tokens, heads,
@@ -22,8 +24,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "fp8_quantize", "fwd_fp8", "int8_quantize", "fwd_int8", "fwd_varlen", "bwd", "lib_path", "AttnError",
-           "ATTN_BF16", "ATTN_FP16"]
+__all__ = ["fwd", "fwd_bias", "fp8_quantize", "fwd_fp8", "int8_quantize", "fwd_int8", "fwd_varlen", "fwd_splitkv",
+           "fwd_splitkv_noalloc", "bwd", "lib_path", "AttnError", "ATTN_BF16", "ATTN_FP16"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libattn_fwd.so")
@@ -69,6 +71,8 @@ def _load():
     SZ = ctypes.c_size_t
     lib.attn_fwd_splitkv.argtypes = [I, P, P, P, P, P, P, I, I, P, P, I, I, I, I, I, I, F, I, I, P, SZ, P]
     lib.attn_fwd_splitkv.restype = I
+    lib.attn_fwd_splitkv_noalloc.argtypes = [I, P, P, P, P, P, P, I, I, P, P, I, I, I, I, I, I, F, I, I, P]
+    lib.attn_fwd_splitkv_noalloc.restype = I
     lib.attn_fwd_splitkv_workspace_bytes.argtypes = [I, I, I, I]
     lib.attn_fwd_splitkv_workspace_bytes.restype = SZ
     lib.attn_status_string.argtypes = [I]
@@ -424,6 +428,24 @@ def fwd_splitkv(q, cu_seqlens_q, k, v, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                                  _ptr(cu_seqlens_k), _ptr(block_table), max_pages, int(page_size), _ptr(out),
                                  _ptr(lse), B, H, D, total_q, int(max_seqlen_q), int(max_seqlen_k), scale,
                                  int(bool(causal)), num_splits, _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def fwd_splitkv_noalloc(q, cu_seqlens_q, k, v, cu_seqlens_k, max_seqlen_q, max_seqlen_k, out, lse,
+                        num_splits, softmax_scale=None, causal=False, block_table=None, page_size=0, stream=None):
+    """fwd_splitkv for callers that cannot allocate: the partial results go to
+    the library's per-device scratch (attn_fwd_splitkv_noalloc), and the caller
+    passes the outputs, out [total_q, H, D] and lse fp32 [H, total_q] (or
+    None).  Calls that overlap on one device race on that scratch."""
+    _require_cuda(q, cu_seqlens_q, k, v, cu_seqlens_k, block_table, out, lse)
+    total_q, H, D = q.shape
+    B, max_pages = _check_varlen(q, cu_seqlens_q, k, v, cu_seqlens_k, block_table, page_size, out, lse)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    _check(_lib.attn_fwd_splitkv_noalloc(_dtype_code(q.dtype), _ptr(q), _ptr(cu_seqlens_q), _ptr(k), _ptr(v),
+                                         _ptr(cu_seqlens_k), _ptr(block_table), max_pages, int(page_size),
+                                         _ptr(out), _ptr(lse), B, H, D, total_q, int(max_seqlen_q),
+                                         int(max_seqlen_k), scale, int(bool(causal)), int(num_splits),
+                                         _stream(stream)))
     return out, lse
 
 

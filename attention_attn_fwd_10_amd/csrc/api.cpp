@@ -25,6 +25,8 @@ hipError_t launch_splitkv_merge(const MergeArgs& a, int D, int dtype, hipStream_
 hipError_t launch_fwd_fp8(const Fp8Args& a, int D, bool causal, hipStream_t s);
 hipError_t launch_int8_quantize(const QuantArgs& a, int D, hipStream_t s);
 hipError_t launch_fwd_int8(const Fp8Args& a, int D, bool causal, hipStream_t s);
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(float** out);
 }  // namespace attn
 
 namespace {
@@ -298,6 +300,36 @@ attn_status_t attn_fwd_varlen(int dtype, const void* q, const int32_t* cu_seqlen
   return hip_status(dispatch_fwd16(a, D, dtype, causal != 0, mode, (hipStream_t)stream), "attn_fwd_varlen launch");
 }
 
+}  // extern "C"
+
+namespace {
+
+// The split-key launch and its merge, with the partial results in `part`
+// (num_splits * total_q * H * (D + 1) floats, validated by the caller).
+attn_status_t splitkv_launch(attn::FwdArgs a, int mode, int dtype, int D, int causal, int num_splits, float* part,
+                             const char* name, hipStream_t stream) {
+  const int total_q = a.total_q, H = a.H, B = a.B;
+  if ((int64_t)H * ((total_q + kBR - 1) / kBR + B) * num_splits > INT32_MAX)
+    return fail(ATTN_ERR_INVALID, "problem too large for one launch");
+  const int tiles = (a.Sk + 63) / 64;
+  a.n_split = num_splits;
+  a.split_tiles = (tiles + num_splits - 1) / num_splits;
+  a.part_o = part;
+  a.part_lse = a.part_o + (size_t)num_splits * total_q * H * D;
+  hipError_t e = dispatch_fwd16(a, D, dtype, causal != 0, mode, stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s launch: %s", name, hipGetErrorString(e));
+  attn::MergeArgs m{};
+  m.part_o = a.part_o; m.part_lse = a.part_lse; m.o = a.o; m.lse = a.lse;
+  m.n_split = num_splits; m.total_q = total_q; m.H = H;
+  e = attn::launch_splitkv_merge(m, D, dtype, stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s merge launch: %s", name, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t attn_fwd_splitkv_workspace_bytes(int total_q, int H, int D, int num_splits) {
   if (num_splits <= 1 || total_q <= 0 || H <= 0 || D <= 0) return 0;
   return (size_t)num_splits * (size_t)total_q * (size_t)H * (size_t)(D + 1) * sizeof(float);
@@ -323,19 +355,37 @@ attn_status_t attn_fwd_splitkv(int dtype, const void* q, const int32_t* cu_seqle
   if (workspace == nullptr || workspace_bytes < need)
     return fail(ATTN_ERR_INVALID, "workspace of %zu bytes needed (got %zu)", need, workspace == nullptr ? 0 : workspace_bytes);
   if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID, "workspace must be 16-byte aligned");
-  if ((int64_t)H * ((total_q + kBR - 1) / kBR + B) * num_splits > INT32_MAX)
-    return fail(ATTN_ERR_INVALID, "problem too large for one launch");
-  const int tiles = (max_seqlen_k + 63) / 64;
-  a.n_split = num_splits;
-  a.split_tiles = (tiles + num_splits - 1) / num_splits;
-  a.part_o = (float*)workspace;
-  a.part_lse = a.part_o + (size_t)num_splits * total_q * H * D;
-  hipError_t e = dispatch_fwd16(a, D, dtype, causal != 0, mode, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_status(e, "attn_fwd_splitkv launch");
-  attn::MergeArgs m{};
-  m.part_o = a.part_o; m.part_lse = a.part_lse; m.o = o; m.lse = lse;
-  m.n_split = num_splits; m.total_q = total_q; m.H = H;
-  return hip_status(attn::launch_splitkv_merge(m, D, dtype, (hipStream_t)stream), "attn_fwd_splitkv merge launch");
+  return splitkv_launch(a, mode, dtype, D, causal, num_splits, (float*)workspace, "attn_fwd_splitkv", (hipStream_t)stream);
+}
+
+attn_status_t attn_fwd_splitkv_noalloc(int dtype, const void* q, const int32_t* cu_seqlens_q, const void* k,
+                                       const void* v, const int32_t* cu_seqlens_k, const int32_t* block_table,
+                                       int max_pages_per_seq, int page_size, void* o, float* lse, int B, int H, int D,
+                                       int total_q, int max_seqlen_q, int max_seqlen_k, float softmax_scale,
+                                       int causal, int num_splits, void* stream) {
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(ATTN_ERR_INVALID, "num_splits %d must be in 1..%d", num_splits, kMaxSplits);
+  attn::FwdArgs a;
+  int mode;
+  bool empty;
+  const attn_status_t st = varlen_args(dtype, q, cu_seqlens_q, k, v, cu_seqlens_k, block_table, max_pages_per_seq,
+                                       page_size, o, lse, B, H, D, total_q, max_seqlen_q, max_seqlen_k,
+                                       softmax_scale, causal, &a, &mode, &empty);
+  if (st != ATTN_OK || empty) return st;
+  if (num_splits == 1)
+    return hip_status(dispatch_fwd16(a, D, dtype, causal != 0, mode, (hipStream_t)stream),
+                      "attn_fwd_splitkv_noalloc launch");
+  const size_t need = attn_fwd_splitkv_workspace_bytes(total_q, H, D, num_splits);
+  if (need > attn::noalloc_scratch_bytes())
+    return fail(ATTN_ERR_INVALID,
+                "num_splits * total_q * H * (D + 1) * 4 = %zu bytes of partial results exceed the %zu-byte scratch "
+                "of attn_fwd_splitkv_noalloc (use attn_fwd_splitkv with a workspace, or fewer splits)",
+                need, attn::noalloc_scratch_bytes());
+  float* scratch_ptr = nullptr;
+  const hipError_t e = attn::noalloc_scratch(&scratch_ptr);
+  if (e != hipSuccess) return hip_status(e, "attn_fwd_splitkv_noalloc scratch lookup");
+  return splitkv_launch(a, mode, dtype, D, causal, num_splits, scratch_ptr, "attn_fwd_splitkv_noalloc",
+                        (hipStream_t)stream);
 }
 
 typedef hipError_t (*quant_launcher_t)(const attn::QuantArgs&, int, hipStream_t);

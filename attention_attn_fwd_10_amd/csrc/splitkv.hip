@@ -6,9 +6,46 @@
 // computed as m = max_s L_s, w_s = exp(L_s - m), O = sum w_s O_s / sum w_s,
 // L = m + ln sum w_s.  Splits that saw no key (L_s = -inf) weigh nothing; a row
 // with no key at all gets O = 0 and L = -inf.
+#include <mutex>
+
+#include "../../include/attn.h"
 #include "common.hpp"
 
 namespace attn {
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free split-key entry point: the partial outputs
+// and logsumexps live in this file-scope device array instead of a workspace
+// the caller allocates.  Each GPU the library runs on holds its own copy until
+// the process ends.  In host code `scratch` names a host-side stand-in, never
+// the device memory: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is ever passed on.
+constexpr size_t kNoAllocScratchBytes = ATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+size_t noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+// Device address of this device's `scratch` (the current device's), looked
+// up on the first call on each device and kept.
+hipError_t noalloc_scratch(float** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = static_cast<float*>(addr[dev]);
+  return hipSuccess;
+}
 
 // one wave per (row, head); lane l owns head-dim columns E*l .. E*l+E-1
 template <int D, int DT>

@@ -254,6 +254,38 @@ attn_status_t attn_fwd_splitkv(int dtype,
  * bytes (0 for num_splits <= 1 or an empty problem). */
 size_t attn_fwd_splitkv_workspace_bytes(int total_q, int H, int D, int num_splits);
 
+/* Size of the scratch attn_fwd_splitkv_noalloc keeps on each device. */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * attn_fwd_splitkv_noalloc — attn_fwd_splitkv for callers that cannot
+ * allocate device memory at call time: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, results
+ * and errors as attn_fwd_splitkv without the workspace: the partial outputs
+ * and logsumexps go to a scratch array of ATTN_NOALLOC_SCRATCH_BYTES (32 MiB)
+ * that the library holds on each device it runs on until the process ends.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); on its first call on a device it looks up that device's scratch
+ * address (the current device, which must own `stream`).
+ *
+ * Limit: num_splits * total_q * H * (D + 1) * 4 bytes (what
+ * attn_fwd_splitkv_workspace_bytes reports) must not exceed
+ * ATTN_NOALLOC_SCRATCH_BYTES; a larger request returns ATTN_ERR_INVALID and
+ * launches nothing.  num_splits == 1 uses no scratch.
+ * Every call on one device shares that device's scratch: calls that overlap
+ * in time on one device (other streams, other host threads) race and must be
+ * serialised by the caller.  No part of the scratch needs to start at zero
+ * (every partial result the merge reads is written by the same call).
+ */
+attn_status_t attn_fwd_splitkv_noalloc(int dtype,
+                                       const void* q, const int32_t* cu_seqlens_q,
+                                       const void* k, const void* v,
+                                       const int32_t* cu_seqlens_k,
+                                       const int32_t* block_table, int max_pages_per_seq, int page_size,
+                                       void* o, float* lse,
+                                       int B, int H, int D, int total_q, int max_seqlen_q, int max_seqlen_k,
+                                       float softmax_scale, int causal, int num_splits, void* stream);
+
 /*
  * attn_bwd — gradients of attn_fwd with respect to q, k and v.
  * (The FlashAttention-3 summary page reports a backward pass beside the

@@ -36,6 +36,7 @@ def lib():
     L.attn_fwd_varlen.argtypes = [I, P, P, P, P, P, P, I, I, P, P, I, I, I, I, I, I, F, I, P]
     L.attn_fwd_splitkv.argtypes = [I, P, P, P, P, P, P, I, I, P, P, I, I, I, I, I, I, F, I, I, P,
                                    ctypes.c_size_t, P]
+    L.attn_fwd_splitkv_noalloc.argtypes = [I, P, P, P, P, P, P, I, I, P, P, I, I, I, I, I, I, F, I, I, P]
     L.attn_fwd_splitkv_workspace_bytes.argtypes = [I, I, I, I]
     L.attn_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
     L.attn_fwd_bias.argtypes = [I, P, I64P, P, I64P, P, I64P, P, I64P, P, I64P, P, I, I, I, I, I, F, I, P]
@@ -55,7 +56,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("attn_fwd", "attn_fp8_quantize", "attn_fwd_fp8", "attn_fwd_varlen", "attn_fwd_splitkv",
               "attn_fwd_splitkv_workspace_bytes", "attn_fwd_bias", "attn_int8_quantize", "attn_fwd_int8",
-              "attn_bwd", "attn_status_string", "attn_last_error"):
+              "attn_bwd", "attn_status_string", "attn_last_error", "attn_fwd_splitkv_noalloc"):
         assert n in names
 
 
@@ -163,6 +164,20 @@ def test_splitkv_validation(lib):
     assert f(page=48) == INVALID                      # the varlen checks apply
     assert f(D=80) == UNSUPPORTED
     assert f(B=0) == OK and f(total_q=0) == OK          # empty problems: no-op
+
+
+def test_splitkv_noalloc_validation(lib):
+    def f(splits=4, B=2, total_q=10, H=2, D=128, page=64, table=A16):
+        return lib.attn_fwd_splitkv_noalloc(0, A16, A16, A16, A16, A16, table, 4, page, A16, None, B, H, D, total_q,
+                                            100, 200, 0.1, 1, splits, None)
+    assert f(splits=0) == INVALID
+    assert f(splits=257) == INVALID
+    assert f(page=48) == INVALID                      # the varlen checks apply
+    assert f(D=80) == UNSUPPORTED
+    assert f(B=0) == OK and f(total_q=0) == OK          # empty problems: no-op
+    # partial results beyond the library's scratch are refused before anything runs
+    assert f(splits=16, total_q=4096, H=32) == INVALID
+    assert b"scratch" in lib.attn_last_error()
 
 
 def test_bias_validation(lib):
