@@ -1,18 +1,30 @@
 // The 8-bit prologue ("Fused attention kernel" page, section "8-bit forward
 // pass"): optional incoherent processing — every row multiplied by
-// diag(signs) H_D / sqrt(D), evaluated as a fast Walsh-Hadamard transform in
-// float32 — then block quantisation to e4m3: one scale per (b, h, 128 rows)
-// (or one per tensor for the baseline), scale = amax / 448, code =
-// e4m3fn(x / scale) with round-to-nearest-even and saturation.
+// diag(signs) H_D / sqrt(D) — then block quantisation to e4m3: one scale per
+// (b, h, 128 rows) (or one per tensor for the baseline), scale = amax / 448,
+// code = e4m3fn(x / scale) with round-to-nearest-even and saturation.
 //
 // The int8 form (the case study's int8 path) quantises symmetrically instead:
 // scale = amax / 127, code = x / scale rounded to nearest-even and clamped to
 // [-127, 127].
 //
-// This step streams every element once from HBM and writes a byte back, so it
-// is bandwidth bound; a workgroup owns one 128-row block of one head, holds
-// the whole block in registers (16 values per lane), reduces the block amax
-// through LDS and writes 16 codes per lane with one 16-byte store.
+// This step streams every element once from HBM and writes a byte back; a
+// workgroup owns one 128-row block of one head and holds it in registers,
+// reduces the block amax through LDS and writes the codes.  What each element
+// costs on the vector units decides whether the pass reaches the bandwidth
+// bound, so:
+//  * the rotation runs on the matrix cores: (x * signs) H_D is a product with
+//    a +-1 matrix, exact in bf16 operands (the signs flip sign bits of the bf16
+//    inputs; H_D's entries are generated in registers from the parity of the
+//    row and column indices) with float32 accumulation;
+//  * the quotient x / scale, which decides the code, is correctly rounded
+//    float32 without a division per element: r = 1 / scale once per block,
+//    q = x r, then two residual corrections q += fma(-q, scale, x) r (with r
+//    within half an ulp of 1 / scale each residual is exact and the corrected
+//    quotient is the correctly rounded one).  Blocks whose scale is below
+//    2^-60 are first multiplied by 2^64 (exact), so no residual falls in the
+//    subnormal range where that fails; elsewhere a subnormal x gives a
+//    quotient below 2^-66, which codes as a zero of x's sign either way.
 #include "common.hpp"
 
 namespace attn {
@@ -20,7 +32,7 @@ namespace attn {
 // float32 (already divided by the scale) -> int8 code: nearest-even, clamped
 // to [-127, 127], returned as its byte
 __device__ __forceinline__ uint32_t int8_encode(float y) {
-  const float r = fminf(fmaxf(__builtin_rintf(y), -127.f), 127.f);
+  const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(y), -127.f, 127.f);
   return (uint32_t)(int32_t)r & 0xffu;
 }
 
@@ -30,8 +42,60 @@ enum QuantFormat { kE4M3 = 0, kInt8 = 1 };
 template <int FMT>
 constexpr float code_max() { return FMT == kInt8 ? 127.f : 448.f; }
 
+// The correctly rounded float32 quotient x / s from r = RN(1 / s): one
+// product and two fma residual corrections; the sign of a zero quotient is
+// taken from x.
+struct QuotientRN {
+  float s, r, pre;  // scale (pre-multiplied), its reciprocal, the factor applied to x
+  __device__ __forceinline__ explicit QuotientRN(float scale) {
+    pre = scale < 0x1p-60f ? 0x1p64f : 1.f;
+    s = scale * pre;
+    r = __fdiv_rn(1.f, s);
+  }
+  __device__ __forceinline__ float operator()(float x) const {
+    const float q0 = x * r;
+    const float q1 = fmaf(fmaf(-q0, s, x), r, q0);
+    return __builtin_copysignf(fmaf(fmaf(-q1, s, x), r, q1), x);
+  }
+};
+
+// four quotients -> four code bytes (byte i = value i)
+template <int FMT>
+__device__ __forceinline__ uint32_t encode4(float y0, float y1, float y2, float y3) {
+  if constexpr (FMT == kInt8) {
+    return int8_encode(y0) | int8_encode(y1) << 8 | int8_encode(y2) << 16 | int8_encode(y3) << 24;
+  } else {
+    // the hardware converter rounds to nearest-even into e4m3fn but does not
+    // saturate: clamp to +-448 first (one v_med3 per value)
+    y0 = __builtin_amdgcn_fmed3f(y0, -448.f, 448.f);
+    y1 = __builtin_amdgcn_fmed3f(y1, -448.f, 448.f);
+    y2 = __builtin_amdgcn_fmed3f(y2, -448.f, 448.f);
+    y3 = __builtin_amdgcn_fmed3f(y3, -448.f, 448.f);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, lo, true);
+  }
+}
+
+// amax of the workgroup (4 waves) through LDS
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) v = fmaxf(v, __shfl_xor(v, s));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// scale of a block (or of the tensor) from its amax
+template <int FMT>
+__device__ __forceinline__ float scale_of(float amax) {
+  return amax > 0.f ? __fdiv_rn(amax, code_max<FMT>()) : 1.f;
+}
+
+// ---------------------------------------------------------------------------
+// Without rotation: D/16 lanes per row, 16 consecutive values per lane.
+// ---------------------------------------------------------------------------
 template <int D, int MODE, int FMT>
-__global__ void __launch_bounds__(256) fp8_quant_kernel(QuantArgs a) {
+__global__ void __launch_bounds__(256) quant_plain_kernel(QuantArgs a) {
   constexpr int LPR = D / 16;          // lanes per row (16 values per lane)
   constexpr int RP = 256 / LPR;        // rows per pass
   constexpr int NP = 128 / RP;         // passes over a 128-row block
@@ -65,53 +129,31 @@ __global__ void __launch_bounds__(256) fp8_quant_kernel(QuantArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) x[p][e] = 0.f;
     }
-    if (a.signs != nullptr) {
-      // x <- (x * signs) H_D: butterflies of span 1..8 inside the lane, then
-      // span 16..D/2 across the LPR lanes of the row (lane xor span/16)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) x[p][e] *= (float)a.signs[16 * seg + e];
-#pragma unroll
-      for (int span = 1; span < 16; span <<= 1)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if ((e & span) == 0) {
-            const float u = x[p][e], v = x[p][e + span];
-            x[p][e] = u + v;
-            x[p][e + span] = u - v;
-          }
-#pragma unroll
-      for (int s = 1; s < LPR; s <<= 1) {
-        const bool upper = (seg & s) != 0;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float other = __shfl_xor(x[p][e], s);
-          x[p][e] = upper ? other - x[p][e] : x[p][e] + other;
-        }
-      }
-      const float norm = 1.0f / __builtin_sqrtf((float)D);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) x[p][e] *= norm;
-    }
 #pragma unroll
     for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[p][e]));
   }
 
-  if constexpr (MODE != kQuantGlobal) {
+  if constexpr (MODE == kAmaxOnly) {
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) amax = fmaxf(amax, __shfl_xor(amax, s));
-    if ((tid & 63) == 0) red[tid >> 6] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  }
-  if constexpr (MODE == kAmaxOnly) {
     // non-negative floats order like their bit patterns
-    if (tid == 0) atomicMax((unsigned int*)a.scales, __float_as_uint(amax));
+    if ((tid & 63) == 0) atomicMax((unsigned int*)a.scales, __float_as_uint(amax));
     return;
   }
-  if constexpr (MODE == kQuantGlobal) amax = a.scales[0];
-  const float scale = amax > 0.f ? __fdiv_rn(amax, code_max<FMT>()) : 1.f;
-  if constexpr (MODE == kQuantBlock)
+  float scale;
+  if constexpr (MODE == kQuantGlobal) {
+    scale = a.scales[0];
+  } else {
+    scale = scale_of<FMT>(block_max(amax, red));
     if (tid == 0) a.scales[(int64_t)bh * nblk + blk] = scale;
+  }
+  const QuotientRN div(scale);
+  if (div.pre != 1.f) {  // uniform: a block of tiny values
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[p][e] *= div.pre;
+  }
 
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
@@ -119,26 +161,127 @@ __global__ void __launch_bounds__(256) fp8_quant_kernel(QuantArgs a) {
     if (row < a.S) {
       u32x4 out;
 #pragma unroll
-      for (int wd = 0; wd < 4; ++wd) {
-        float y[4];
-#pragma unroll
-        for (int by = 0; by < 4; ++by) y[by] = __fdiv_rn(x[p][4 * wd + by], scale);
-        if constexpr (FMT == kInt8) {
-          uint32_t v = 0;
-#pragma unroll
-          for (int by = 0; by < 4; ++by) v |= int8_encode(y[by]) << (8 * by);
-          out[wd] = v;
-        } else {
-          // the hardware converter rounds to nearest-even into e4m3fn but does
-          // not saturate: clamp to +-448 first (one v_med3 per value)
-#pragma unroll
-          for (int by = 0; by < 4; ++by) y[by] = __builtin_amdgcn_fmed3f(y[by], -448.f, 448.f);
-          const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-          out[wd] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
-        }
-      }
+      for (int wd = 0; wd < 4; ++wd)
+        out[wd] = encode4<FMT>(div(x[p][4 * wd]), div(x[p][4 * wd + 1]), div(x[p][4 * wd + 2]), div(x[p][4 * wd + 3]));
       *(u32x4*)(a.x8 + (((int64_t)b * a.S + row) * a.H + h) * D + 16 * seg) = out;
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// With rotation: y = (x * signs) H_D on the matrix cores, then y / sqrt(D).
+// Wave w owns rows 32w .. 32w+31 of the block.  Y^T = H_D^T (x * signs)^T is
+// computed 32 output columns (tile jt) x 32 rows at a time with
+// v_mfma_f32_32x32x16_bf16: the A operand is a 32 x 16 tile of H_D^T, whose
+// row m stands for output column 32 jt + swz23(m), so that accumulator
+// register r of lane-half hh holds output column 32 jt + 16 (r / 8) + 8 hh +
+// r % 8 of data row (lane % 32): runs of 8 consecutive codes per lane.  The B
+// operand is the lane's 8 inputs x[row][16 kk + 8 hh .. +7] (one 16-byte
+// load each), their sign bits flipped where signs are negative.
+// ---------------------------------------------------------------------------
+template <int D, int MODE, int FMT>
+__global__ void __launch_bounds__(256) quant_rot_kernel(QuantArgs a) {
+  constexpr int NK = D / 16, NJ = D / 32;
+  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint32_t smask[D / 2];  // sign-bit masks of bf16 pairs (k, k + 1)
+
+  const int tid = threadIdx.x;
+  const int nblk = (a.S + 127) / 128;
+  const int w = blockIdx.x;
+  const int bh = w / nblk, blk = w - bh * nblk;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int row = blk * 128 + 32 * wave + l32;
+  const bool valid = row < a.S;
+
+  // inputs, as B operands
+  u32x4 xb[NK];
+  {
+    const uint16_t* src = a.x + b * a.x_sb + (int64_t)(valid ? row : 0) * a.x_ss + h * a.x_sh + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) xb[kk] = valid ? *(const u32x4*)(src + 16 * kk) : u32x4{0, 0, 0, 0};
+  }
+  for (int p = tid; p < D / 2; p += 256)
+    smask[p] = (a.signs[2 * p] < 0 ? 0x8000u : 0u) | (a.signs[2 * p + 1] < 0 ? 0x80000000u : 0u);
+  __syncthreads();
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) xb[kk] ^= *(const u32x4*)&smask[(16 * kk + 8 * hh) / 2];
+
+  // A operands.  H_D[k][j] = (-1)^popcount(k & j); with k = 16 kk + 8 hh + e
+  // and j = 32 jt + jl, jl = swz23(m):
+  //   popcount(k & j) = popcount(e & jl & 7) + hh * jl[3] + kk[0] * jl[4]
+  //                     + popcount((kk >> 1) & jt),
+  // so every tile is one per-lane vector (the first two terms) with its sign
+  // flipped by a per-lane bit (kk odd and jl[4]) and by a compile-time bit.
+  const int jl = swz23(l32);
+  u32x4 h00;
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int e = 2 * e2 + t;
+      const int par = (__builtin_popcount(e & jl & 7) + (hh & (jl >> 3))) & 1;
+      v |= (par ? 0xBF80u : 0x3F80u) << (16 * t);
+    }
+    h00[e2] = v;
+  }
+  const uint32_t lane_flip = ((jl >> 4) & 1) ? 0x80008000u : 0u;
+  const u32x4 h01 = h00 ^ 0x80008000u, h10 = h00 ^ lane_flip, h11 = h10 ^ 0x80008000u;
+
+  f32x16 acc[NJ];
+  const f32x16 zero16 = {};
+#pragma unroll
+  for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const bool odd = kk & 1, ct = __builtin_popcount((kk >> 1) & jt) & 1;
+      const u32x4 hop = odd ? (ct ? h11 : h10) : (ct ? h01 : h00);
+      acc[jt] = mfma32<kBF16>(hop, xb[kk], kk == 0 ? zero16 : acc[jt]);
+    }
+
+  const float norm = 1.0f / __builtin_sqrtf((float)D);
+  float amax = 0.f;
+#pragma unroll
+  for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      acc[jt][r] *= norm;
+      amax = fmaxf(amax, fabsf(acc[jt][r]));
+    }
+
+  if constexpr (MODE == kAmaxOnly) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) amax = fmaxf(amax, __shfl_xor(amax, s));
+    if (lane == 0) atomicMax((unsigned int*)a.scales, __float_as_uint(amax));
+    return;
+  }
+  float scale;
+  if constexpr (MODE == kQuantGlobal) {
+    scale = a.scales[0];
+  } else {
+    scale = scale_of<FMT>(block_max(amax, red));
+    if (tid == 0) a.scales[(int64_t)bh * nblk + blk] = scale;
+  }
+  const QuotientRN div(scale);
+  if (div.pre != 1.f) {
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[jt][r] *= div.pre;
+  }
+  if (valid) {
+    uint8_t* dst = a.x8 + (((int64_t)b * a.S + row) * a.H + h) * D + 8 * hh;
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+      for (int run = 0; run < 2; ++run) {
+        const f32x16& y = acc[jt];
+        const int r0 = 8 * run;
+        *(u32x2*)(dst + 32 * jt + 16 * run) =
+            u32x2{encode4<FMT>(div(y[r0]), div(y[r0 + 1]), div(y[r0 + 2]), div(y[r0 + 3])),
+                  encode4<FMT>(div(y[r0 + 4]), div(y[r0 + 5]), div(y[r0 + 6]), div(y[r0 + 7]))};
+      }
   }
 }
 
@@ -149,18 +292,26 @@ __global__ void fp8_finalize_scale_kernel(float* p, float code_max) {
   *p = amax > 0.f ? __fdiv_rn(amax, code_max) : 1.f;
 }
 
+template <int D, int MODE, int FMT>
+void launch_quant_pass(const QuantArgs& a, dim3 grid, hipStream_t s) {
+  if (a.signs != nullptr)
+    hipLaunchKernelGGL((quant_rot_kernel<D, MODE, FMT>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((quant_plain_kernel<D, MODE, FMT>), grid, dim3(256), 0, s, a);
+}
+
 template <int D, int FMT>
 hipError_t launch_quant_d(const QuantArgs& a, hipStream_t s) {
   const int nblk = (a.S + 127) / 128;
-  const dim3 grid(a.B * a.H * nblk), block(256);
+  const dim3 grid(a.B * a.H * nblk);
   if (a.block_rows == 128) {
-    hipLaunchKernelGGL((fp8_quant_kernel<D, kQuantBlock, FMT>), grid, block, 0, s, a);
+    launch_quant_pass<D, kQuantBlock, FMT>(a, grid, s);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(fp8_fill_kernel, dim3(1), dim3(1), 0, s, a.scales, 0.f);
-  hipLaunchKernelGGL((fp8_quant_kernel<D, kAmaxOnly, FMT>), grid, block, 0, s, a);
-  hipLaunchKernelGGL((fp8_quant_kernel<D, kQuantGlobal, FMT>), grid, block, 0, s, a);
+  launch_quant_pass<D, kAmaxOnly, FMT>(a, grid, s);
   hipLaunchKernelGGL(fp8_finalize_scale_kernel, dim3(1), dim3(1), 0, s, a.scales, code_max<FMT>());
+  launch_quant_pass<D, kQuantGlobal, FMT>(a, grid, s);
   return hipGetLastError();
 }
 

@@ -87,6 +87,43 @@ def test_quantize_rounding_ties_bitexact(lib, block_rows):
     np.testing.assert_array_equal(codes.cpu().numpy(), rc)
 
 
+def _across_magnitudes(rng, shape):
+    """N(0,1) blocks, each (batch, head, 128-row block) multiplied by its own
+    power of two from 2^-140 (bf16 subnormals, and a scale below 2^-60 whose
+    reciprocal would overflow) to 2^100, rounded to bf16."""
+    B, S, H, D = shape
+    x = rng.standard_normal(shape).astype(np.float64)
+    exps = np.array([-140, -133, -128, -126, -100, -64, -61, -60, -59, -20, -1, 0, 3, 40, 100])
+    for b in range(B):
+        for h in range(H):
+            for blk in range(0, S, 128):
+                x[b, blk:blk + 128, h] *= 2.0 ** int(rng.choice(exps))
+    bits = W.bf16_round(x.astype(np.float32))
+    return W.bf16_bits_to_f32(bits)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "int8"])
+@pytest.mark.parametrize("block_rows", [128, 0])
+def test_quantize_bitexact_across_magnitudes(lib, fmt, block_rows):
+    """The code decision (a correctly rounded float32 quotient x / scale, then
+    the format's rounding) matches the oracle bit for bit for blocks of every
+    magnitude, subnormal inputs and scales included."""
+    import torch
+    from oracle import int8 as OI
+    x = _across_magnitudes(np.random.default_rng(61 + block_rows), (2, 640, 4, 128))
+    xd = to_dev(x)
+    assert np.array_equal(xd.float().cpu().numpy(), x)   # bf16-exact inputs
+    if fmt == "e4m3":
+        codes, scales = lib.fp8_quantize(xd, block_rows, None)
+        rc, rs = OF.quantize(x, block_rows)
+    else:
+        codes, scales = lib.int8_quantize(xd, block_rows, None)
+        rc, rs = OI.quantize(x, block_rows)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+
+
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_quantize_with_rotation_within_one_step(lib, d):
     import torch
