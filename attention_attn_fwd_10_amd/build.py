@@ -1,8 +1,10 @@
-"""Build the HIP library ``libattn_fwd.so`` in-tree with hipcc for gfx950.
+"""Build the HIP libraries in-tree with hipcc for gfx950.
 
-Each translation unit under ``csrc/`` is compiled to an object in ``_build/``
-(in parallel), then everything is linked into a shared library next to this
-file.  ``python -m attention_attn_fwd_10_amd.build`` runs it."""
+``libattn_fwd.so``: every translation unit under ``csrc/`` is compiled to an
+object in ``_build/`` (in parallel) and linked into a shared library next to
+this file.  ``libattn_probe.so``: the measured-ceilings probes under
+``probe/`` (not part of the attention path).
+``python -m attention_attn_fwd_10_amd.build`` runs it."""
 from __future__ import annotations
 
 import concurrent.futures as cf
@@ -14,8 +16,10 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
+PROBE = os.path.join(PKG, "probe")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn_fwd.so")
+PROBE_LIB = os.path.join(PKG, "libattn_probe.so")
 
 ARCH = "gfx950"
 # Packed fp32 VALU forms are kept out of the generated code on purpose.
@@ -30,12 +34,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build the library")
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+def sources(folder: str = CSRC):
+    return sorted(os.path.join(folder, f) for f in os.listdir(folder) if f.endswith((".hip", ".cpp")))
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    obj = os.path.join(BUILD, os.path.basename(os.path.dirname(src)) + "_" + os.path.basename(src) + ".o")
     cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -43,20 +47,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    jobs = jobs or min(len(srcs), os.cpu_count() or 4, 8)
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int | None = None, verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs, probe_srcs = sources(), sources(PROBE)
+    jobs = jobs or min(len(srcs) + len(probe_srcs), os.cpu_count() or 4, 8)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, srcs + probe_srcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources", file=sys.stderr)
+        print(f"built {LIB} from {len(srcs)} sources and {PROBE_LIB} from {len(probe_srcs)}", file=sys.stderr)
     return LIB
 
 

@@ -80,6 +80,9 @@ def parse():
     p.add_argument("--sweep", action="store_true", help="also time the 16384-token seq sweep (extra output)")
     p.add_argument("--no-decode", action="store_true", help="skip the long-cache decoding leg")
     p.add_argument("--no-bias", action="store_true", help="skip the additive-bias leg")
+    p.add_argument("--no-points", action="store_true",
+                   help="skip the extra workload points (seq-8192 headline, seq-512 GB/s, varlen+paged, causal fp8)")
+    p.add_argument("--no-ceilings", action="store_true", help="skip the measured-ceiling probes and clock")
     p.add_argument("--source-hash", action="store_true", help="print the timed kernel's source hash and exit")
     p.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (calibrates the FETCH_SIZE/WRITE_SIZE counters)")
@@ -115,9 +118,21 @@ def time_launches(fn, steps, warmup):
     return start.elapsed_time(end) / steps  # ms
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, q, k, v, target_s):
     """The float64 oracle (three-pass definition) on whole heads of the same
-    workload until about ``target_s`` seconds of CPU work have run."""
+    workload until about ``target_s`` seconds of CPU work have run.  `cores`
+    is the number of BLAS threads the oracle ran on; the host's own core count
+    and CPU model are reported beside it."""
     from oracle import attention as OA
     try:
         from threadpoolctl import threadpool_info
@@ -137,7 +152,9 @@ def cpu_baseline(w, q, k, v, target_s):
     dt = time.perf_counter() - t0
     out = {"value": n * flops_head / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
            "sample": f"{n} of {len(pairs)} (batch, head) pairs of {w.name}, all rows, float64 numpy "
-                     f"three-pass, {dt:.1f} s"}
+                     f"three-pass, {dt:.1f} s",
+           "host_nproc": os.cpu_count(), "host_affinity_cpus": len(os.sched_getaffinity(0)),
+           "cpu_model": cpu_model()}
     # one (batch, head) on one core, beside the threaded figure
     try:
         from threadpoolctl import threadpool_limits
@@ -222,6 +239,12 @@ def main():
 
     if not args.no_bias:
         result["bias"] = bench_bias(A, W, args)
+
+    if not args.no_points:
+        result["points"] = bench_points(A, W, args)
+
+    if not args.no_ceilings:
+        result["ceilings"] = measured_ceilings(result)
 
     if args.sweep:
         result["sweep"] = bench_sweep(A, W, args)
@@ -380,6 +403,140 @@ def bench_bias(A, W, args):
     out["full_bias_bytes"] = full.numel() * 2
     out["full_bias_gbs"] = round(full.numel() * 2 / (out["ms_full"] * 1e-3) / 1e9, 1)
     del full
+    return out
+
+
+def bench_points(A, W, args):
+    """The other workload points the metric and the pages single out, each
+    timed with HIP events on device-resident inputs drawn from its seed:
+    the d128 seq-8k headline point of the 16384-token sweep (batch 2, 16
+    heads, non-causal), the seq-512 d128 points in GB/s (HBM-bound), the
+    varlen + paged workload (packed and with 64-token pages), and the 8-bit
+    kernel under a causal mask."""
+    import torch
+    steps = max(5, args.steps // 3)
+    out = {}
+    pts = {p.name: p for p in W.seq_sweep_points()}
+    for name in ("sweep_s8192_d128_full", "sweep_s8192_d128_causal", "sweep_s512_d128_full",
+                 "sweep_s512_d128_causal"):
+        w = pts[name]
+        qs, _ = w.shapes()
+        g = torch.Generator(device="cuda").manual_seed(w.seed)
+        q, k, v = (torch.randn(qs, generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.batch, w.heads, w.seq_q), dtype=torch.float32, device="cuda")
+        ms = time_launches(lambda: A.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse), steps, 10)
+        tf = w.flops / (ms * 1e-3) / 1e12
+        byts = 4 * q.numel() * 2 + 4 * w.batch * w.heads * w.seq_q
+        out[name] = {"batch": w.batch, "heads": w.heads, "seq": w.seq_q, "head_dim": w.head_dim,
+                     "causal": w.causal, "ms": round(ms, 4), "tflops": round(tf, 1),
+                     "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                     "gbs": round(byts / (ms * 1e-3) / 1e9, 1), "pct_of_hbm_peak": round(100 * byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)}
+        print(f"[bench] {name}: {ms:.3f} ms {tf:.1f} TFLOP/s {out[name]['gbs']} GB/s", file=sys.stderr, flush=True)
+        del q, k, v, o
+    out["varlen_paged"] = bench_varlen(A, W, steps)
+    out["fp8_causal"] = bench_fp8_causal(A, W, steps)
+    return out
+
+
+def bench_varlen(A, W, steps):
+    """32 sequences U{128..4096} (seed 5), 32 heads, d128, causal: packed and
+    with 64-token pages at permuted slots."""
+    import torch
+    cfg = W.VARLEN
+    lens = W.varlen_lengths(cfg["seed_lengths"], cfg["n_seq"], cfg["lo"], cfg["hi"])
+    H, D, page = cfg["heads"], cfg["head_dim"], cfg["page_size"]
+    cu = torch.from_numpy(W.cu_seqlens(lens)).cuda()
+    tot = int(lens.sum())
+    g = torch.Generator(device="cuda").manual_seed(cfg["seed_values"])
+    q, k, v = (torch.randn((tot, H, D), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+    table, npages = W.paged_layout(cfg["seed_pages"], lens, page)
+    # scatter every sequence's keys into its pages (one gather index per token)
+    cuh = W.cu_seqlens(lens)
+    dst = np.concatenate([table[b, np.arange(int(n)) // page] * page + np.arange(int(n)) % page
+                          for b, n in enumerate(lens)])
+    src = np.concatenate([cuh[b] + np.arange(int(n)) for b, n in enumerate(lens)])
+    kp = torch.zeros((npages * page, H, D), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros_like(kp)
+    di, si = torch.from_numpy(dst.astype(np.int64)).cuda(), torch.from_numpy(src.astype(np.int64)).cuda()
+    kp[di] = k[si]
+    vp[di] = v[si]
+    kp, vp = kp.view(npages, page, H, D), vp.view(npages, page, H, D)
+    tab = torch.from_numpy(table).cuda()
+    flops = sum(4.0 * H * int(n) * int(n) * D / 2 for n in lens)
+    mx = int(lens.max())
+    o = torch.empty_like(q)
+    lse = torch.empty((H, tot), dtype=torch.float32, device="cuda")
+    res = {"workload": f"varlen_32seq_u128_4096_h{H}_d{D}_causal", "tokens": tot, "flops": flops}
+    for name, kk, vv, bt in (("packed", k, v, None), ("paged64", kp, vp, tab)):
+        ms = time_launches(lambda: A.fwd_varlen(q, cu, kk, vv, cu, mx, mx, None, True, block_table=bt,
+                                                page_size=page if bt is not None else 0, out=o, lse=lse),
+                           steps, 10)
+        tf = flops / (ms * 1e-3) / 1e12
+        res[f"ms_{name}"] = round(ms, 4)
+        res[f"tflops_{name}"] = round(tf, 1)
+        print(f"[bench] varlen {name}: {ms:.3f} ms {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    return res
+
+
+def bench_fp8_causal(A, W, steps):
+    """The 8-bit kernel with a causal mask on the 8-bit workload shape
+    (quantised inputs; FLOPs halved)."""
+    import torch
+    w = W.WORKLOADS["fp8"]
+    qs, _ = w.shapes()
+    qh, kh, vh = W.qkv_outlier(w.seed, qs)
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in (qh, kh, vh))
+    signs = torch.from_numpy(W.random_signs(4, w.head_dim)).cuda()
+    q8, qsc = A.fp8_quantize(q, 128, signs)
+    k8, ksc = A.fp8_quantize(k, 128, signs)
+    v8, vsc = A.fp8_quantize(v, 128, None)
+    del q, k, v
+    o = torch.empty((w.batch, w.seq_q, w.heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.batch, w.heads, w.seq_q), dtype=torch.float32, device="cuda")
+    ms = time_launches(lambda: A.fwd_fp8(q8, qsc, k8, ksc, v8, vsc, 128, w.scale, True, out=o, lse=lse), steps, 10)
+    tf = w.flops / 2 / (ms * 1e-3) / 1e12
+    print(f"[bench] fp8 causal: {ms:.3f} ms {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    return {"workload": w.name + "_causal", "ms": round(ms, 4), "tflops": round(tf, 1),
+            "pct_of_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2)}
+
+
+def measured_ceilings(result):
+    """Sustained clock, matrix-core rates and vector-instruction costs measured
+    by libattn_probe.so on this GPU, and what they imply for the timed kernels:
+    the datasheet peaks assume 2.4 GHz; the exp2-bound ceiling is the rate at
+    which the chip evaluates one exponential per score (4 * D flops per score
+    at D = 128)."""
+    import ctypes
+    path = os.path.join(ROOT, "attention_attn_fwd_10_amd", "libattn_probe.so")
+    if not os.path.exists(path):
+        return {"available": False, "reason": "libattn_probe.so not built"}
+    lib = ctypes.CDLL(path)
+    n = 32
+    r = (ctypes.c_double * n)()
+    rc = lib.attn_probe_ceilings(r, n)
+    names = ["exp", "fma", "add", "max3", "cvt_pk_fp8", "cvt_pk_bf16", "rcp"]
+    clock = r[10]
+    cus = r[18]
+    simds = 4 * cus
+    out = {"ok": rc == 0, "clock_ghz": round(clock, 3), "cus": int(cus),
+           "mfma_bf16_tflops": round(r[7] / 1e12, 1), "mfma_fp8_tflops": round(r[8] / 1e12, 1),
+           "mfma_i8_tops": round(r[9] / 1e12, 1)}
+    # cycles one wave64 instruction holds its SIMD's vector unit
+    for i, nm in enumerate(names):
+        out[f"{nm}_cycles_per_wave_instr"] = round(simds * clock * 1e9 * 64 / r[i], 2) if r[i] > 0 else None
+    out["exp2_bound_ceiling_tflops_d128"] = round(r[0] * 4 * 128 / 1e12, 1)
+    out["overlap_ms"] = {"one_wave_mfma": round(r[11], 4), "one_wave_exp16": round(r[12], 4),
+                         "one_wave_mfma_plus_exp8": round(r[13], 4), "one_wave_mfma_plus_exp16": round(r[14], 4),
+                         "two_waves_mfma": round(r[15], 4), "two_waves_exp": round(r[16], 4),
+                         "two_waves_both": round(r[17], 4)}
+    # the timed bf16 and fp8 kernels against the measured (not datasheet) matrix rates
+    if clock > 0:
+        out["bf16_frac_of_measured_mfma"] = round(result["value"] / (r[7] / 1e12), 4)
+        if isinstance(result.get("fp8"), dict) and result["fp8"].get("available"):
+            out["fp8_frac_of_measured_mfma"] = round(result["fp8"]["tflops"] / (r[8] / 1e12), 4)
+    print(f"[bench] ceilings: clock {clock:.3f} GHz, bf16 MFMA {r[7] / 1e12:.0f} TFLOP/s, "
+          f"fp8 {r[8] / 1e12:.0f}, exp {out['exp_cycles_per_wave_instr']} cycles/instr", file=sys.stderr, flush=True)
     return out
 
 

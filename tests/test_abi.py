@@ -38,6 +38,10 @@ def lib():
                                    ctypes.c_size_t, P]
     L.attn_fwd_splitkv_noalloc.argtypes = [I, P, P, P, P, P, P, I, I, P, P, I, I, I, I, I, I, F, I, I, P]
     L.attn_fwd_splitkv_workspace_bytes.argtypes = [I, I, I, I]
+    I32P = ctypes.POINTER(ctypes.c_int32)
+    L.attn_check_indices_host.argtypes = [I32P, I32P, I32P, I, I, I, I, I, I]
+    L.attn_set_index_checks.argtypes = [I]
+    L.attn_set_index_checks.restype = None
     L.attn_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
     L.attn_fwd_bias.argtypes = [I, P, I64P, P, I64P, P, I64P, P, I64P, P, I64P, P, I, I, I, I, I, F, I, P]
     L.attn_status_string.argtypes = [I]
@@ -56,7 +60,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("attn_fwd", "attn_fp8_quantize", "attn_fwd_fp8", "attn_fwd_varlen", "attn_fwd_splitkv",
               "attn_fwd_splitkv_workspace_bytes", "attn_fwd_bias", "attn_int8_quantize", "attn_fwd_int8",
-              "attn_bwd", "attn_status_string", "attn_last_error", "attn_fwd_splitkv_noalloc"):
+              "attn_bwd", "attn_status_string", "attn_last_error", "attn_fwd_splitkv_noalloc",
+              "attn_set_index_checks", "attn_check_indices_host"):
         assert n in names
 
 
@@ -66,6 +71,23 @@ def test_library_exports_every_declared_symbol(lib):
     for n in declared_functions():
         assert n in exported, n
         assert hasattr(lib, n)
+
+
+def test_probe_library_exports_its_header():
+    """libattn_probe.so (measured ceilings, not on the attention path) exports
+    every function include/attn_probe.h declares."""
+    path = os.path.join(ROOT, "attention_attn_fwd_10_amd", "libattn_probe.so")
+    if not os.path.exists(path):
+        sys.path.insert(0, ROOT)
+        from attention_attn_fwd_10_amd import build
+        build.build(verbose=False)
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "attn_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["attn_probe_ceilings", "attn_probe_cycles"]
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if " T " in line)
+    for n in names:
+        assert n in exported, n
 
 
 def _s(*v):
@@ -246,3 +268,30 @@ def test_splitkv_num_splits_bounds():
     assert A.splitkv_num_splits(160, 32768) == 16
     assert A.splitkv_num_splits(544, 8192) == 4
     assert A.splitkv_num_splits(32, 131072) >= A.splitkv_num_splits(5000, 131072)
+
+
+def _i32(vals):
+    return (ctypes.c_int32 * len(vals))(*vals) if vals is not None else None
+
+
+def test_index_check_host(lib):
+    """The invariants the varlen kernels rely on, checked on host copies."""
+    def f(cq=(0, 3, 3, 10), ck=(0, 5, 9, 9), table=None, maxp=0, page=0, total_q=10, mq=7, mk=5):
+        B = len(cq) - 1
+        return lib.attn_check_indices_host(_i32(cq), _i32(ck), _i32(table), maxp, page, B, total_q, mq, mk)
+    assert f() == OK
+    assert f(cq=(1, 3, 3, 10)) == INVALID                 # first query offset not 0
+    assert f(ck=(-1, 5, 9, 9)) == INVALID                 # negative key offset
+    assert f(cq=(0, 3, 2, 10)) == INVALID                 # decreasing
+    assert f(ck=(0, 5, 4, 9)) == INVALID
+    assert f(mq=6) == INVALID                             # 7 queries > max_seqlen_q
+    assert f(mk=4) == INVALID                             # 5 keys > max_seqlen_k
+    assert f(total_q=11) == INVALID                       # cu_seqlens_q[B] != total_q
+    assert b"total_q" in lib.attn_last_error()
+    # paged: 3 sequences with 5, 4, 0 keys in 4-token pages -> 2, 1, 0 pages
+    good = [7, 2, -1, 0, -1, -1, -1, -1, -1]
+    assert f(table=good, maxp=3, page=4) == OK            # entries past a sequence's pages are ignored
+    assert f(table=[7, -1, -1, 0, -1, -1, -1, -1, -1], maxp=3, page=4) == INVALID   # needed page < 0
+    assert b"block_table[0][1]" in lib.attn_last_error()
+    assert f(table=[7], maxp=1, page=4) == INVALID        # 2 pages needed, 1 allowed
+    assert f(cq=(0,), ck=(0,), total_q=0) == OK           # no sequences
