@@ -72,10 +72,36 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// max of three (two) floats as one v_max3_f32 (v_max_f32).  Scores are never
+// signalling NaNs, so the quieting that fmaxf wraps around its operands
+// (a v_max x, x each) is not needed; the result is exact, so any order of
+// the operands gives the same bits.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max2f(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// max of the 32 scores of two 16-value score tiles (16 v_max3)
+__device__ __forceinline__ float tile_max32(const f32x16& a, const f32x16& b) {
+  float m = max3f(a[0], a[1], a[2]);
+#pragma unroll
+  for (int r = 3; r < 15; r += 2) m = max3f(m, a[r], a[r + 1]);
+  m = max3f(m, a[15], b[0]);
+#pragma unroll
+  for (int r = 1; r < 15; r += 2) m = max3f(m, b[r], b[r + 1]);
+  return max2f(m, b[15]);
+}
+
 // max / sum of a value with the same lane of the other half-wave (l ^ 32)
 __device__ __forceinline__ float halfwave_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max2f(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float halfwave_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -343,25 +343,25 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
       return key0;
     }
   };
-  // (tile ranges are clamped below 2^31; the host limits seq strides to 2^24
-  // elements, so a tile's 64 rows always lie inside them)
   // (row0: tile_row0(key0), looked up once per tile by the caller)
   // Copies of a tile whose rows are contiguous: one buffer resource from the
   // tile's first row to row Lk (rows past the sequence end read as zeros);
   // round ii adds the byte offset of its key shift to the lane's round-0
   // offset (a scalar, below 2^31 since the shift is < 64 rows).
+  // (a resource covers the tile's own rows, at most 64, so its size fits
+  // 32 bits: 64 rows of at most 2^25 bytes; the copies never address past
+  // row 63 of a tile, and rows past Lk read as zeros)
+  const uint32_t k_rowb = 2u * (uint32_t)a.k_ss, v_rowb = 2u * (uint32_t)a.v_ss;
   auto dma_k_c = [&](int key0, auto buf, int64_t row0) {
     uint16_t* kb = kbuf(buf) + wave * C::KGRP;
-    const uint64_t kn = 2ull * (uint64_t)(Lk - key0) * (uint64_t)a.k_ss;
-    const i32x4 kr = make_rsrc(kg + row0 * a.k_ss, (uint32_t)min(kn, (uint64_t)0x7fff0000u));
+    const i32x4 kr = make_rsrc(kg + row0 * a.k_ss, (uint32_t)min(Lk - key0, BC) * k_rowb);
 #pragma unroll
     for (int ii = 0; ii < C::CI_W; ++ii)
       dma16_buf(kr, k_boff + 2u * (uint32_t)k_key_shift(ii) * (uint32_t)a.k_ss, kb + NW * ii * C::KGRP);
   };
   auto dma_v_c = [&](int key0, auto buf, int64_t row0) {
     uint16_t* vb = vbuf(buf) + wave * C::VGRP;
-    const uint64_t vn = 2ull * (uint64_t)(Lk - key0) * (uint64_t)a.v_ss;
-    const i32x4 vr = make_rsrc(vg + row0 * a.v_ss, (uint32_t)min(vn, (uint64_t)0x7fff0000u));
+    const i32x4 vr = make_rsrc(vg + row0 * a.v_ss, (uint32_t)min(Lk - key0, BC) * v_rowb);
 #pragma unroll
     for (int ii = 0; ii < C::CI_W; ++ii)
       dma16_buf(vr, v_boff + 2u * (uint32_t)v_key_shift(ii) * (uint32_t)a.v_ss, vb + NW * ii * C::VGRP);
@@ -515,18 +515,14 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
           if (bad) s[tt][r] = -INFINITY;
         }
     }
-    float mx = s[0][0];
-#pragma unroll
-    for (int tt = 0; tt < BC / 32; ++tt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tt][r]);
+    const float mx = tile_max32(s[0], s[1]);
     const float mxs = halfwave_max(mx) * c2k;
     // move the running max only when some row's new max exceeds it by > 2^8;
     // the row sum takes alpha in the same fused update as the pipelined tiles
     // (l = fma(l, alpha, psum)), so every path rounds it identically
     float alpha = 1.f;
     if (__builtin_amdgcn_ballot_w64(mxs > m_run + kLazyRescale) != 0) {
-      const float m_new = fmaxf(m_run, mxs);
+      const float m_new = max2f(m_run, mxs);
       alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
@@ -546,7 +542,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
     }
     const float nb = m_run == -INFINITY ? 0.f : -m_run;
     const uint16_t* vs = vbuf(buf) + vtr_off;
-    float psum = 0.f;
+    float psum;  // (starts at the first probability: 0 + p is p exactly)
     // O^T += V^T P^T over four 16-key chunks: the exponentials of a chunk, then
     // its D/32 MFMAs, so the matrix work of one chunk overlaps the next chunk's
     // exponentials
@@ -557,7 +553,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         p[e] = fast_exp2(fmaf(s[tt][r0p + e], c2k, nb));
-        psum += p[e];
+        psum = c == 0 && e == 0 ? p[e] : psum + p[e];
       }
       const u32x4 pk = {pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3]), pack2<DT>(p[4], p[5]),
                         pack2<DT>(p[6], p[7])};
@@ -616,11 +612,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
           if (bad) s[tt][r] = -INFINITY;
         }
     }
-    float mx = s[0][0];
-#pragma unroll
-    for (int tt = 0; tt < BC / 32; ++tt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tt][r]);
+    const float mx = tile_max32(s[0], s[1]);
     mxs = halfwave_max(mx) * c2;
     // move the running max only when some row's new max exceeds it by > 2^8
     return __builtin_amdgcn_ballot_w64(mxs > m_run + kLazyRescale) != 0;
@@ -629,7 +621,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   // alpha in softmax_pv's fused update
   float alpha_pend = 1.f;
   auto rescale = [&]() {
-    const float m_new = fmaxf(m_run, mxs);
+    const float m_new = max2f(m_run, mxs);
     const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
     alpha_pend = alpha;
 #pragma unroll
@@ -654,7 +646,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   auto softmax_pv = [&](int buf) {
     const float nb = m_run == -INFINITY ? 0.f : -m_run;
     const uint16_t* vs = vbuf(buf) + vtr_off;
-    float psum = 0.f;
+    float psum;
 #pragma unroll
     for (int c = 0; c < BC / 16; ++c) {
       const int tt = c >> 1, r0p = 8 * (c & 1);
@@ -662,7 +654,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         p[e] = fast_exp2(fmaf(s[tt][r0p + e], c2, nb));
-        psum += p[e];
+        psum = c == 0 && e == 0 ? p[e] : psum + p[e];
       }
       const u32x4 pk = {pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3]), pack2<DT>(p[4], p[5]),
                         pack2<DT>(p[6], p[7])};
@@ -693,18 +685,14 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   // sum, with no branch; returns whether the running max moved, in which case
   // the accumulators must still be multiplied by alpha
   auto softmax_pack = [&](const f32x16 (&sc)[BC / 32], u32x4 (&pk)[BC / 16], float& alpha) -> bool {
-    float mx = sc[0][0];
-#pragma unroll
-    for (int tt = 0; tt < BC / 32; ++tt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[tt][r]);
+    const float mx = tile_max32(sc[0], sc[1]);
     const float mxs = halfwave_max(mx) * c2;
     const bool moved = __builtin_amdgcn_ballot_w64(mxs > m_run + kLazyRescale) != 0;
-    const float m_new = moved ? fmaxf(m_run, mxs) : m_run;
+    const float m_new = moved ? max2f(m_run, mxs) : m_run;
     const float m_safe = m_new == -INFINITY ? 0.f : m_new;
     alpha = fast_exp2(m_run - m_safe);
     m_run = m_new;
-    float psum = 0.f;
+    float psum;
 #pragma unroll
     for (int c = 0; c < BC / 16; ++c) {
       const int tt = c >> 1, r0p = 8 * (c & 1);
@@ -712,7 +700,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         p[e] = fast_exp2(fmaf(sc[tt][r0p + e], c2, -m_safe));
-        psum += p[e];
+        psum = c == 0 && e == 0 ? p[e] : psum + p[e];
       }
       pk[c] = u32x4{pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3]), pack2<DT>(p[4], p[5]), pack2<DT>(p[6], p[7])};
     }
@@ -784,7 +772,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
             const uint16_t* vs = vbuf(cur) + vtr_off;
             float p[BC / 2];
             u32x4 pk[BC / 16];
-            float psum = 0.f, mx = 0.f, m_safe = 0.f, alpha = 1.f;
+            float psum = 0.f, mx = 0.f, m_safe = 0.f, alpha = 1.f;  // (psum starts at p[0])
             bool moved = false;
             // exponentials [lo, hi) in chunk-major order (value 8c + e is
             // register 8(c%2) + e of score tile c/2); a chunk is packed as soon
@@ -794,7 +782,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
               for (int x = lo; x < hi; ++x) {
                 const int c = x >> 3, e = x & 7;
                 p[x] = fast_exp2(fmaf(sc[c >> 1][8 * (c & 1) + e], c2, -m_safe));
-                psum += p[x];
+                psum = x == 0 ? p[x] : psum + p[x];
                 if (e == 7)
                   pk[c] = u32x4{pack2<DT>(p[x - 7], p[x - 6]), pack2<DT>(p[x - 5], p[x - 4]),
                                 pack2<DT>(p[x - 3], p[x - 2]), pack2<DT>(p[x - 1], p[x])};
@@ -811,19 +799,22 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
               if (i + KPRE < NA)
                 kop[i + KPRE] = *(const u32x4*)(ks + C::krow(32 * ((i + KPRE) & 1)) + 16 * ((i + KPRE) >> 1));
               if (i == 0) {
-                mx = sc[0][0];
+                mx = max3f(sc[0][0], sc[0][1], sc[0][2]);
 #pragma unroll
-                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
+                for (int r = 3; r < 15; r += 2) mx = max3f(mx, sc[0][r], sc[0][r + 1]);
               } else if (i == 1) {
+                mx = max3f(mx, sc[0][15], sc[1][0]);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
+                for (int r = 1; r < 15; r += 2) mx = max3f(mx, sc[1][r], sc[1][r + 1]);
+                mx = max2f(mx, sc[1][15]);
               } else if (i == 2) {
+                // (no mask in these tiles: every score and the new max are
+                // finite, and alpha = 2^(m_old - m_new) is 0 on a row's first tile)
                 const float mxs = halfwave_max(mx) * c2;
                 moved = __builtin_amdgcn_ballot_w64(mxs > m_run + kLazyRescale) != 0;
-                const float m_new = moved ? fmaxf(m_run, mxs) : m_run;
-                m_safe = m_new == -INFINITY ? 0.f : m_new;
+                m_safe = moved ? max2f(m_run, mxs) : m_run;
                 alpha = fast_exp2(m_run - m_safe);
-                m_run = m_new;
+                m_run = m_safe;
               } else {
                 exps((i - 3) * 24 / (NA - 3), (i - 2) * 24 / (NA - 3));
               }
