@@ -25,7 +25,7 @@ import math
 import os
 
 __all__ = ["fwd", "fwd_bias", "fp8_quantize", "fwd_fp8", "int8_quantize", "fwd_int8", "fwd_varlen", "fwd_splitkv",
-           "fwd_splitkv_noalloc", "bwd", "lib_path", "AttnError", "ATTN_BF16", "ATTN_FP16"]
+           "fwd_splitkv_noalloc", "bwd", "set_index_checks", "lib_path", "AttnError", "ATTN_BF16", "ATTN_FP16"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libattn_fwd.so")
@@ -75,6 +75,8 @@ def _load():
     lib.attn_fwd_splitkv_noalloc.restype = I
     lib.attn_fwd_splitkv_workspace_bytes.argtypes = [I, I, I, I]
     lib.attn_fwd_splitkv_workspace_bytes.restype = SZ
+    lib.attn_set_index_checks.argtypes = [I]
+    lib.attn_set_index_checks.restype = None
     lib.attn_status_string.argtypes = [I]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
@@ -96,6 +98,13 @@ class _Library:
 
 
 _lib = _Library()
+
+
+def set_index_checks(enable: bool) -> None:
+    """Debug switch (process-wide, off by default): the varlen, split-key and
+    allocation-free entry points copy cu_seqlens and the block table to the
+    host and validate them before launching (attn_set_index_checks)."""
+    _lib.attn_set_index_checks(int(bool(enable)))
 
 
 def _check(status: int):

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -12,6 +13,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/attn.h"
 #include "bwd.hpp"
@@ -282,9 +284,65 @@ attn_status_t varlen_args(int dtype, const void* q, const int32_t* cu_seqlens_q,
   return ATTN_OK;
 }
 
+std::atomic<bool> g_index_checks{false};
+
+// With index checks on: copy the index arrays to the host (on the call's
+// stream, after the work that produced them) and validate them there.
+attn_status_t check_device_indices(const attn::FwdArgs& a, int B, int total_q, int max_seqlen_q, int max_seqlen_k,
+                                   int page_size, hipStream_t stream) {
+  if (!g_index_checks.load(std::memory_order_relaxed)) return ATTN_OK;
+  std::vector<int32_t> cq(B + 1), ck(B + 1), tab;
+  hipError_t e = hipMemcpyAsync(cq.data(), a.cu_q, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(ck.data(), a.cu_k, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess && a.block_table != nullptr) {
+    tab.resize((size_t)B * a.max_pages);
+    e = hipMemcpyAsync(tab.data(), a.block_table, sizeof(int32_t) * tab.size(), hipMemcpyDeviceToHost, stream);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_status(e, "index check copy");
+  return attn_check_indices_host(cq.data(), ck.data(), a.block_table != nullptr ? tab.data() : nullptr,
+                                 a.max_pages, page_size, B, total_q, max_seqlen_q, max_seqlen_k);
+}
+
 }  // namespace
 
 extern "C" {
+
+void attn_set_index_checks(int enable) { g_index_checks.store(enable != 0, std::memory_order_relaxed); }
+
+attn_status_t attn_check_indices_host(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                      const int32_t* block_table, int max_pages_per_seq, int page_size, int B,
+                                      int total_q, int max_seqlen_q, int max_seqlen_k) {
+  if (B < 0) return fail(ATTN_ERR_INVALID, "negative batch");
+  if (B == 0) return ok();
+  if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return fail(ATTN_ERR_INVALID, "cu_seqlens is NULL");
+  if (cu_seqlens_q[0] != 0) return fail(ATTN_ERR_INVALID, "cu_seqlens_q[0] = %d, not 0", cu_seqlens_q[0]);
+  if (cu_seqlens_k[0] < 0) return fail(ATTN_ERR_INVALID, "cu_seqlens_k[0] = %d is negative", cu_seqlens_k[0]);
+  for (int b = 0; b < B; ++b) {
+    const int64_t lq = (int64_t)cu_seqlens_q[b + 1] - cu_seqlens_q[b];
+    const int64_t lk = (int64_t)cu_seqlens_k[b + 1] - cu_seqlens_k[b];
+    if (lq < 0 || lk < 0) return fail(ATTN_ERR_INVALID, "cu_seqlens decrease at sequence %d", b);
+    if (lq > max_seqlen_q)
+      return fail(ATTN_ERR_INVALID, "sequence %d has %lld queries, above max_seqlen_q %d", b, (long long)lq, max_seqlen_q);
+    if (lk > max_seqlen_k)
+      return fail(ATTN_ERR_INVALID, "sequence %d has %lld keys, above max_seqlen_k %d", b, (long long)lk, max_seqlen_k);
+    if (block_table != nullptr) {
+      if (page_size <= 0) return fail(ATTN_ERR_INVALID, "page_size %d", page_size);
+      const int64_t pages = (lk + page_size - 1) / page_size;
+      if (pages > max_pages_per_seq)
+        return fail(ATTN_ERR_INVALID, "sequence %d needs %lld pages, above max_pages_per_seq %d", b, (long long)pages,
+                    max_pages_per_seq);
+      for (int64_t p = 0; p < pages; ++p)
+        if (block_table[(int64_t)b * max_pages_per_seq + p] < 0)
+          return fail(ATTN_ERR_INVALID, "block_table[%d][%lld] = %d is negative", b, (long long)p,
+                      block_table[(int64_t)b * max_pages_per_seq + p]);
+    }
+  }
+  if (cu_seqlens_q[B] != total_q)
+    return fail(ATTN_ERR_INVALID, "cu_seqlens_q[B] = %d, but total_q is %d", cu_seqlens_q[B], total_q);
+  return ok();
+}
 
 attn_status_t attn_fwd_varlen(int dtype, const void* q, const int32_t* cu_seqlens_q, const void* k, const void* v,
                               const int32_t* cu_seqlens_k, const int32_t* block_table, int max_pages_per_seq,
@@ -297,6 +355,10 @@ attn_status_t attn_fwd_varlen(int dtype, const void* q, const int32_t* cu_seqlen
                                        page_size, o, lse, B, H, D, total_q, max_seqlen_q, max_seqlen_k,
                                        softmax_scale, causal, &a, &mode, &empty);
   if (st != ATTN_OK || empty) return st;
+  if (const attn_status_t ci = check_device_indices(a, B, total_q, max_seqlen_q, max_seqlen_k, page_size,
+                                                    (hipStream_t)stream);
+      ci != ATTN_OK)
+    return ci;
   return hip_status(dispatch_fwd16(a, D, dtype, causal != 0, mode, (hipStream_t)stream), "attn_fwd_varlen launch");
 }
 
@@ -349,6 +411,10 @@ attn_status_t attn_fwd_splitkv(int dtype, const void* q, const int32_t* cu_seqle
                                        page_size, o, lse, B, H, D, total_q, max_seqlen_q, max_seqlen_k,
                                        softmax_scale, causal, &a, &mode, &empty);
   if (st != ATTN_OK || empty) return st;
+  if (const attn_status_t ci = check_device_indices(a, B, total_q, max_seqlen_q, max_seqlen_k, page_size,
+                                                    (hipStream_t)stream);
+      ci != ATTN_OK)
+    return ci;
   if (num_splits == 1)
     return hip_status(dispatch_fwd16(a, D, dtype, causal != 0, mode, (hipStream_t)stream), "attn_fwd_splitkv launch");
   const size_t need = attn_fwd_splitkv_workspace_bytes(total_q, H, D, num_splits);
@@ -372,6 +438,10 @@ attn_status_t attn_fwd_splitkv_noalloc(int dtype, const void* q, const int32_t* 
                                        page_size, o, lse, B, H, D, total_q, max_seqlen_q, max_seqlen_k,
                                        softmax_scale, causal, &a, &mode, &empty);
   if (st != ATTN_OK || empty) return st;
+  if (const attn_status_t ci = check_device_indices(a, B, total_q, max_seqlen_q, max_seqlen_k, page_size,
+                                                    (hipStream_t)stream);
+      ci != ATTN_OK)
+    return ci;
   if (num_splits == 1)
     return hip_status(dispatch_fwd16(a, D, dtype, causal != 0, mode, (hipStream_t)stream),
                       "attn_fwd_splitkv_noalloc launch");

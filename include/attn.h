@@ -312,6 +312,31 @@ attn_status_t attn_bwd(int dtype,
                        int B, int H, int Sq, int Sk, int D,
                        float softmax_scale, int causal, void* stream);
 
+/*
+ * attn_set_index_checks — debug switch for the device-resident index arrays
+ * of attn_fwd_varlen, attn_fwd_splitkv and attn_fwd_splitkv_noalloc, which
+ * are otherwise trusted.  With enable != 0 (process-wide; off by default)
+ * each of those calls first copies cu_seqlens_q, cu_seqlens_k and the block
+ * table to host memory on its stream, waits for the stream, and returns
+ * ATTN_ERR_INVALID (launching nothing) unless attn_check_indices_host
+ * accepts them.  The checked calls synchronise and use host memory.
+ */
+void attn_set_index_checks(int enable);
+
+/*
+ * attn_check_indices_host — the invariants of the index arrays, on HOST
+ * copies: cu_seqlens_q[0] == 0 and cu_seqlens_k[0] >= 0, both non-decreasing,
+ * every sequence's query and key counts within max_seqlen_q / max_seqlen_k,
+ * cu_seqlens_q[B] == total_q, and (block_table != NULL) every sequence's
+ * ceil(Lk / page_size) pages within max_pages_per_seq with non-negative
+ * entries.  (Page ids above the cache's page count cannot be checked: the
+ * library is not told that count.)  Returns ATTN_OK or ATTN_ERR_INVALID with
+ * the first violation in attn_last_error().
+ */
+attn_status_t attn_check_indices_host(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                      const int32_t* block_table, int max_pages_per_seq, int page_size,
+                                      int B, int total_q, int max_seqlen_q, int max_seqlen_k);
+
 /* Human-readable name of a status code (static storage). */
 const char* attn_status_string(int status);
 

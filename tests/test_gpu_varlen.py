@@ -241,3 +241,30 @@ def test_bit_identity_when_running_max_moves(lib, d, causal):
     rows, o_ref, lse_ref = _sample_rows_ref(q, k, v, cu_q, cu_k, lens, lens, causal, heads=[0, 1], seed=43)
     og, lg = _gather(o_pk, lse_pk, rows)
     assert_close16(og, o_ref, lg, lse_ref, f"growing scores d{d} causal={causal}")
+
+
+def test_index_checks_refuse_bad_offsets(lib):
+    """With the debug index checks on, cu_seqlens that break the stated
+    invariants are refused before any launch (the bad cases here would only
+    leave rows unwritten if they ran); valid inputs give the unchecked
+    result bit for bit."""
+    import torch
+    lens = np.array([70, 129, 1], dtype=np.int64)
+    q, k, v, cu_q, cu_k = _pack(lens, lens, 2, 64, 17)
+    tq, tk, tv = to_dev(q), to_dev(k), to_dev(v)
+    o0, l0 = lib.fwd_varlen(tq, _t32(cu_q), tk, tv, _t32(cu_k), 129, 129)
+    lib.set_index_checks(True)
+    try:
+        o1, l1 = lib.fwd_varlen(tq, _t32(cu_q), tk, tv, _t32(cu_k), 129, 129)
+        torch.cuda.synchronize()
+        assert torch.equal(o0, o1) and torch.equal(l0, l1)
+        short = cu_q.copy()
+        short[-1] -= 1                                   # cu_seqlens_q[B] != total_q
+        with pytest.raises(lib.AttnError, match="total_q"):
+            lib.fwd_varlen(tq, _t32(short), tk, tv, _t32(cu_k), 129, 129)
+        with pytest.raises(lib.AttnError, match="max_seqlen_k"):
+            lib.fwd_varlen(tq, _t32(cu_q), tk, tv, _t32(cu_k), 129, 128)
+        with pytest.raises(lib.AttnError, match="max_seqlen_q"):
+            lib.fwd_splitkv(tq, _t32(cu_q), tk, tv, _t32(cu_k), 100, 129, num_splits=2)
+    finally:
+        lib.set_index_checks(False)
