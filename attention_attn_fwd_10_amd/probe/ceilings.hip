@@ -241,7 +241,7 @@ __global__ void __launch_bounds__(256) mix_cycles_kernel(float* out, uint64_t* c
 // products only (four accumulators, bf16 or fp8), waves 4-7 vector
 // instructions only (16 independent exps or fmas per round).  MODE 1 =
 // products alone, 2 = vector alone, 3 = both.  Each wave reports its cycles.
-template <bool FP8, bool EXP, int MODE>
+template <bool FP8, bool EXP, int MODE, bool AGPR = false>
 __global__ void __launch_bounds__(512) pair_cycles_kernel(float* out, uint64_t* cyc, int m_iters, int v_iters) {
   extern __shared__ float lds_hold[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -259,8 +259,17 @@ __global__ void __launch_bounds__(512) pair_cycles_kernel(float* out, uint64_t* 
       for (int it = 0; it < m_iters; ++it)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if constexpr (FP8) acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, a8, acc[j], 0, 0, 0, 127, 0, 127);
-          else acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, ab, acc[j], 0, 0, 0);
+          if constexpr (AGPR) {
+            // accumulators held in AGPRs
+            if constexpr (FP8)
+              asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(acc[j]) : "v"(a8), "v"(a8));
+            else
+              asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[j]) : "v"(ab), "v"(ab));
+          } else if constexpr (FP8) {
+            acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, a8, acc[j], 0, 0, 0, 127, 0, 127);
+          } else {
+            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, ab, acc[j], 0, 0, 0);
+          }
         }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -289,8 +298,48 @@ __global__ void __launch_bounds__(512) pair_cycles_kernel(float* out, uint64_t* 
   if (lane == 0 && blockIdx.x == 0) cyc[(size_t)gridDim.x * 8 + wave] = __builtin_amdgcn_s_getreg((31 << 11) | 4);
 }
 
-}  // namespace probe
+// Vector throughput against waves per SIMD: one workgroup of 4 K waves per
+// CU (K waves on every SIMD), each wave 16 independent chains.  With MFMA,
+// wave 0 of each SIMD issues bf16 products instead (four accumulators).
+template <int OP, bool MFMA>
+__global__ void __launch_bounds__(1024) waves_kernel(float* out, uint64_t* cyc, int iters) {
+  extern __shared__ float lds_hold[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  float s = lds_hold[0] * 0.f;
+  uint64_t t0 = __builtin_amdgcn_s_memtime();
+  if (MFMA && wave < 4) {
+    f32x16 acc[4] = {};
+    i32x4 a4 = {0x3f803f80 ^ lane, 0x3f003f00, 0x3e803e80, 0x3f803f80};
+    const bf16x8 ab = __builtin_bit_cast(bf16x8, a4);
+    t0 = __builtin_amdgcn_s_memtime();
+    for (int it = 0; it < 4 * iters; ++it)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, ab, acc[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s += acc[j][r];
+  } else {
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = 0.01f * (lane + i);
+    const float a = 0.999f, b = 1e-3f;
+    t0 = __builtin_amdgcn_s_memtime();
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if constexpr (OP == kExp) asm volatile("v_exp_f32 %0, %0" : "+v"(x[i]));
+        else asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(x[i]) : "v"(a), "v"(b));
+      }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += x[i];
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+  if (lane == 0) cyc[blockIdx.x * 16 + wave] = t1 - t0;
+}
 
+}  // namespace probe
 
 namespace {
 
@@ -348,8 +397,8 @@ extern "C" int attn_probe_cycles(double* r, int n) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 1;
   float* out = nullptr;
   uint64_t* cyc = nullptr;
-  if (hipMalloc(&out, sizeof(float) * (size_t)cus * 512) != hipSuccess) return 1;
-  if (hipMalloc(&cyc, sizeof(uint64_t) * ((size_t)cus * 8 + 8)) != hipSuccess) {
+  if (hipMalloc(&out, sizeof(float) * (size_t)cus * 1024) != hipSuccess) return 1;
+  if (hipMalloc(&cyc, sizeof(uint64_t) * ((size_t)cus * 16 + 8)) != hipSuccess) {
     (void)hipFree(out);
     return 1;
   }
@@ -387,15 +436,15 @@ extern "C" int attn_probe_cycles(double* r, int n) {
   mix(T{}, T{}, std::integral_constant<int, 8>{}, ATTN_PROBE_CYC_FP8_EXP8);
   mix(T{}, T{}, std::integral_constant<int, 16>{}, ATTN_PROBE_CYC_FP8_EXP16);
   // two waves per SIMD: products beside vector instructions
-  auto pair = [&](auto fp8, auto exp, int slot) {
-    constexpr bool F = decltype(fp8)::value, E = decltype(exp)::value;
+  auto pair = [&](auto fp8, auto exp, int slot, auto agpr) {
+    constexpr bool F = decltype(fp8)::value, E = decltype(exp)::value, G = decltype(agpr)::value;
     const int mi = 1024, vi = 512;
     double m_alone, v_alone;
-    err |= timed([&] { hipLaunchKernelGGL((pair_cycles_kernel<F, E, 1>), dim3(cus), dim3(512), hold, 0, out, cyc, mi, vi); }, &ms);
+    err |= timed([&] { hipLaunchKernelGGL((pair_cycles_kernel<F, E, 1, G>), dim3(cus), dim3(512), hold, 0, out, cyc, mi, vi); }, &ms);
     m_alone = mean_cycles(cyc, cus, 8, 0, 4, &err);
-    err |= timed([&] { hipLaunchKernelGGL((pair_cycles_kernel<F, E, 2>), dim3(cus), dim3(512), hold, 0, out, cyc, mi, vi); }, &ms);
+    err |= timed([&] { hipLaunchKernelGGL((pair_cycles_kernel<F, E, 2, G>), dim3(cus), dim3(512), hold, 0, out, cyc, mi, vi); }, &ms);
     v_alone = mean_cycles(cyc, cus, 8, 4, 4, &err);
-    err |= timed([&] { hipLaunchKernelGGL((pair_cycles_kernel<F, E, 3>), dim3(cus), dim3(512), hold, 0, out, cyc, mi, vi); }, &ms);
+    err |= timed([&] { hipLaunchKernelGGL((pair_cycles_kernel<F, E, 3, G>), dim3(cus), dim3(512), hold, 0, out, cyc, mi, vi); }, &ms);
     r[slot] = m_alone;
     r[slot + 1] = v_alone;
     r[slot + 2] = mean_cycles(cyc, cus, 8, 0, 4, &err);
@@ -407,9 +456,30 @@ extern "C" int attn_probe_cycles(double* r, int n) {
     for (int w = 0; w < 8; ++w) code = code * 16.0 + (double)((ids[w] >> 4) & 3);
     r[ATTN_PROBE_CYC_WAVE_SIMDS] = code;
   };
-  pair(Fa{}, T{}, ATTN_PROBE_CYC_PAIR_BF16_EXP);
-  pair(Fa{}, Fa{}, ATTN_PROBE_CYC_PAIR_BF16_FMA);
-  pair(T{}, T{}, ATTN_PROBE_CYC_PAIR_FP8_EXP);
+  // vector instructions per SIMD per cycle-block against waves per SIMD
+  auto waves = [&](auto op, auto mfma, int k, int slot) {
+    constexpr int OP = decltype(op)::value;
+    constexpr bool M = decltype(mfma)::value;
+    const int vi = 512;
+    err |= timed([&] { hipLaunchKernelGGL((waves_kernel<OP, M>), dim3(cus), dim3(256 * k), hold, 0, out, cyc, vi); }, &ms);
+    // cycles of the vector waves; SIMD cycles per vector instruction
+    const int first = M ? 4 : 0, nvec = 4 * k - first;
+    const double c = mean_cycles(cyc, cus, 16, first, nvec, &err);
+    r[slot] = c / (16.0 * vi * (nvec / 4.0));
+    if (M) r[slot + 1] = mean_cycles(cyc, cus, 16, 0, 4, &err) / (4.0 * 4 * vi);  // cycles per product
+  };
+  for (int k = 1; k <= 4; ++k) {
+    waves(std::integral_constant<int, kFma>{}, Fa{}, k, ATTN_PROBE_CYC_FMA_W1 + k - 1);
+    waves(std::integral_constant<int, kExp>{}, Fa{}, k, ATTN_PROBE_CYC_EXP_W1 + k - 1);
+  }
+  waves(std::integral_constant<int, kFma>{}, T{}, 3, ATTN_PROBE_CYC_MFMA_PLUS_2FMA);
+  waves(std::integral_constant<int, kExp>{}, T{}, 3, ATTN_PROBE_CYC_MFMA_PLUS_2EXP);
+  pair(Fa{}, T{}, ATTN_PROBE_CYC_PAIR_BF16_EXP, Fa{});
+  pair(Fa{}, Fa{}, ATTN_PROBE_CYC_PAIR_BF16_FMA, Fa{});
+  pair(T{}, T{}, ATTN_PROBE_CYC_PAIR_FP8_EXP, Fa{});
+  pair(Fa{}, Fa{}, ATTN_PROBE_CYC_PAIR_BF16_FMA_AGPR, T{});
+  pair(T{}, Fa{}, ATTN_PROBE_CYC_PAIR_FP8_FMA_AGPR, T{});
+  pair(T{}, Fa{}, ATTN_PROBE_CYC_PAIR_FP8_FMA, Fa{});
   (void)hipFree(out);
   (void)hipFree(cyc);
   return err ? 1 : 0;

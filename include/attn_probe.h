@@ -69,7 +69,12 @@ int attn_probe_ceilings(double* r, int n);
  * run together.  SNOP15: counter ticks per `s_nop 15` (16 cycles of the
  * shader clock), which calibrates the counter.  WAVE_SIMDS: the SIMD of each
  * of the 8 waves of one pair workgroup, as 8 hexadecimal digits (wave 0
- * first).
+ * first).  FMA_Wk / EXP_Wk: SIMD cycles per fma / exp instruction with k
+ * waves per SIMD issuing 16 independent chains each.  MFMA_PLUS_2FMA /
+ * MFMA_PLUS_2EXP: the same with three waves per SIMD, one of them issuing
+ * bf16 products instead (four accumulators); the _MFMA entry after each is
+ * that wave's cycles per product.  PAIR_*_AGPR: the pair probes with the
+ * products' accumulators in AGPRs (the _AGPR-less entries use VGPRs).
  */
 enum {
     ATTN_PROBE_CYC_LAT_EXP = 0,
@@ -91,7 +96,22 @@ enum {
     ATTN_PROBE_CYC_PAIR_FP8_EXP = ATTN_PROBE_CYC_PAIR_BF16_FMA + 4,
     ATTN_PROBE_CYC_SNOP15 = ATTN_PROBE_CYC_PAIR_FP8_EXP + 4,
     ATTN_PROBE_CYC_WAVE_SIMDS,
-    ATTN_PROBE_CYC_NUM
+    ATTN_PROBE_CYC_FMA_W1,
+    ATTN_PROBE_CYC_FMA_W2,
+    ATTN_PROBE_CYC_FMA_W3,
+    ATTN_PROBE_CYC_FMA_W4,
+    ATTN_PROBE_CYC_EXP_W1,
+    ATTN_PROBE_CYC_EXP_W2,
+    ATTN_PROBE_CYC_EXP_W3,
+    ATTN_PROBE_CYC_EXP_W4,
+    ATTN_PROBE_CYC_MFMA_PLUS_2FMA,
+    ATTN_PROBE_CYC_MFMA_PLUS_2FMA_MFMA,
+    ATTN_PROBE_CYC_MFMA_PLUS_2EXP,
+    ATTN_PROBE_CYC_MFMA_PLUS_2EXP_MFMA,
+    ATTN_PROBE_CYC_PAIR_BF16_FMA_AGPR,
+    ATTN_PROBE_CYC_PAIR_FP8_FMA_AGPR = ATTN_PROBE_CYC_PAIR_BF16_FMA_AGPR + 4,
+    ATTN_PROBE_CYC_PAIR_FP8_FMA = ATTN_PROBE_CYC_PAIR_FP8_FMA_AGPR + 4,
+    ATTN_PROBE_CYC_NUM = ATTN_PROBE_CYC_PAIR_FP8_FMA + 4
 };
 
 int attn_probe_cycles(double* r, int n);
