@@ -339,6 +339,45 @@ __global__ void __launch_bounds__(1024) waves_kernel(float* out, uint64_t* cyc, 
   if (lane == 0) cyc[blockIdx.x * 16 + wave] = t1 - t0;
 }
 
+
+// LDS read bandwidth: one workgroup of 4 K waves per CU, each wave `iters`
+// rounds of 16 independent reads of 16 bytes per lane (ds_read_b128, TR =
+// false) or of 8 bytes per lane through the transposing read
+// (ds_read_b64_tr_b16, TR = true), consecutive lanes at consecutive addresses
+// (no bank conflicts); the values are folded with xor so that no read is dead.
+template <bool TR>
+__global__ void __launch_bounds__(1024) lds_read_kernel(uint32_t* out, uint64_t* cyc, int iters) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(16))) uint32_t buf[16384];  // 64 KiB
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  for (int i = threadIdx.x; i < 16384; i += blockDim.x) buf[i] = (uint32_t)i * 2654435761u;
+  __syncthreads();
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const int base = (wave & 3) * 4096;  // words: each wave reads its own 16 KiB
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if constexpr (TR) {
+        typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+        const uint32_t* p = buf + base + ((i * 128 + 2 * lane + 2 * it) & 4094);  // 8-byte aligned
+        const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+        const u32x2 u = __builtin_bit_cast(u32x2, v);
+        acc[0] ^= u[0];
+        acc[1] ^= u[1];
+      } else {
+        const u32x4 v = *(const u32x4*)(buf + base + ((i * 256 + 4 * lane + 4 * it) & 4095));
+        acc ^= v;
+      }
+    }
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  out[blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  if (lane == 0) cyc[blockIdx.x * 16 + wave] = t1 - t0;
+}
+
 }  // namespace probe
 
 namespace {
@@ -472,6 +511,20 @@ extern "C" int attn_probe_cycles(double* r, int n) {
     waves(std::integral_constant<int, kFma>{}, Fa{}, k, ATTN_PROBE_CYC_FMA_W1 + k - 1);
     waves(std::integral_constant<int, kExp>{}, Fa{}, k, ATTN_PROBE_CYC_EXP_W1 + k - 1);
   }
+  // LDS bytes read per CU per cycle (over the mean wave's cycle count)
+  auto lds = [&](auto tr, int k, int slot) {
+    constexpr bool TR = decltype(tr)::value;
+    const int li = 256;
+    err |= timed([&] { hipLaunchKernelGGL((lds_read_kernel<TR>), dim3(cus), dim3(256 * k), 0, 0, (uint32_t*)out, cyc, li); }, &ms);
+    const double c = mean_cycles(cyc, cus, 16, 0, 4 * k, &err);
+    r[slot] = (double)(4 * k) * li * 16 * 64 * (TR ? 8 : 16) / c;
+  };
+  lds(Fa{}, 1, ATTN_PROBE_CYC_LDS_B128_W1);
+  lds(Fa{}, 2, ATTN_PROBE_CYC_LDS_B128_W2);
+  lds(Fa{}, 4, ATTN_PROBE_CYC_LDS_B128_W4);
+  lds(T{}, 1, ATTN_PROBE_CYC_LDS_TR16_W1);
+  lds(T{}, 2, ATTN_PROBE_CYC_LDS_TR16_W2);
+  lds(T{}, 4, ATTN_PROBE_CYC_LDS_TR16_W4);
   waves(std::integral_constant<int, kFma>{}, T{}, 3, ATTN_PROBE_CYC_MFMA_PLUS_2FMA);
   waves(std::integral_constant<int, kExp>{}, T{}, 3, ATTN_PROBE_CYC_MFMA_PLUS_2EXP);
   pair(Fa{}, T{}, ATTN_PROBE_CYC_PAIR_BF16_EXP, Fa{});

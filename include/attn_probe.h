@@ -75,6 +75,10 @@ int attn_probe_ceilings(double* r, int n);
  * bf16 products instead (four accumulators); the _MFMA entry after each is
  * that wave's cycles per product.  PAIR_*_AGPR: the pair probes with the
  * products' accumulators in AGPRs (the _AGPR-less entries use VGPRs).
+ * LDS_B128_Wk / LDS_TR16_Wk: bytes read from LDS per CU per cycle with k
+ * waves per SIMD issuing independent conflict-free reads of 16 bytes per lane
+ * (ds_read_b128) or 8 bytes per lane through the transposing read
+ * (ds_read_b64_tr_b16).
  */
 enum {
     ATTN_PROBE_CYC_LAT_EXP = 0,
@@ -111,7 +115,13 @@ enum {
     ATTN_PROBE_CYC_PAIR_BF16_FMA_AGPR,
     ATTN_PROBE_CYC_PAIR_FP8_FMA_AGPR = ATTN_PROBE_CYC_PAIR_BF16_FMA_AGPR + 4,
     ATTN_PROBE_CYC_PAIR_FP8_FMA = ATTN_PROBE_CYC_PAIR_FP8_FMA_AGPR + 4,
-    ATTN_PROBE_CYC_NUM = ATTN_PROBE_CYC_PAIR_FP8_FMA + 4
+    ATTN_PROBE_CYC_LDS_B128_W1 = ATTN_PROBE_CYC_PAIR_FP8_FMA + 4,
+    ATTN_PROBE_CYC_LDS_B128_W2,
+    ATTN_PROBE_CYC_LDS_B128_W4,
+    ATTN_PROBE_CYC_LDS_TR16_W1,
+    ATTN_PROBE_CYC_LDS_TR16_W2,
+    ATTN_PROBE_CYC_LDS_TR16_W4,
+    ATTN_PROBE_CYC_NUM
 };
 
 int attn_probe_cycles(double* r, int n);
