@@ -38,8 +38,10 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
+#include "ring.hpp"
 
 namespace attn {
 
@@ -154,6 +156,16 @@ constexpr bool fwd16_layout_ok() {
 static_assert(fwd16_layout_ok<Fwd16Cfg<64, 4>>() && fwd16_layout_ok<Fwd16Cfg<64, 8>>(), "fwd16 tile layout, head dim 64");
 static_assert(fwd16_layout_ok<Fwd16Cfg<128, 4>>() && fwd16_layout_ok<Fwd16Cfg<128, 8>>(), "fwd16 tile layout, head dim 128");
 static_assert(fwd16_layout_ok<Fwd16Cfg<256, 4>>(), "fwd16 tile layout, head dim 256");
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, unrolled
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Probabilities may grow to 2^kLazyRescale before the running max is moved.
 constexpr float kLazyRescale = 8.0f;
@@ -728,6 +740,45 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   // ---- key loop: two-stage LDS ring; tile j uses stage (j - j0) % 2 --------
   if (j1 > j0) {
     if constexpr (D != 256) {
+      // The ring's schedule (ring.hpp) is executed from its tables: op o of a
+      // table run for tile j acts on tile j + o.d, in stage (j + o.d - j0) %
+      // 2; `par` is the stage of tile j, a compile-time constant in the
+      // pipelined loop and an int in the one-at-a-time loop, and `math(kind,
+      // stage)` does the reads.  The tables are proven free of stage hazards
+      // at compile time (ring.hpp), so no copy, wait or barrier exists outside
+      // them.
+      int jm = j0;  // end of the pipelined tiles
+      auto stage_of = [](auto par, auto dd) {
+        constexpr int DD = decltype(dd)::value;
+        if constexpr (std::is_same_v<decltype(par), int>) return (par + DD) & 1;
+        else return std::integral_constant<int, (decltype(par)::value + DD) & 1>{};
+      };
+      // (contig: the pipelined tiles, whose copies are single buffer loads)
+      auto run = [&](auto table, int j, auto par, auto contig, auto&& math) {
+        using T = decltype(table);
+        static_for<T::size>([&](auto I) {
+          constexpr ring::Op o = T::at(decltype(I)::value);
+          const int t = j + o.d;
+          if (!ring::guard_ok(o.guard, t - j0, jm - j0, j1 - j0)) return;
+          const auto st = stage_of(par, std::integral_constant<int, o.d>{});
+          if constexpr (o.kind == ring::kCopyK) {
+            if constexpr (decltype(contig)::value) dma_k_c(t * BC, st, tile_row0(t * BC));
+            else dma_k(t * BC, st, contiguous ? tile_row0(t * BC) : 0);
+          } else if constexpr (o.kind == ring::kCopyV) {
+            if constexpr (decltype(contig)::value) dma_v_c(t * BC, st, tile_row0(t * BC));
+            else dma_v(t * BC, st, contiguous ? tile_row0(t * BC) : 0);
+          } else if constexpr (o.kind == ring::kCopyKV) {
+            static_assert(!decltype(contig)::value, "the pipelined tables copy K and V separately");
+            dma_tile(t * BC, st);
+          } else if constexpr (o.kind == ring::kWait) {
+            wait_vmem();
+          } else if constexpr (o.kind == ring::kSync) {
+            __syncthreads();
+          } else {
+            math(std::integral_constant<int, o.kind>{}, st);
+          }
+        });
+      };
       int jg = j0;  // first tile of the generic loop below
       // (not with a score bias, and for paged caches only with pages of >= 64
       // tokens, whose tiles are copied like contiguous ones: the registers of
@@ -738,7 +789,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
         // units, the same wave issues the score MFMAs of tile j+1; then P V of
         // tile j.  K and V copies are a step apart (K(j+2) and V(j+1) land
         // during step j), so the ring keeps two stages of each.
-        int jm = CAUSAL ? (qs + diag + 1) / BC : Lk / BC;
+        jm = CAUSAL ? (qs + diag + 1) / BC : Lk / BC;
         jm = min(j1, max(j0, jm));
         if (jm > j0) {
           constexpr std::integral_constant<int, 0> S0{};
@@ -746,18 +797,16 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
           f32x16 sa[BC / 32], sb[BC / 32];
           // (a tile's first row: its first key, or for a paged cache its
           // page's base plus the slot, one table read per copied tile)
-          dma_k_c(j0 * BC, S0, tile_row0(j0 * BC));
-          dma_v_c(j0 * BC, S0, tile_row0(j0 * BC));
-          if (j0 + 1 < j1) dma_k_c((j0 + 1) * BC, S1, tile_row0((j0 + 1) * BC));  // (j0 + 1 <= jm)
-          wait_vmem();
-          __syncthreads();
-          // waves whose rows all lie past the sequence end only copy and
-          // synchronise (with one query row, as in decoding, three of four)
-          if (wave_active) qk_tile(S0, sa);
-          // the first step copies K(j0 + 2) into stage 0: every wave must have
-          // read K(j0) from it first (waves with no rows skip the read and
-          // would otherwise overwrite the stage while it is still being read)
-          __syncthreads();
+          // prologue: K(j0), V(j0), K(j0 + 1); the scores of tile j0.  Waves
+          // whose rows all lie past the sequence end only copy and
+          // synchronise (with one query row, as in decoding, three of four).
+          // The first step copies K(j0 + 2) into stage 0, so a barrier
+          // separates the scores from it: every wave must have read K(j0)
+          // first (waves with no rows skip the read and would otherwise
+          // overwrite the stage while it is still being read).
+          run(ring::Table<ring::kPrologue>{}, j0, S0, std::true_type{}, [&](auto, auto st) {
+            if (wave_active) qk_tile(st, sa);
+          });
           // One step with the next tile's scores overlapped (needs j + 1 < jm).
           // The order of the work is fixed by scheduling fences: region A
           // issues the NA score MFMAs of tile j+1, and after each one a share
@@ -847,23 +896,20 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
             }
           };
           auto step = [&](int j, auto cur, auto nxt, f32x16 (&sc)[BC / 32], f32x16 (&sn)[BC / 32]) {
-            if (j + 2 <= jm && j + 2 < j1) dma_k_c((j + 2) * BC, cur, tile_row0((j + 2) * BC));
-            dma_v_c((j + 1) * BC, nxt, tile_row0((j + 1) * BC));
-            if (wave_active) step_math(cur, nxt, sc, sn);
-            wait_vmem();
-            __syncthreads();
+            run(ring::Table<ring::kStep>{}, j, cur, std::true_type{}, [&](auto, auto) {
+              if (wave_active) step_math(cur, nxt, sc, sn);
+            });
           };
           // the last pipelined tile: softmax and P V only
-          auto last = [&](int j, auto cur, auto nxt, f32x16 (&sc)[BC / 32]) {
-            if (j + 1 < j1) dma_v_c((j + 1) * BC, nxt, tile_row0((j + 1) * BC));
-            if (wave_active) {
-              u32x4 pk[BC / 16];
-              float alpha;
-              if (softmax_pack(sc, pk, alpha)) scale_acc(alpha);
-              pv_tile(cur, pk);
-            }
-            wait_vmem();
-            __syncthreads();
+          auto last = [&](int j, auto cur, f32x16 (&sc)[BC / 32]) {
+            run(ring::Table<ring::kLast>{}, j, cur, std::true_type{}, [&](auto, auto) {
+              if (wave_active) {
+                u32x4 pk[BC / 16];
+                float alpha;
+                if (softmax_pack(sc, pk, alpha)) scale_acc(alpha);
+                pv_tile(cur, pk);
+              }
+            });
           };
           int j = j0;
           for (; j + 2 < jm; j += 2) {
@@ -872,26 +918,20 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
           }
           if (j + 1 < jm) {
             step(j, S0, S1, sa, sb);
-            last(j + 1, S1, S0, sb);
+            last(j + 1, S1, sb);
           } else {
-            last(j, S0, S1, sa);
+            last(j, S0, sa);
           }
           jg = jm;  // tile jm (if any) is in stage (jm - j0) % 2
         }
       }
-      if (jg == j0) {
-        dma_tile(j0 * BC, 0);
-        wait_vmem();
-        __syncthreads();
-      }
+      // tiles one at a time (tile j + 1 lands while tile j is computed)
+      if (jg == j0) run(ring::Table<ring::kTileStart>{}, j0, 0, std::false_type{}, [](auto, auto) {});
       for (int j = jg; j < j1; ++j) {
         const int buf = (j - j0) & 1;
         BiasRaw br{};
         if constexpr (BIAS) br = bias_fetch(j * BC);
-        if (j + 1 < j1) dma_tile((j + 1) * BC, buf ^ 1);  // lands while tile j is computed
-        compute(j * BC, buf, br);
-        wait_vmem();
-        __syncthreads();
+        run(ring::Table<ring::kTile>{}, j, buf, std::false_type{}, [&](auto, auto st) { compute(j * BC, st, br); });
       }
     } else {
       dma_tile(j0 * BC, 0);

@@ -1,0 +1,57 @@
+// Mutations of the K/V ring schedule tables of the 16-bit forward, each of
+// which the compile-time hazard checker must reject; the unmutated tables
+// must pass.  Prints one line per case: "<name> <0|1>" (1 = schedule ok).
+#include <cstdio>
+
+#include "../attention_attn_fwd_10_amd/csrc/ring.hpp"
+
+using namespace attn::ring;
+
+int main() {
+  int bad = 0;
+  auto report = [&](const char* name, bool ok, bool expect) {
+    std::printf("%s %d\n", name, ok ? 1 : 0);
+    if (ok != expect) ++bad;
+  };
+  report("tables", schedule_ok_all(kPrologue, kStep, kLast, kTileStart, kTile), true);
+
+  // the prologue without the barrier between the scores of tile 0 and the
+  // first step's copy of K2 into the same stage
+  constexpr Op pro_no_second_sync[] = {{kCopyK, 0, kAlways}, {kCopyV, 0, kAlways}, {kCopyK, 1, kLtTotal},
+                                       {kWait, 0, kAlways},  {kSync, 0, kAlways},  {kScores, 0, kAlways}};
+  report("prologue_without_second_barrier", schedule_ok_all(pro_no_second_sync, kStep, kLast, kTileStart, kTile), false);
+  // the prologue without the wait for its copies
+  constexpr Op pro_no_wait[] = {{kCopyK, 0, kAlways}, {kCopyV, 0, kAlways}, {kCopyK, 1, kLtTotal},
+                                {kSync, 0, kAlways},  {kScores, 0, kAlways}, {kSync, 0, kAlways}};
+  report("prologue_without_wait", schedule_ok_all(pro_no_wait, kStep, kLast, kTileStart, kTile), false);
+  // a step without its barrier, or without its wait
+  constexpr Op step_no_sync[] = {{kCopyK, 2, kLePipeLtTotal}, {kCopyV, 1, kAlways}, {kStepMath, 0, kAlways},
+                                 {kWait, 0, kAlways}};
+  report("step_without_barrier", schedule_ok_all(kPrologue, step_no_sync, kLast, kTileStart, kTile), false);
+  constexpr Op step_no_wait[] = {{kCopyK, 2, kLePipeLtTotal}, {kCopyV, 1, kAlways}, {kStepMath, 0, kAlways},
+                                 {kSync, 0, kAlways}};
+  report("step_without_wait", schedule_ok_all(kPrologue, step_no_wait, kLast, kTileStart, kTile), false);
+  // a step copying K one tile ahead instead of two (into the stage it reads)
+  constexpr Op step_k_one_ahead[] = {{kCopyK, 1, kLePipeLtTotal}, {kCopyV, 1, kAlways}, {kStepMath, 0, kAlways},
+                                     {kWait, 0, kAlways},        {kSync, 0, kAlways}};
+  report("step_copies_k_one_ahead", schedule_ok_all(kPrologue, step_k_one_ahead, kLast, kTileStart, kTile), false);
+  // a step that copies V(j+1) only after its math (same interval as the reads
+  // of other waves: still a write into a stage nobody reads this step, so
+  // this one is allowed), and one that copies V(j) (read this step)
+  constexpr Op step_v_current[] = {{kCopyK, 2, kLePipeLtTotal}, {kCopyV, 0, kAlways}, {kStepMath, 0, kAlways},
+                                   {kWait, 0, kAlways},        {kSync, 0, kAlways}};
+  report("step_copies_v_of_its_own_tile", schedule_ok_all(kPrologue, step_v_current, kLast, kTileStart, kTile), false);
+  constexpr Op step_v_late[] = {{kCopyK, 2, kLePipeLtTotal}, {kStepMath, 0, kAlways}, {kCopyV, 1, kAlways},
+                                {kWait, 0, kAlways},        {kSync, 0, kAlways}};
+  report("step_copies_v_after_math", schedule_ok_all(kPrologue, step_v_late, kLast, kTileStart, kTile), true);
+  // the last pipelined tile without its barrier (the one-at-a-time loop then
+  // refills the stage the last tile reads)
+  constexpr Op last_no_sync[] = {{kCopyV, 1, kLtTotal}, {kLastMath, 0, kAlways}, {kWait, 0, kAlways}};
+  report("last_without_barrier", schedule_ok_all(kPrologue, kStep, last_no_sync, kTileStart, kTile), false);
+  // the one-at-a-time loop without its barrier, and copying its own tile
+  constexpr Op tile_no_sync[] = {{kCopyKV, 1, kLtTotal}, {kTileMath, 0, kAlways}, {kWait, 0, kAlways}};
+  report("tile_without_barrier", schedule_ok_all(kPrologue, kStep, kLast, kTileStart, tile_no_sync), false);
+  constexpr Op tile_own[] = {{kCopyKV, 0, kLtTotal}, {kTileMath, 0, kAlways}, {kWait, 0, kAlways}, {kSync, 0, kAlways}};
+  report("tile_copies_its_own_tile", schedule_ok_all(kPrologue, kStep, kLast, kTileStart, tile_own), false);
+  return bad;
+}
