@@ -16,8 +16,8 @@
 #include <vector>
 
 #include "../../include/attn.h"
+#include "args.hpp"
 #include "bwd.hpp"
-#include "common.hpp"
 
 namespace attn {
 template <int D, int DT, bool CAUSAL, int MODE>
@@ -57,6 +57,10 @@ attn_status_t hip_status(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// a * b * c > INT32_MAX for non-negative factors below 2^62, without overflow
+// (a grid size: workgroups per launch)
+bool grid_too_large(int64_t a, int64_t b, int64_t c) { return (__int128)a * b * c > INT32_MAX; }
 
 attn_status_t check_strides(const char* name, const int64_t* s) {
   if (s == nullptr) return fail(ATTN_ERR_INVALID, "%s_strides is NULL", name);
@@ -165,8 +169,8 @@ attn_status_t dense_args(int dtype, const void* q, const int64_t q_strides[3], c
     return fail(ATTN_ERR_UNSUPPORTED, "k/v sequence strides above 2^24 elements are not supported");
   if (!aligned16(q) || !aligned16(o) || !aligned16(k) || !aligned16(v) || !aligned16(lse))
     return fail(ATTN_ERR_INVALID, "q, k, v, o and lse must be 16-byte aligned");
-  const int64_t n_qblk = (Sq + kBR - 1) / kBR;
-  if ((int64_t)B * H * n_qblk > INT32_MAX) return fail(ATTN_ERR_INVALID, "problem too large for one launch");
+  const int64_t n_qblk = ((int64_t)Sq + kBR - 1) / kBR;
+  if (grid_too_large(B, H, n_qblk)) return fail(ATTN_ERR_INVALID, "problem too large for one launch");
 
   *a = attn::FwdArgs{};
   a->q = q; a->k = k; a->v = v; a->o = o; a->lse = lse;
@@ -214,7 +218,7 @@ attn_status_t attn_fwd_bias(int dtype, const void* q, const int64_t q_strides[3]
       return fail(ATTN_ERR_INVALID, "bias strides must be non-negative multiples of 8 elements");
   if (empty) return ok();
   if (Sk > 0 && (bias == nullptr || !aligned16(bias))) return fail(ATTN_ERR_INVALID, "bias must be a 16-byte aligned pointer");
-  if (2 * ((int64_t)(Sq - 1) * bias_strides[2] + ((Sk + 7) & ~7)) >= (int64_t(1) << 31))
+  if (2 * ((int64_t)(Sq - 1) * bias_strides[2] + (((int64_t)Sk + 7) & ~int64_t(7))) >= (int64_t(1) << 31))
     return fail(ATTN_ERR_UNSUPPORTED, "one (batch, head) plane of the bias must span less than 2^31 bytes");
   a.bias = bias;
   a.bias_sb = bias_strides[0]; a.bias_sh = bias_strides[1]; a.bias_ss = bias_strides[2];
@@ -262,8 +266,8 @@ attn_status_t varlen_args(int dtype, const void* q, const int32_t* cu_seqlens_q,
   if ((int64_t)H * D > kMaxSeqStride) return fail(ATTN_ERR_UNSUPPORTED, "H * head_dim above 2^24 elements");
   if (!aligned16(q) || !aligned16(o) || !aligned16(k) || !aligned16(v) || !aligned16(lse))
     return fail(ATTN_ERR_INVALID, "q, k, v, o and lse must be 16-byte aligned");
-  const int64_t n_qblk = (max_seqlen_q + kBR - 1) / kBR;
-  if ((int64_t)B * H * n_qblk > INT32_MAX || (int64_t)H * ((total_q + kBR - 1) / kBR + B) > INT32_MAX)
+  const int64_t n_qblk = ((int64_t)max_seqlen_q + kBR - 1) / kBR;
+  if (grid_too_large(B, H, n_qblk) || grid_too_large(H, ((int64_t)total_q + kBR - 1) / kBR + B, 1))
     return fail(ATTN_ERR_INVALID, "problem too large for one launch");
 
   *a = attn::FwdArgs{};
@@ -371,9 +375,9 @@ namespace {
 attn_status_t splitkv_launch(attn::FwdArgs a, int mode, int dtype, int D, int causal, int num_splits, float* part,
                              const char* name, hipStream_t stream) {
   const int total_q = a.total_q, H = a.H, B = a.B;
-  if ((int64_t)H * ((total_q + kBR - 1) / kBR + B) * num_splits > INT32_MAX)
+  if (grid_too_large(H, ((int64_t)total_q + kBR - 1) / kBR + B, num_splits))
     return fail(ATTN_ERR_INVALID, "problem too large for one launch");
-  const int tiles = (a.Sk + 63) / 64;
+  const int tiles = (int)(((int64_t)a.Sk + 63) / 64);
   a.n_split = num_splits;
   a.split_tiles = (tiles + num_splits - 1) / num_splits;
   a.part_o = part;
@@ -471,7 +475,7 @@ static attn_status_t quantize_8bit(const char* name, quant_launcher_t launch, co
   if (B == 0 || H == 0 || S == 0) return ok();
   if (x == nullptr || x8 == nullptr || scales == nullptr) return fail(ATTN_ERR_INVALID, "x, x8 or scales is NULL");
   if (!aligned16(x) || !aligned16(x8)) return fail(ATTN_ERR_INVALID, "x and x8 must be 16-byte aligned");
-  if ((int64_t)B * H * ((S + 127) / 128) > INT32_MAX) return fail(ATTN_ERR_INVALID, "problem too large");
+  if (grid_too_large(B, H, ((int64_t)S + 127) / 128)) return fail(ATTN_ERR_INVALID, "problem too large");
   attn::QuantArgs a{};
   a.x = (const uint16_t*)x;
   a.x_sb = x_strides[0]; a.x_ss = x_strides[1]; a.x_sh = x_strides[2];
@@ -511,8 +515,8 @@ static attn_status_t fwd_8bit(const char* name, fwd8_launcher_t launch, const ui
     return fail(ATTN_ERR_INVALID, "k8, v8 or their scales are NULL");
   if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) || !aligned16(lse))
     return fail(ATTN_ERR_INVALID, "q8, k8, v8, o and lse must be 16-byte aligned");
-  const int64_t n_qblk = (Sq + kBR - 1) / kBR;
-  if ((int64_t)B * H * n_qblk > INT32_MAX) return fail(ATTN_ERR_INVALID, "problem too large for one launch");
+  const int64_t n_qblk = ((int64_t)Sq + kBR - 1) / kBR;
+  if (grid_too_large(B, H, n_qblk)) return fail(ATTN_ERR_INVALID, "problem too large for one launch");
   attn::Fp8Args a{};
   a.q = q8; a.k = k8; a.v = v8; a.qs = q_scale; a.ks = k_scale; a.vs = v_scale;
   a.o = o; a.lse = lse;
@@ -557,7 +561,7 @@ attn_status_t attn_bwd(int dtype, const void* q, const void* k, const void* v, c
       !aligned16(dk) || !aligned16(dv) || !aligned16(lse) || !aligned16(workspace))
     return fail(ATTN_ERR_INVALID, "every tensor must be 16-byte aligned");
   if ((int64_t)H * D > kMaxSeqStride) return fail(ATTN_ERR_INVALID, "H * D too large");
-  if ((int64_t)B * H * ((std::max(Sq, Sk) + kBR - 1) / kBR) > INT32_MAX)
+  if (grid_too_large(B, H, ((int64_t)std::max(Sq, Sk) + kBR - 1) / kBR))
     return fail(ATTN_ERR_INVALID, "problem too large for one launch");
   attn::BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
