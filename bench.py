@@ -31,6 +31,7 @@ PEAK_HBM_GBS = 8000.0
 
 # sources of the timed kernel; the committed counter summary names their hash
 KERNEL_SOURCES = ("attention_attn_fwd_10_amd/csrc/fwd16.hpp", "attention_attn_fwd_10_amd/csrc/common.hpp",
+                  "attention_attn_fwd_10_amd/csrc/args.hpp", "attention_attn_fwd_10_amd/csrc/ring.hpp",
                   "attention_attn_fwd_10_amd/csrc/fwd16_d128.hip")
 TRAFFIC_PROFILE = "profiles/fwd16_d128_bf16_b4_h16_s8448.md"
 
@@ -84,6 +85,9 @@ def parse():
                    help="skip the extra workload points (seq-8192 headline, seq-512 GB/s, varlen+paged, causal fp8)")
     p.add_argument("--no-ceilings", action="store_true", help="skip the measured-ceiling probes and clock")
     p.add_argument("--source-hash", action="store_true", help="print the timed kernel's source hash and exit")
+    p.add_argument("--short-points", action="store_true",
+                   help="only the short-sequence points (seq 512 at d64/128/256, causal and not) and the varlen "
+                        "workload, --warmup then --steps launches each, one JSON line (for counter passes)")
     p.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (calibrates the FETCH_SIZE/WRITE_SIZE counters)")
     return p.parse_args()
@@ -182,6 +186,10 @@ def main():
     import torch
     import attention_attn_fwd_10_amd as A
     import workloads as W
+
+    if args.short_points:
+        print(json.dumps(short_points(A, W, args)), flush=True)
+        return
 
     w = W.WORKLOADS["ablation"]
     if args.causal:
@@ -439,7 +447,34 @@ def bench_points(A, W, args):
     return out
 
 
-def bench_varlen(A, W, steps):
+def short_points(A, W, args):
+    """The short-sequence points of the 16384-token sweep (seq 512: 32
+    sequences, 16 heads, d64/128/256, causal and not) and the varlen workload
+    (packed and paged), timed with HIP events; algorithmic bytes are Q, K, V
+    read and O, LSE written once.  In launch order, so that a counter pass
+    over this run maps its dispatches to the points."""
+    import torch
+    out = {"metric": "short-sequence forward, algorithmic GB/s", "steps": args.steps, "warmup": args.warmup,
+           "points": {}}
+    for w in W.seq_sweep_points():
+        if w.seq_q != 512:
+            continue
+        qs, _ = w.shapes()
+        g = torch.Generator(device="cuda").manual_seed(w.seed)
+        q, k, v = (torch.randn(qs, generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.batch, w.heads, w.seq_q), dtype=torch.float32, device="cuda")
+        ms = time_launches(lambda: A.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse), args.steps, args.warmup)
+        byts = 4 * q.numel() * 2 + 4 * w.batch * w.heads * w.seq_q
+        out["points"][w.name] = {"ms": round(ms, 4), "algorithmic_bytes": byts,
+                                 "gbs": round(byts / (ms * 1e-3) / 1e9, 1)}
+        print(f"[bench] {w.name}: {ms:.4f} ms {out['points'][w.name]['gbs']} GB/s", file=sys.stderr, flush=True)
+        del q, k, v, o
+    out["varlen_paged"] = bench_varlen(A, W, args.steps, args.warmup)
+    return out
+
+
+def bench_varlen(A, W, steps, warmup=10):
     """32 sequences U{128..4096} (seed 5), 32 heads, d128, causal: packed and
     with 64-token pages at permuted slots."""
     import torch
@@ -467,14 +502,17 @@ def bench_varlen(A, W, steps):
     mx = int(lens.max())
     o = torch.empty_like(q)
     lse = torch.empty((H, tot), dtype=torch.float32, device="cuda")
-    res = {"workload": f"varlen_32seq_u128_4096_h{H}_d{D}_causal", "tokens": tot, "flops": flops}
+    byts = 4 * tot * H * D * 2 + 4 * H * tot  # Q, K, V read, O written (bf16); LSE (fp32)
+    res = {"workload": f"varlen_32seq_u128_4096_h{H}_d{D}_causal", "tokens": tot, "flops": flops,
+           "algorithmic_bytes": byts}
     for name, kk, vv, bt in (("packed", k, v, None), ("paged64", kp, vp, tab)):
         ms = time_launches(lambda: A.fwd_varlen(q, cu, kk, vv, cu, mx, mx, None, True, block_table=bt,
                                                 page_size=page if bt is not None else 0, out=o, lse=lse),
-                           steps, 10)
+                           steps, warmup)
         tf = flops / (ms * 1e-3) / 1e12
         res[f"ms_{name}"] = round(ms, 4)
         res[f"tflops_{name}"] = round(tf, 1)
+        res[f"gbs_{name}"] = round(byts / (ms * 1e-3) / 1e9, 1)
         print(f"[bench] varlen {name}: {ms:.3f} ms {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
     return res
 
