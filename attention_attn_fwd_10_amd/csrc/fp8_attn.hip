@@ -272,6 +272,9 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
   float l_run = 0.f;        // this half-wave's share of sum p * 2^kMu (float32 terms)
   float lq_run = 0.f;       // sum over all 64 keys of the e4m3-rounded terms (full row, both halves)
   float sv_ref = 0.f;       // V scale the accumulator is expressed in
+  // sv_ref / sv and log2(sv / sv_ref) of the current 128-key V scale block
+  // (both tiles of a block share them; sv_ref only moves on a block's first)
+  float inv_vratio = 1.f, lv = 0.f;
   const f32x16 zero16 = {};
   // e4m3 1.0 in every byte; kept in registers across the key loop
   i32x8 ones;
@@ -363,8 +366,12 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
     // p'' = 2^(c2 s - m + kMu) * sv / sv_ref is what enters the MFMA; the sum
     // keeps p' = p'' * sv_ref / sv (approximate reciprocals: both factors only
     // need to be consistent to float precision)
-    const float vratio = sv * __builtin_amdgcn_rcpf(sv_ref), inv_vratio = sv_ref * __builtin_amdgcn_rcpf(sv);
-    float bias = m_run == -INFINITY ? 0.f : kMu + __log2f(vratio) - m_run;
+    if (blocked ? (key0 & 127) == 0 : j == 0) {
+      const float vratio = sv * __builtin_amdgcn_rcpf(sv_ref);
+      inv_vratio = sv_ref * __builtin_amdgcn_rcpf(sv);
+      lv = __log2f(vratio);
+    }
+    float bias = m_run == -INFINITY ? 0.f : kMu + lv - m_run;
     // the int8 score offset enters once per tile: kSOff * c2 is rounded once,
     // a shift shared by the whole tile of at most one score unit
     if constexpr (QK_I8) bias -= kSOff * c2;
