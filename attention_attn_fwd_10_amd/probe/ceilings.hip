@@ -341,11 +341,11 @@ __global__ void __launch_bounds__(1024) waves_kernel(float* out, uint64_t* cyc, 
 
 
 // LDS read bandwidth: one workgroup of 4 K waves per CU, each wave `iters`
-// rounds of 16 independent reads of 16 bytes per lane (ds_read_b128, TR =
-// false) or of 8 bytes per lane through the transposing read
-// (ds_read_b64_tr_b16, TR = true), consecutive lanes at consecutive addresses
+// rounds of 16 independent reads of 16 bytes per lane (ds_read_b128, TR = 0)
+// or of 8 bytes per lane through a transposing read (ds_read_b64_tr_b16, TR
+// = 1; ds_read_b64_tr_b8, TR = 2), consecutive lanes at consecutive addresses
 // (no bank conflicts); the values are folded with xor so that no read is dead.
-template <bool TR>
+template <int TR>
 __global__ void __launch_bounds__(1024) lds_read_kernel(uint32_t* out, uint64_t* cyc, int iters) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -360,10 +360,18 @@ __global__ void __launch_bounds__(1024) lds_read_kernel(uint32_t* out, uint64_t*
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if constexpr (TR) {
+      if constexpr (TR == 1) {
         typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
         const uint32_t* p = buf + base + ((i * 128 + 2 * lane + 2 * it) & 4094);  // 8-byte aligned
         const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+        const u32x2 u = __builtin_bit_cast(u32x2, v);
+        acc[0] ^= u[0];
+        acc[1] ^= u[1];
+      } else if constexpr (TR == 2) {
+        typedef int v2i __attribute__((vector_size(8)));
+        typedef __attribute__((address_space(3))) v2i lds_v2i;
+        const uint32_t* p = buf + base + ((i * 128 + 2 * lane + 2 * it) & 4094);  // 8-byte aligned
+        const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p));
         const u32x2 u = __builtin_bit_cast(u32x2, v);
         acc[0] ^= u[0];
         acc[1] ^= u[1];
@@ -376,6 +384,50 @@ __global__ void __launch_bounds__(1024) lds_read_kernel(uint32_t* out, uint64_t*
   const uint64_t t1 = __builtin_amdgcn_s_memtime();
   out[blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
   if (lane == 0) cyc[blockIdx.x * 16 + wave] = t1 - t0;
+}
+
+
+// Asynchronous global -> LDS copies (buffer_load_dwordx4 ... lds, 16 bytes
+// per lane, 1 KB per wave instruction): one workgroup of 8 waves per CU,
+// each wave `iters` rounds of 8 copies into its own 8 KB of LDS, then a wait
+// for them.  The source is one buffer resource of `bytes` per workgroup at
+// `stride` bytes from the previous workgroup's (stride 0: every CU copies the
+// same bytes, which then come from L2; a stride past the data: HBM); a wave
+// walks its slice round by round, wrapping inside the resource, so every copy
+// stays in bounds.  Per wave: the cycles of the whole loop (cyc[.. + 0]) and
+// of the copy instructions' issue alone (cyc[.. + 16]).
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ void buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) void* lds, int size, int voffset,
+                                int soffset, int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+__global__ void __launch_bounds__(512) lds_dma_kernel(const uint8_t* src, uint32_t bytes, uint32_t stride,
+                                                       uint64_t* cyc, int iters) {
+  __shared__ __attribute__((aligned(16))) uint8_t lbuf[8 * 8192];  // 8 KB per wave
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const uint64_t base = (uint64_t)(src + (uint64_t)blockIdx.x * stride);
+  const i32x4 rsrc = {(int)(uint32_t)base, (int)((uint32_t)(base >> 32) & 0xffffu), (int)bytes, 0x00020000};
+  const uint32_t slice = bytes / 8192u;  // 8 KB slices in the resource
+  uint64_t issue = 0;
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+    const uint32_t off0 = ((uint32_t)(wave + 8 * it) % slice) * 8192u + 16u * (uint32_t)lane;
+    __builtin_amdgcn_sched_barrier(0);
+    const uint64_t a = __builtin_amdgcn_s_memtime();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(lbuf + wave * 8192 + i * 1024), 16,
+                      (int)(off0 + 1024u * (uint32_t)i), 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint64_t b = __builtin_amdgcn_s_memtime();
+    __builtin_amdgcn_sched_barrier(0);
+    issue += b - a;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  if (lane == 0) {
+    cyc[blockIdx.x * 32 + wave] = t1 - t0;
+    cyc[blockIdx.x * 32 + 16 + wave] = issue;
+  }
 }
 
 }  // namespace probe
@@ -437,7 +489,7 @@ extern "C" int attn_probe_cycles(double* r, int n) {
   float* out = nullptr;
   uint64_t* cyc = nullptr;
   if (hipMalloc(&out, sizeof(float) * (size_t)cus * 1024) != hipSuccess) return 1;
-  if (hipMalloc(&cyc, sizeof(uint64_t) * ((size_t)cus * 16 + 8)) != hipSuccess) {
+  if (hipMalloc(&cyc, sizeof(uint64_t) * ((size_t)cus * 32 + 8)) != hipSuccess) {
     (void)hipFree(out);
     return 1;
   }
@@ -513,18 +565,47 @@ extern "C" int attn_probe_cycles(double* r, int n) {
   }
   // LDS bytes read per CU per cycle (over the mean wave's cycle count)
   auto lds = [&](auto tr, int k, int slot) {
-    constexpr bool TR = decltype(tr)::value;
+    constexpr int TR = decltype(tr)::value;
     const int li = 256;
     err |= timed([&] { hipLaunchKernelGGL((lds_read_kernel<TR>), dim3(cus), dim3(256 * k), 0, 0, (uint32_t*)out, cyc, li); }, &ms);
     const double c = mean_cycles(cyc, cus, 16, 0, 4 * k, &err);
     r[slot] = (double)(4 * k) * li * 16 * 64 * (TR ? 8 : 16) / c;
   };
-  lds(Fa{}, 1, ATTN_PROBE_CYC_LDS_B128_W1);
-  lds(Fa{}, 2, ATTN_PROBE_CYC_LDS_B128_W2);
-  lds(Fa{}, 4, ATTN_PROBE_CYC_LDS_B128_W4);
-  lds(T{}, 1, ATTN_PROBE_CYC_LDS_TR16_W1);
-  lds(T{}, 2, ATTN_PROBE_CYC_LDS_TR16_W2);
-  lds(T{}, 4, ATTN_PROBE_CYC_LDS_TR16_W4);
+  using M0 = std::integral_constant<int, 0>;
+  using M1 = std::integral_constant<int, 1>;
+  using M2 = std::integral_constant<int, 2>;
+  lds(M0{}, 1, ATTN_PROBE_CYC_LDS_B128_W1);
+  lds(M0{}, 2, ATTN_PROBE_CYC_LDS_B128_W2);
+  lds(M0{}, 4, ATTN_PROBE_CYC_LDS_B128_W4);
+  lds(M1{}, 1, ATTN_PROBE_CYC_LDS_TR16_W1);
+  lds(M1{}, 2, ATTN_PROBE_CYC_LDS_TR16_W2);
+  lds(M1{}, 4, ATTN_PROBE_CYC_LDS_TR16_W4);
+  lds(M2{}, 1, ATTN_PROBE_CYC_LDS_TR8_W1);
+  lds(M2{}, 2, ATTN_PROBE_CYC_LDS_TR8_W2);
+  lds(M2{}, 4, ATTN_PROBE_CYC_LDS_TR8_W4);
+  // global -> LDS copies, 2 waves per SIMD: from L2 (every CU copies the same
+  // 256 KB) and streaming from HBM (each CU its own 4 MB, 1 GB in all)
+  {
+    const uint32_t l2_bytes = 256u << 10, hbm_bytes = 4u << 20;
+    uint8_t* src = nullptr;
+    const size_t total = (size_t)cus * hbm_bytes;
+    if (hipMalloc(&src, total) != hipSuccess) {
+      err = 1;
+    } else {
+      err |= hipMemset(src, 0, total) != hipSuccess;
+      auto dma = [&](uint32_t bytes, uint32_t stride, int slot) {
+        const int di = 256;
+        err |= timed([&] { hipLaunchKernelGGL(lds_dma_kernel, dim3(cus), dim3(512), 0, 0, src, bytes, stride, cyc, di); }, &ms);
+        const double c = mean_cycles(cyc, cus, 32, 0, 8, &err), iss = mean_cycles(cyc, cus, 32, 16, 8, &err);
+        r[slot] = 8.0 * di * 8 * 1024 / c;          // bytes per CU per cycle
+        r[slot + 1] = iss / (8.0 * di);             // issue cycles per copy instruction
+        r[slot + 2] = (double)cus * 8 * di * 8 * 1024 / (ms * 1e-3) / 1e9;  // GB/s, whole chip
+      };
+      dma(l2_bytes, 0, ATTN_PROBE_CYC_DMA_L2);
+      dma(hbm_bytes, hbm_bytes, ATTN_PROBE_CYC_DMA_HBM);
+      (void)hipFree(src);
+    }
+  }
   waves(std::integral_constant<int, kFma>{}, T{}, 3, ATTN_PROBE_CYC_MFMA_PLUS_2FMA);
   waves(std::integral_constant<int, kExp>{}, T{}, 3, ATTN_PROBE_CYC_MFMA_PLUS_2EXP);
   pair(Fa{}, T{}, ATTN_PROBE_CYC_PAIR_BF16_EXP, Fa{});

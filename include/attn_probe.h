@@ -78,7 +78,12 @@ int attn_probe_ceilings(double* r, int n);
  * LDS_B128_Wk / LDS_TR16_Wk: bytes read from LDS per CU per cycle with k
  * waves per SIMD issuing independent conflict-free reads of 16 bytes per lane
  * (ds_read_b128) or 8 bytes per lane through the transposing read
- * (ds_read_b64_tr_b16).
+ * (ds_read_b64_tr_b16; LDS_TR8_Wk: ds_read_b64_tr_b8).  DMA_L2 / DMA_HBM:
+ * asynchronous global -> LDS copies (buffer_load_dwordx4 ... lds, 1 KB per
+ * wave instruction) with two waves per SIMD, each wave issuing 8 copies and
+ * waiting for them, from a 256 KB source every CU shares (L2) or from 4 MB
+ * per CU (HBM); three entries each: bytes per CU per cycle, cycles a wave
+ * spends issuing one copy instruction, and chip-wide GB/s.
  */
 enum {
     ATTN_PROBE_CYC_LAT_EXP = 0,
@@ -121,7 +126,12 @@ enum {
     ATTN_PROBE_CYC_LDS_TR16_W1,
     ATTN_PROBE_CYC_LDS_TR16_W2,
     ATTN_PROBE_CYC_LDS_TR16_W4,
-    ATTN_PROBE_CYC_NUM
+    ATTN_PROBE_CYC_LDS_TR8_W1,
+    ATTN_PROBE_CYC_LDS_TR8_W2,
+    ATTN_PROBE_CYC_LDS_TR8_W4,
+    ATTN_PROBE_CYC_DMA_L2,
+    ATTN_PROBE_CYC_DMA_HBM = ATTN_PROBE_CYC_DMA_L2 + 3,
+    ATTN_PROBE_CYC_NUM = ATTN_PROBE_CYC_DMA_HBM + 3
 };
 
 int attn_probe_cycles(double* r, int n);
