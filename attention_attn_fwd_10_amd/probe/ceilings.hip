@@ -388,7 +388,7 @@ __global__ void __launch_bounds__(1024) lds_read_kernel(uint32_t* out, uint64_t*
 
 
 // Asynchronous global -> LDS copies (buffer_load_dwordx4 ... lds, 16 bytes
-// per lane, 1 KB per wave instruction): one workgroup of 8 waves per CU,
+// per lane, 1 KB per wave instruction): one workgroup of up to 8 waves per CU,
 // each wave `iters` rounds of 8 copies into its own 8 KB of LDS, then a wait
 // for them.  The source is one buffer resource of `bytes` per workgroup at
 // `stride` bytes from the previous workgroup's (stride 0: every CU copies the
@@ -593,16 +593,17 @@ extern "C" int attn_probe_cycles(double* r, int n) {
       err = 1;
     } else {
       err |= hipMemset(src, 0, total) != hipSuccess;
-      auto dma = [&](uint32_t bytes, uint32_t stride, int slot) {
+      auto dma = [&](uint32_t bytes, uint32_t stride, int waves, int slot) {
         const int di = 256;
-        err |= timed([&] { hipLaunchKernelGGL(lds_dma_kernel, dim3(cus), dim3(512), 0, 0, src, bytes, stride, cyc, di); }, &ms);
-        const double c = mean_cycles(cyc, cus, 32, 0, 8, &err), iss = mean_cycles(cyc, cus, 32, 16, 8, &err);
-        r[slot] = 8.0 * di * 8 * 1024 / c;          // bytes per CU per cycle
-        r[slot + 1] = iss / (8.0 * di);             // issue cycles per copy instruction
-        r[slot + 2] = (double)cus * 8 * di * 8 * 1024 / (ms * 1e-3) / 1e9;  // GB/s, whole chip
+        err |= timed([&] { hipLaunchKernelGGL(lds_dma_kernel, dim3(cus), dim3(64 * waves), 0, 0, src, bytes, stride, cyc, di); }, &ms);
+        const double c = mean_cycles(cyc, cus, 32, 0, waves, &err), iss = mean_cycles(cyc, cus, 32, 16, waves, &err);
+        r[slot] = (double)waves * di * 8 * 1024 / c;  // bytes per CU per cycle
+        r[slot + 1] = iss / (8.0 * di);               // issue cycles per copy instruction
+        r[slot + 2] = (double)cus * waves * di * 8 * 1024 / (ms * 1e-3) / 1e9;  // GB/s, whole chip
       };
-      dma(l2_bytes, 0, ATTN_PROBE_CYC_DMA_L2);
-      dma(hbm_bytes, hbm_bytes, ATTN_PROBE_CYC_DMA_HBM);
+      dma(l2_bytes, 0, 8, ATTN_PROBE_CYC_DMA_L2);
+      dma(hbm_bytes, hbm_bytes, 8, ATTN_PROBE_CYC_DMA_HBM);
+      dma(l2_bytes, 0, 1, ATTN_PROBE_CYC_DMA_L2_ONE_WAVE);
       (void)hipFree(src);
     }
   }

@@ -82,8 +82,9 @@ int attn_probe_ceilings(double* r, int n);
  * asynchronous global -> LDS copies (buffer_load_dwordx4 ... lds, 1 KB per
  * wave instruction) with two waves per SIMD, each wave issuing 8 copies and
  * waiting for them, from a 256 KB source every CU shares (L2) or from 4 MB
- * per CU (HBM); three entries each: bytes per CU per cycle, cycles a wave
- * spends issuing one copy instruction, and chip-wide GB/s.
+ * per CU (HBM); DMA_L2_ONE_WAVE: the L2 case with one wave per CU; three
+ * entries each: bytes per CU per cycle, cycles a wave spends issuing one copy
+ * instruction, and chip-wide GB/s.
  */
 enum {
     ATTN_PROBE_CYC_LAT_EXP = 0,
@@ -131,7 +132,8 @@ enum {
     ATTN_PROBE_CYC_LDS_TR8_W4,
     ATTN_PROBE_CYC_DMA_L2,
     ATTN_PROBE_CYC_DMA_HBM = ATTN_PROBE_CYC_DMA_L2 + 3,
-    ATTN_PROBE_CYC_NUM = ATTN_PROBE_CYC_DMA_HBM + 3
+    ATTN_PROBE_CYC_DMA_L2_ONE_WAVE = ATTN_PROBE_CYC_DMA_HBM + 3,
+    ATTN_PROBE_CYC_NUM = ATTN_PROBE_CYC_DMA_L2_ONE_WAVE + 3
 };
 
 int attn_probe_cycles(double* r, int n);
