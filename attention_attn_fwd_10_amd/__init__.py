@@ -4,7 +4,8 @@ Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``libattn_fwd.so``.  torch supplies device memory and the stream.
 The entry points mirror the C ABI in ``include/attn.h``:
 
-* ``fwd``            -> ``attn_fwd``            (bf16 / fp16, optional causal mask)
+* ``fwd``            -> ``attn_fwd_ws``         (bf16 / fp16, optional causal mask; the
+  workspace for a split tail of the grid, sized by ``attn_fwd_workspace_bytes``)
 * ``fp8_quantize``   -> ``attn_fp8_quantize``   (rotation + e4m3 block quantisation)
 * ``fwd_fp8``        -> ``attn_fwd_fp8``        (e4m3 forward with per-block scales)
 * ``int8_quantize``  -> ``attn_int8_quantize``  (rotation + int8 block quantisation)
@@ -69,6 +70,10 @@ def _load():
     lib.attn_fwd_varlen.argtypes = [I, P, P, P, P, P, P, I, I, P, P, I, I, I, I, I, I, F, I, P]
     lib.attn_fwd_varlen.restype = I
     SZ = ctypes.c_size_t
+    lib.attn_fwd_ws.argtypes = [I, P, I64P, P, I64P, P, I64P, P, I64P, P, I, I, I, I, I, F, I, P, SZ, P]
+    lib.attn_fwd_ws.restype = I
+    lib.attn_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.attn_fwd_workspace_bytes.restype = SZ
     lib.attn_fwd_splitkv.argtypes = [I, P, P, P, P, P, P, I, I, P, P, I, I, I, I, I, I, F, I, I, P, SZ, P]
     lib.attn_fwd_splitkv.restype = I
     lib.attn_fwd_splitkv_noalloc.argtypes = [I, P, P, P, P, P, P, I, I, P, P, I, I, I, I, I, I, F, I, I, P]
@@ -162,11 +167,14 @@ def _scale_shape(B, H, S, block_rows):
     return (B, H, (S + 127) // 128) if block_rows else (1,)
 
 
-def fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None, return_lse=True, stream=None):
+def fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None, return_lse=True, stream=None,
+        workspace=None):
     """Fused attention forward.  q [B, Sq, H, D], k/v [B, Sk, H, D] (bf16 or
-    fp16, head_dim contiguous).  Returns (o [B, Sq, H, D], lse [B, H, Sq] fp32)."""
+    fp16, head_dim contiguous).  The fp32 workspace of a split grid tail is
+    allocated here (through torch's allocator) unless given.  Returns
+    (o [B, Sq, H, D], lse [B, H, Sq] fp32)."""
     import torch
-    _require_cuda(q, k, v, out, lse)
+    _require_cuda(q, k, v, out, lse, workspace)
     B, Sq, H, D = q.shape
     Sk = k.shape[1]
     if k.shape != (B, Sk, H, D) or v.shape != (B, Sk, H, D):
@@ -183,9 +191,14 @@ def fwd(q, k, v, softmax_scale=None, causal=False, out=None, lse=None, return_ls
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     if lse is not None:
         _require(lse, "lse", (B, H, Sq), torch.float32)
-    _check(_lib.attn_fwd(_dtype_code(q.dtype), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
-                         _ptr(out), _strides(out), _ptr(lse), B, H, Sq, Sk, D, scale, int(bool(causal)),
-                         _stream(stream)))
+    with torch.cuda.device(q.device):
+        need = int(_lib.attn_fwd_workspace_bytes(_dtype_code(q.dtype), B, H, Sq, Sk, D, int(bool(causal))))
+        if workspace is None and need > 0:
+            workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _check(_lib.attn_fwd_ws(_dtype_code(q.dtype), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
+                                _strides(v), _ptr(out), _strides(out), _ptr(lse), B, H, Sq, Sk, D, scale,
+                                int(bool(causal)), _ptr(workspace), ws_bytes, _stream(stream)))
     return out, lse
 
 

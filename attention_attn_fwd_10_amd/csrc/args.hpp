@@ -15,7 +15,12 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kBF16 = 0;
 constexpr int kFP16 = 1;
 
-enum KvMode { kDense = 0, kVarlen = 1, kPaged = 2, kDenseBias = 3 };
+// kDenseWide: the dense layout in workgroups of 256 query rows (8 waves, one
+// workgroup per CU, each K/V tile copied once for all of them; non-causal,
+// head dim 128); the work items of a last, partial round of the grid may run
+// as key ranges (FwdArgs tail_start) whose partial results a merge combines.
+enum KvMode { kDense = 0, kVarlen = 1, kPaged = 2, kDenseBias = 3, kDenseWide = 4 };
+constexpr int kWideRows = 256;  // query rows per kDenseWide workgroup
 
 struct FwdArgs {
   const void* q;
@@ -47,6 +52,14 @@ struct FwdArgs {
   int split_tiles;
   float* part_o;             // [n_split, total_q, H, D]
   float* part_lse;           // [n_split, H, total_q]
+  // kDenseWide: work items (logical tiles) [0, tail_start) run whole, in
+  // workgroups [0, tail_start); every later item runs as n_split key ranges of
+  // split_tiles tiles, item tail_start + u in workgroups tail_start +
+  // u * n_split + split, and writes its partial output and logsumexp to
+  // part_o [n_split, n_tail * kWideRows, D] / part_lse [n_split, n_tail *
+  // kWideRows] (n_tail = B * H * n_qblk - tail_start); tail_start = B * H *
+  // n_qblk when nothing is split
+  int tail_start;
 };
 
 struct MergeArgs {
@@ -55,6 +68,17 @@ struct MergeArgs {
   void* o;                // [total_q, H, D] bf16 / fp16
   float* lse;             // [H, total_q] or null
   int n_split, total_q, H;
+};
+
+// merge of the split tail of a kDenseWide launch: tail row r = u * kWideRows
+// + i is row i of work item tail_start + u, written to the dense O / LSE
+struct TailMergeArgs {
+  const float* part_o;    // [n_split, n_tail * kWideRows, D]
+  const float* part_lse;  // [n_split, n_tail * kWideRows]
+  void* o;                // [B, Sq, H, D] by the strides below, bf16 / fp16
+  float* lse;             // [B, H, Sq] or null
+  int64_t o_sb, o_ss, o_sh;
+  int H, Sq, n_qblk, tail_start, n_tail, n_split;
 };
 
 struct Fp8Args {

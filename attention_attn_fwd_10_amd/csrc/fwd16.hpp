@@ -47,12 +47,13 @@ namespace attn {
 
 // Waves per workgroup: 8 (256 query rows, one workgroup per CU, each K/V tile
 // copied once for all 8 waves) for the dense causal layout at head dims up to
-// 128, where it measured faster; otherwise 4 (128 rows, two workgroups per CU
-// whose waves run out of phase), which measured faster without the mask, suits
-// the packed layouts, whose sequences may be short, and is the only choice at
-// head dim 256, where a SIMD holds one wave.
+// 128 and for the wide dense layout (kDenseWide), where they measured faster;
+// otherwise 4 (128 rows, two workgroups per CU), which suits the packed
+// layouts, whose sequences may be short, runs a grid that does not fill whole
+// rounds of one-workgroup-per-CU slots with a shorter tail, and is the only
+// choice at head dim 256, where a SIMD holds one wave.
 constexpr int fwd16_waves(int D, int MODE, bool CAUSAL) {
-  return D <= 128 && CAUSAL && (MODE == 0 || MODE == 3) ? 8 : 4;
+  return MODE == kDenseWide || (D <= 128 && CAUSAL && (MODE == kDense || MODE == kDenseBias)) ? 8 : 4;
 }
 
 template <int D, int NW = 4>
@@ -156,6 +157,7 @@ constexpr bool fwd16_layout_ok() {
 static_assert(fwd16_layout_ok<Fwd16Cfg<64, 4>>() && fwd16_layout_ok<Fwd16Cfg<64, 8>>(), "fwd16 tile layout, head dim 64");
 static_assert(fwd16_layout_ok<Fwd16Cfg<128, 4>>() && fwd16_layout_ok<Fwd16Cfg<128, 8>>(), "fwd16 tile layout, head dim 128");
 static_assert(fwd16_layout_ok<Fwd16Cfg<256, 4>>(), "fwd16 tile layout, head dim 256");
+static_assert(Fwd16Cfg<128, 8>::BR == kWideRows, "rows of a wide workgroup");
 
 // f(integral_constant<int, I>) for I = 0 .. N-1, unrolled
 template <class F, int... I>
@@ -176,8 +178,10 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   constexpr int NW = fwd16_waves(D, MODE, CAUSAL);
   using C = Fwd16Cfg<D, NW>;
   constexpr int BR = C::BR, BC = C::BC, CPR = C::CPR;
-  constexpr bool DENSE = MODE == kDense || MODE == kDenseBias;
+  constexpr bool DENSE = MODE == kDense || MODE == kDenseBias || MODE == kDenseWide;
   constexpr bool BIAS = MODE == kDenseBias;
+  constexpr bool WIDE = MODE == kDenseWide;
+  static_assert(!WIDE || (D == 128 && !CAUSAL), "the wide dense layout is the non-causal forward at head dim 128");
   static_assert(!BIAS || D <= 128, "the score bias is supported up to head dim 128");
   // The two stages of the K and V rings are separate arrays: when a stage is
   // named by a compile-time constant, the compiler can tell the copies into
@@ -202,8 +206,20 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
 
   // ---- work item: (b, h, query block) -------------------------------------
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  int b, h, qblk, split = 0;
+  // Wide layout: workgroups [0, tail_start) run work items [0, tail_start)
+  // whole (XCD-remapped); each later work item runs as n_split workgroups,
+  // one key range each (the tail of the grid, spread over every CU).
+  int t, split = 0;
+  bool tail = false;
+  if (WIDE && (int)blockIdx.x >= a.tail_start) {
+    const int u = (int)blockIdx.x - a.tail_start;
+    t = a.tail_start + u / a.n_split;
+    split = u - (u / a.n_split) * a.n_split;
+    tail = true;
+  } else {
+    t = xcd_remap(blockIdx.x, WIDE ? a.tail_start : (int)gridDim.x);
+  }
+  int b, h, qblk;
   if constexpr (DENSE) {
     const int bh = t / a.n_qblk;
     qblk = t - bh * a.n_qblk;
@@ -266,6 +282,10 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   }
   // key tiles [j0, j1) of this work item (all of them unless keys are split)
   int j0 = 0, j1 = n_kv;
+  if (WIDE && tail) {
+    j0 = min(n_kv, split * a.split_tiles);
+    j1 = min(n_kv, j0 + a.split_tiles);
+  }
   if constexpr (!DENSE) {
     if (a.n_split > 1) {
       j0 = min(n_kv, split * a.split_tiles);
@@ -970,27 +990,39 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
 
   // ---- epilogue: o / l, lse = ln2 * (m + log2 l) -----------------------------
   const float l_tot = halfwave_sum(l_run);
+  // partial result of a key range, in fp32, at pp (this row's D values) and
+  // pl (its logsumexp); register r of tile dt is head-dim column 32dt +
+  // 16(r/8) + 8hh + r%8
+  auto store_partial = [&](float* pp, float* pl) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    pp += 8 * hh;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const f32x16& o = oacc[dt];
+        const int r0p = 8 * half;
+        float* dst = pp + 32 * dt + 16 * half;
+        *(f32x4*)dst = f32x4{o[r0p] * inv, o[r0p + 1] * inv, o[r0p + 2] * inv, o[r0p + 3] * inv};
+        *(f32x4*)(dst + 4) = f32x4{o[r0p + 4] * inv, o[r0p + 5] * inv, o[r0p + 6] * inv, o[r0p + 7] * inv};
+      }
+    if (hh == 0) *pl = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  };
+  if constexpr (WIDE) {
+    if (tail) {
+      if (qi < Lq) {
+        const int64_t n_rows = ((int64_t)a.B * a.H * a.n_qblk - a.tail_start) * BR;
+        const int64_t row = (int64_t)split * n_rows + (int64_t)(t - a.tail_start) * BR + (qi - qs);
+        store_partial(a.part_o + row * D, a.part_lse + row);
+      }
+      return;
+    }
+  }
   if constexpr (!DENSE) {
     if (a.n_split > 1) {
-      // partial result of this key split, in fp32; register r of tile dt is
-      // head-dim column 32dt + 16(r/8) + 8hh + r%8
       if (qi < Lq) {
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         const int64_t row = (int64_t)split * a.total_q + (lse_base - (int64_t)h * a.total_q) + qi;
-        float* pp = a.part_o + (row * a.H + h) * D + 8 * hh;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const f32x16& o = oacc[dt];
-            const int r0p = 8 * half;
-            float* dst = pp + 32 * dt + 16 * half;
-            *(f32x4*)dst = f32x4{o[r0p] * inv, o[r0p + 1] * inv, o[r0p + 2] * inv, o[r0p + 3] * inv};
-            *(f32x4*)(dst + 4) = f32x4{o[r0p + 4] * inv, o[r0p + 5] * inv, o[r0p + 6] * inv, o[r0p + 7] * inv};
-          }
-        if (hh == 0)
-          a.part_lse[(int64_t)split * a.H * a.total_q + lse_base + qi] =
-              l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+        store_partial(a.part_o + (row * a.H + h) * D, a.part_lse + (int64_t)split * a.H * a.total_q + lse_base + qi);
       }
       return;
     }
@@ -1021,6 +1053,10 @@ hipError_t launch_fwd16(FwdArgs a, hipStream_t s) {
   if constexpr (MODE == kDense || MODE == kDenseBias) {
     a.n_qblk = (a.Sq + BR - 1) / BR;
     n = a.B * a.H * a.n_qblk;
+  } else if constexpr (MODE == kDenseWide) {
+    // (n_qblk, tail_start and the split are set by the caller, which sizes
+    // the partial results)
+    n = a.tail_start + (a.B * a.H * a.n_qblk - a.tail_start) * a.n_split;
   } else {
     n = a.H * ((a.total_q + BR - 1) / BR + a.B) * max(a.n_split, 1);
   }
@@ -1033,6 +1069,10 @@ hipError_t launch_fwd16(FwdArgs a, hipStream_t s) {
   template hipError_t launch_fwd16<D, kBF16, true, kDenseBias>(FwdArgs, hipStream_t);  \
   template hipError_t launch_fwd16<D, kFP16, false, kDenseBias>(FwdArgs, hipStream_t); \
   template hipError_t launch_fwd16<D, kFP16, true, kDenseBias>(FwdArgs, hipStream_t);
+
+#define ATTN_INSTANTIATE_FWD16_WIDE(D)                                                       \
+  template hipError_t launch_fwd16<D, kBF16, false, kDenseWide>(FwdArgs, hipStream_t); \
+  template hipError_t launch_fwd16<D, kFP16, false, kDenseWide>(FwdArgs, hipStream_t);
 
 #define ATTN_INSTANTIATE_FWD16(D)                                          \
   template hipError_t launch_fwd16<D, kBF16, false, kDense>(FwdArgs, hipStream_t);  \

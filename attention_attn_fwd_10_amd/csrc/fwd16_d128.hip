@@ -4,4 +4,5 @@
 namespace attn {
 ATTN_INSTANTIATE_FWD16(128)
 ATTN_INSTANTIATE_FWD16_BIAS(128)
+ATTN_INSTANTIATE_FWD16_WIDE(128)
 }  // namespace attn

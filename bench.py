@@ -32,7 +32,8 @@ PEAK_HBM_GBS = 8000.0
 # sources of the timed kernel; the committed counter summary names their hash
 KERNEL_SOURCES = ("attention_attn_fwd_10_amd/csrc/fwd16.hpp", "attention_attn_fwd_10_amd/csrc/common.hpp",
                   "attention_attn_fwd_10_amd/csrc/args.hpp", "attention_attn_fwd_10_amd/csrc/ring.hpp",
-                  "attention_attn_fwd_10_amd/csrc/fwd16_d128.hip")
+                  "attention_attn_fwd_10_amd/csrc/fwd16_d128.hip", "attention_attn_fwd_10_amd/csrc/splitkv.hip",
+                  "attention_attn_fwd_10_amd/csrc/api.cpp")
 TRAFFIC_PROFILE = "profiles/fwd16_d128_bf16_b4_h16_s8448.md"
 
 
@@ -229,7 +230,8 @@ def main():
         "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": counter_traffic(),
-                     "kernel": "fwd16_kernel<128, bf16, non-causal, dense>",
+                     "kernel": "fwd16_kernel<128, bf16, non-causal, dense wide> (256-row workgroups; the "
+                               "step also runs the split tail's merge)",
                      "algorithmic_bytes": algo_bytes},
     }
 

@@ -79,6 +79,44 @@ attn_status_t attn_fwd(int dtype,
                        float softmax_scale, int causal, void* stream);
 
 /*
+ * attn_fwd_ws — attn_fwd with a workspace, which lets the non-causal forward
+ * at head dim 128 (4096 keys or more) split the last, partial round of its
+ * grid by keys.
+ * (The "Fused attention kernel" page's implementation sketch keeps a running
+ * row max and row sum per query, so the partial results of key ranges merge
+ * exactly through their logsumexps, as for attn_fwd_splitkv.)
+ *
+ * That forward runs in 256-row workgroups, one per compute unit.  When their
+ * number is not a multiple of the device's compute units, the last round
+ * would leave most of them idle; with a workspace, the work items of that
+ * round instead run as up to 8 key ranges each, over the whole device, and a
+ * merge combines them (two extra fp32 roundings of those rows' outputs).
+ *
+ * Arguments as for attn_fwd, plus:
+ * workspace: device memory of at least attn_fwd_workspace_bytes(...) bytes
+ *   for the same sizes, on the current device, 16-byte aligned, owned by the
+ *   caller, free for this call only (it holds fp32 partial outputs and
+ *   logsumexps).  workspace_bytes is its size; a smaller non-NULL workspace is
+ *   an error.  NULL runs the schedule that needs none: attn_fwd itself.
+ */
+attn_status_t attn_fwd_ws(int dtype,
+                          const void* q, const int64_t q_strides[3],
+                          const void* k, const int64_t k_strides[3],
+                          const void* v, const int64_t v_strides[3],
+                          void* o, const int64_t o_strides[3],
+                          float* lse,
+                          int B, int H, int Sq, int Sk, int D,
+                          float softmax_scale, int causal,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace attn_fwd_ws uses for these sizes on the current device (it
+ * depends on the device's compute-unit count): 0 when the problem has no
+ * split tail (causal, head dim other than 128, fewer than 4096 keys, a grid
+ * of whole rounds, a last round more than half full, or invalid sizes), else
+ * splits * tail_items * 256 * (D + 1) * 4 bytes. */
+size_t attn_fwd_workspace_bytes(int dtype, int B, int H, int Sq, int Sk, int D, int causal);
+
+/*
  * attn_fwd_bias — attn_fwd with an additive score bias: s = scale <q, k> +
  * bias[b, h, i, j] before the causal mask and the softmax (Bias is among the
  * features the StreamHPC case study, section "Our approach", adds to its

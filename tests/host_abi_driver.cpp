@@ -23,6 +23,15 @@ hipError_t hipMemcpyAsync(void* dst, const void* src, size_t bytes, hipMemcpyKin
   return hipSuccess;
 }
 hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
+static const int g_cus = 256;  // compute units the stand-in device reports
+hipError_t hipGetDevice(int* device) {
+  *device = 0;
+  return hipSuccess;
+}
+hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t, int) {
+  *value = g_cus;
+  return hipSuccess;
+}
 const char* hipGetErrorString(hipError_t e) { return e == hipSuccess ? "hipSuccess" : "hipError"; }
 
 // ---- recording launchers --------------------------------------------------------
@@ -49,9 +58,19 @@ INST(64, 0, false) INST(64, 0, true) INST(64, 1, false) INST(64, 1, true)
 INST(128, 0, false) INST(128, 0, true) INST(128, 1, false) INST(128, 1, true)
 INST(256, 0, false) INST(256, 0, true) INST(256, 1, false) INST(256, 1, true)
 #undef INST
+template hipError_t launch_fwd16<128, 0, false, kDenseWide>(FwdArgs, hipStream_t);
+template hipError_t launch_fwd16<128, 1, false, kDenseWide>(FwdArgs, hipStream_t);
 hipError_t launch_fp8_quantize(const QuantArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_int8_quantize(const QuantArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_splitkv_merge(const MergeArgs&, int, int, hipStream_t) { ++g_launches; return hipSuccess; }
+}  // namespace attn
+static attn::TailMergeArgs g_tail;
+namespace attn {
+hipError_t launch_tail_merge(const TailMergeArgs& a, int, int, hipStream_t) {
+  ++g_launches;
+  g_tail = a;
+  return hipSuccess;
+}
 hipError_t launch_fwd_fp8(const Fp8Args&, int, bool, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_fwd_int8(const Fp8Args&, int, bool, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_bwd(const BwdArgs&, int, int, bool, hipStream_t) { ++g_launches; return hipSuccess; }
@@ -108,6 +127,60 @@ int main() {
   expect("fwd_too_large", attn_fwd(ATTN_BF16, p, st, p, st, p, st, p, st, lse, INT_MAX, INT_MAX, INT_MAX, 2, 128, sc, 0, nullptr), ATTN_ERR_INVALID);
   const int64_t big[3] = {0, int64_t(1) << 25, 128};
   expect("fwd_huge_kv_stride", attn_fwd(ATTN_BF16, p, st, p, big, p, big, p, st, lse, 1, 4, 2, 2, 128, sc, 0, nullptr), ATTN_ERR_UNSUPPORTED);
+
+  // dense forward with a workspace: the wide layout and its split tail (the
+  // stand-in device has 256 compute units)
+  {
+    const int64_t wst[3] = {8448LL * 8 * 128, 8 * 128, 128};  // [1, 8448, 8, 128]
+    const size_t want = size_t(8) * 8 * 256 * 129 * 4;       // 8 splits x 8 tail items x 256 rows x (D + 1) floats
+    expect("ws_bytes_tail", attn_fwd_workspace_bytes(ATTN_BF16, 1, 8, 8448, 8448, 128, 0) == want, 1);
+    expect("ws_bytes_causal", (int)attn_fwd_workspace_bytes(ATTN_BF16, 1, 8, 8448, 8448, 128, 1), 0);
+    expect("ws_bytes_d256", (int)attn_fwd_workspace_bytes(ATTN_BF16, 1, 8, 8448, 8448, 256, 0), 0);
+    expect("ws_bytes_whole_rounds", (int)attn_fwd_workspace_bytes(ATTN_BF16, 1, 8, 8192, 8192, 128, 0), 0);
+    expect("ws_bytes_invalid", (int)attn_fwd_workspace_bytes(ATTN_BF16, -1, 8, 8448, 8448, 128, 0), 0);
+    static std::vector<float> ws(want / 4 + 4);
+    n = g_launches;
+    expect("fwd_ws_tail", attn_fwd_ws(ATTN_BF16, p, wst, p, wst, p, wst, p, wst, lse, 1, 8, 8448, 8448, 128, sc, 0,
+                                      ws.data(), want, nullptr), ATTN_OK);
+    expect("fwd_ws_tail_plan", g_launches - n == 2 && g_fwd_mode == attn::kDenseWide && g_fwd.n_qblk == 33 &&
+                                   g_fwd.tail_start == 256 && g_fwd.n_split == 8 && g_fwd.split_tiles == 17 &&
+                                   g_fwd.part_o == ws.data() && g_fwd.part_lse == ws.data() + 8 * 8 * 256 * 128 &&
+                                   g_tail.n_tail == 8 && g_tail.tail_start == 256 && g_tail.n_split == 8 &&
+                                   g_tail.n_qblk == 33 && g_tail.o_ss == 8 * 128, 1);
+    n = g_launches;
+    expect("fwd_no_ws_tail", attn_fwd(ATTN_BF16, p, wst, p, wst, p, wst, p, wst, lse, 1, 8, 8448, 8448, 128, sc, 0,
+                                      nullptr), ATTN_OK);
+    expect("fwd_no_ws_tail_plan", g_launches - n == 1 && g_fwd_mode == attn::kDense, 1);
+    expect("fwd_ws_small", attn_fwd_ws(ATTN_BF16, p, wst, p, wst, p, wst, p, wst, lse, 1, 8, 8448, 8448, 128, sc, 0,
+                                       ws.data(), want - 4, nullptr), ATTN_ERR_INVALID);
+    expect("fwd_ws_misaligned", attn_fwd_ws(ATTN_BF16, p, wst, p, wst, p, wst, p, wst, lse, 1, 8, 8448, 8448, 128, sc,
+                                            0, ws.data() + 1, want, nullptr), ATTN_ERR_INVALID);
+    n = g_launches;
+    expect("fwd_whole_rounds", attn_fwd(ATTN_BF16, p, wst, p, wst, p, wst, p, wst, lse, 1, 8, 8192, 8192, 128, sc, 0,
+                                        nullptr), ATTN_OK);
+    expect("fwd_whole_rounds_plan", g_launches - n == 1 && g_fwd_mode == attn::kDenseWide && g_fwd_d == 128 &&
+                                        g_fwd.tail_start == 256 && g_fwd.n_split == 1 && g_fwd.n_qblk == 32, 1);
+    n = g_launches;
+    expect("fwd_d64", attn_fwd(ATTN_BF16, p, wst, p, wst, p, wst, p, wst, lse, 1, 8, 8192, 8192, 64, sc, 0, nullptr),
+           ATTN_OK);
+    expect("fwd_d64_plan", g_launches - n == 1 && g_fwd_mode == attn::kDense, 1);
+    expect("ws_bytes_short_keys", (int)attn_fwd_workspace_bytes(ATTN_BF16, 1, 8, 8448, 4095, 128, 0), 0);
+    expect("ws_bytes_4096_keys", attn_fwd_workspace_bytes(ATTN_BF16, 1, 8, 8448, 4096, 128, 0) ==
+                                     size_t(8) * 8 * 256 * 129 * 4, 1);
+    n = g_launches;
+    expect("fwd_short_keys", attn_fwd(ATTN_BF16, p, wst, p, wst, p, wst, p, wst, lse, 1, 8, 8192, 4095, 128, sc, 0,
+                                      nullptr), ATTN_OK);
+    expect("fwd_short_keys_plan", g_launches - n == 1 && g_fwd_mode == attn::kDense, 1);
+    n = g_launches;
+    expect("fwd_ws_causal", attn_fwd_ws(ATTN_FP16, p, wst, p, wst, p, wst, p, wst, lse, 1, 8, 8448, 8448, 128, sc, 1,
+                                        ws.data(), want, nullptr), ATTN_OK);
+    expect("fwd_ws_causal_plan", g_launches - n == 1 && g_fwd_mode == attn::kDense && g_fwd_causal == 1, 1);
+    n = g_launches;
+    expect("fwd_ws_sq_int_max", attn_fwd_ws(ATTN_BF16, p, st, p, st, p, st, p, st, lse, 1, 1, INT_MAX, 4096, 128, sc,
+                                            0, ws.data(), want, nullptr), ATTN_OK);
+    expect("fwd_ws_sq_int_max_plan", g_launches - n == 1 && g_fwd_mode == attn::kDenseWide &&
+                                         g_fwd.n_qblk == (INT_MAX / 256 + 1) && g_fwd.n_split == 1, 1);
+  }
 
   // dense forward with a score bias
   const int64_t bst[3] = {0, 0, 8};

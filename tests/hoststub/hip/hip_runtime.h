@@ -15,6 +15,10 @@ typedef enum hipMemcpyKind {
   hipMemcpyDefault = 4
 } hipMemcpyKind;
 
+typedef enum hipDeviceAttribute_t { hipDeviceAttributeMultiprocessorCount = 63 } hipDeviceAttribute_t;
+
+hipError_t hipGetDevice(int* device);
+hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t attr, int device);
 hipError_t hipMemcpyAsync(void* dst, const void* src, size_t bytes, hipMemcpyKind kind, hipStream_t stream);
 hipError_t hipStreamSynchronize(hipStream_t stream);
 const char* hipGetErrorString(hipError_t e);
