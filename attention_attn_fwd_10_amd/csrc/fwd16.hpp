@@ -384,19 +384,24 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   // 32 bits: 64 rows of at most 2^25 bytes; the copies never address past
   // row 63 of a tile, and rows past Lk read as zeros)
   const uint32_t k_rowb = 2u * (uint32_t)a.k_ss, v_rowb = 2u * (uint32_t)a.v_ss;
-  auto dma_k_c = [&](int key0, auto buf, int64_t row0) {
+  // (one copy round ii of this wave: one instruction)
+  auto dma_k_round = [&](int key0, auto buf, int64_t row0, int ii) {
     uint16_t* kb = kbuf(buf) + wave * C::KGRP;
     const i32x4 kr = make_rsrc(kg + row0 * a.k_ss, (uint32_t)min(Lk - key0, BC) * k_rowb);
-#pragma unroll
-    for (int ii = 0; ii < C::CI_W; ++ii)
-      dma16_buf(kr, k_boff + 2u * (uint32_t)k_key_shift(ii) * (uint32_t)a.k_ss, kb + NW * ii * C::KGRP);
+    dma16_buf(kr, k_boff + 2u * (uint32_t)k_key_shift(ii) * (uint32_t)a.k_ss, kb + NW * ii * C::KGRP);
   };
-  auto dma_v_c = [&](int key0, auto buf, int64_t row0) {
+  auto dma_v_round = [&](int key0, auto buf, int64_t row0, int ii) {
     uint16_t* vb = vbuf(buf) + wave * C::VGRP;
     const i32x4 vr = make_rsrc(vg + row0 * a.v_ss, (uint32_t)min(Lk - key0, BC) * v_rowb);
+    dma16_buf(vr, v_boff + 2u * (uint32_t)v_key_shift(ii) * (uint32_t)a.v_ss, vb + NW * ii * C::VGRP);
+  };
+  auto dma_k_c = [&](int key0, auto buf, int64_t row0) {
 #pragma unroll
-    for (int ii = 0; ii < C::CI_W; ++ii)
-      dma16_buf(vr, v_boff + 2u * (uint32_t)v_key_shift(ii) * (uint32_t)a.v_ss, vb + NW * ii * C::VGRP);
+    for (int ii = 0; ii < C::CI_W; ++ii) dma_k_round(key0, buf, row0, ii);
+  };
+  auto dma_v_c = [&](int key0, auto buf, int64_t row0) {
+#pragma unroll
+    for (int ii = 0; ii < C::CI_W; ++ii) dma_v_round(key0, buf, row0, ii);
   };
   // Copies for any layout: contiguous tiles as above; otherwise (pages of
   // fewer than 64 tokens) each row through the block table, rows past Lk
@@ -764,9 +769,11 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
       // table run for tile j acts on tile j + o.d, in stage (j + o.d - j0) %
       // 2; `par` is the stage of tile j, a compile-time constant in the
       // pipelined loop and an int in the one-at-a-time loop, and `math(kind,
-      // stage)` does the reads.  The tables are proven free of stage hazards
-      // at compile time (ring.hpp), so no copy, wait or barrier exists outside
-      // them.
+      // stage, copy)` does the reads.  Copies marked in_math are left to the
+      // math, which issues round r of the table's k-th such copy as
+      // copy(k * CI_W + r) (every round once).  The tables are proven free of
+      // stage hazards at compile time (ring.hpp), so no copy, wait or barrier
+      // exists outside them.
       int jm = j0;  // end of the pipelined tiles
       auto stage_of = [](auto par, auto dd) {
         constexpr int DD = decltype(dd)::value;
@@ -776,8 +783,25 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
       // (contig: the pipelined tiles, whose copies are single buffer loads)
       auto run = [&](auto table, int j, auto par, auto contig, auto&& math) {
         using T = decltype(table);
+        // round `part % CI_W` of the table's (part / CI_W)-th in_math copy
+        auto copy = [&](int part) {
+          static_for<T::size>([&](auto I) {
+            constexpr ring::Op o = T::at(decltype(I)::value);
+            if constexpr (o.in_math) {
+              static_assert(decltype(contig)::value && (o.kind == ring::kCopyK || o.kind == ring::kCopyV),
+                            "copies left to the math are the pipelined single-buffer K or V copies");
+              constexpr int k = T::in_math_index(decltype(I)::value);
+              const int t = j + o.d;
+              if (part / C::CI_W != k || !ring::guard_ok(o.guard, t - j0, jm - j0, j1 - j0)) return;
+              const auto st = stage_of(par, std::integral_constant<int, o.d>{});
+              if constexpr (o.kind == ring::kCopyK) dma_k_round(t * BC, st, tile_row0(t * BC), part % C::CI_W);
+              else dma_v_round(t * BC, st, tile_row0(t * BC), part % C::CI_W);
+            }
+          });
+        };
         static_for<T::size>([&](auto I) {
           constexpr ring::Op o = T::at(decltype(I)::value);
+          if constexpr (o.in_math) return;  // issued by the math through `copy`
           const int t = j + o.d;
           if (!ring::guard_ok(o.guard, t - j0, jm - j0, j1 - j0)) return;
           const auto st = stage_of(par, std::integral_constant<int, o.d>{});
@@ -795,7 +819,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
           } else if constexpr (o.kind == ring::kSync) {
             __syncthreads();
           } else {
-            math(std::integral_constant<int, o.kind>{}, st);
+            math(std::integral_constant<int, o.kind>{}, st, copy);
           }
         });
       };
@@ -824,7 +848,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
           // separates the scores from it: every wave must have read K(j0)
           // first (waves with no rows skip the read and would otherwise
           // overwrite the stage while it is still being read).
-          run(ring::Table<ring::kPrologue>{}, j0, S0, std::true_type{}, [&](auto, auto st) {
+          run(ring::Table<ring::kPrologue>{}, j0, S0, std::true_type{}, [&](auto, auto st, auto&&) {
             if (wave_active) qk_tile(st, sa);
           });
           // One step with the next tile's scores overlapped (needs j + 1 < jm).
@@ -834,7 +858,18 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
           // 24 of the 32 exponentials per lane); region B issues the NB P V
           // MFMAs of tile j, in 16-key chunks, and the last 8 exponentials
           // after its first MFMAs (they feed the last chunk).
-          auto step_math = [&](auto cur, auto nxt, f32x16 (&sc)[BC / 32], f32x16 (&sn)[BC / 32]) {
+          // In the wide layout the step's copies (K(j+2), V(j+1): 2 rounds
+          // each per wave) are spread over region A, one after each of the
+          // score MFMAs 4, 6, 8 and 10 (measured 1 % faster than issuing them
+          // first; in region B they land too late for the step's closing
+          // wait, and the step ran 6 % slower).  Elsewhere they precede the
+          // step: the causal 8-wave kernel spills about 190 registers with
+          // them spread, and the 4-wave kernels issue twice the rounds.
+          constexpr bool kSpread = WIDE;
+          using StepTable = std::conditional_t<kSpread, ring::Table<ring::kStepSpread>, ring::Table<ring::kStep>>;
+          constexpr int kParts = StepTable::in_math_count * C::CI_W;  // copy rounds the math issues
+          static_assert(kParts == 0 || 4 + 2 * (kParts - 1) < (D / 16) * (BC / 32), "the spread copies fit region A");
+          auto step_math = [&](auto cur, auto nxt, f32x16 (&sc)[BC / 32], f32x16 (&sn)[BC / 32], auto&& copy) {
             constexpr int NA = (D / 16) * (BC / 32), NB = (D / 32) * (BC / 16);
             constexpr int KPRE = 3, VPRE = 2;
             const uint16_t* ks = kbuf(nxt) + C::krow(l32) + 8 * hh;
@@ -887,6 +922,9 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
               } else {
                 exps((i - 3) * 24 / (NA - 3), (i - 2) * 24 / (NA - 3));
               }
+              if constexpr (kParts > 0) {
+                if (i >= 4 && (i & 1) == 0 && (i - 4) / 2 < kParts) copy((i - 4) / 2);
+              }
               __builtin_amdgcn_sched_barrier(0);
             }
             // keep P here: otherwise it is sunk past the rescale branch below
@@ -916,13 +954,18 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
             }
           };
           auto step = [&](int j, auto cur, auto nxt, f32x16 (&sc)[BC / 32], f32x16 (&sn)[BC / 32]) {
-            run(ring::Table<ring::kStep>{}, j, cur, std::true_type{}, [&](auto, auto) {
-              if (wave_active) step_math(cur, nxt, sc, sn);
+            run(StepTable{}, j, cur, std::true_type{}, [&](auto, auto, auto&& copy) {
+              if (wave_active) {
+                step_math(cur, nxt, sc, sn, copy);
+              } else {
+#pragma unroll
+                for (int part = 0; part < kParts; ++part) copy(part);  // a wave with no rows still copies its share
+              }
             });
           };
           // the last pipelined tile: softmax and P V only
           auto last = [&](int j, auto cur, f32x16 (&sc)[BC / 32]) {
-            run(ring::Table<ring::kLast>{}, j, cur, std::true_type{}, [&](auto, auto) {
+            run(ring::Table<ring::kLast>{}, j, cur, std::true_type{}, [&](auto, auto, auto&&) {
               if (wave_active) {
                 u32x4 pk[BC / 16];
                 float alpha;
@@ -946,12 +989,12 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
         }
       }
       // tiles one at a time (tile j + 1 lands while tile j is computed)
-      if (jg == j0) run(ring::Table<ring::kTileStart>{}, j0, 0, std::false_type{}, [](auto, auto) {});
+      if (jg == j0) run(ring::Table<ring::kTileStart>{}, j0, 0, std::false_type{}, [](auto, auto, auto&&) {});
       for (int j = jg; j < j1; ++j) {
         const int buf = (j - j0) & 1;
         BiasRaw br{};
         if constexpr (BIAS) br = bias_fetch(j * BC);
-        run(ring::Table<ring::kTile>{}, j, buf, std::false_type{}, [&](auto, auto st) { compute(j * BC, st, br); });
+        run(ring::Table<ring::kTile>{}, j, buf, std::false_type{}, [&](auto, auto st, auto&&) { compute(j * BC, st, br); });
       }
     } else {
       dma_tile(j0 * BC, 0);

@@ -20,7 +20,9 @@
 //   step j:        copy K(j+2) (if j + 2 <= n_pipe and j + 2 < n_total) and
 //                  V(j+1), then the scores of tile j+1 (K(j+1)) with the
 //                  softmax and P V of tile j (V(j)), wait, barrier
-//                  (j + 1 < n_pipe);
+//                  (j + 1 < n_pipe); in the spread form the two copies are
+//                  issued by the step's math, between its first score
+//                  products, in the same barrier interval;
 //   last:          copy V(j+1) (if j + 1 < n_total), softmax and P V of tile
 //                  j = n_pipe - 1, wait, barrier;
 //   one at a time: (tile n_pipe = 0: copy K0 and V0, wait, barrier) then per
@@ -47,14 +49,20 @@ enum Guard : int {
   kLtTotal,      // tile j + d < n_total
   kLePipeLtTotal  // tile j + d <= n_pipe and < n_total
 };
+// in_math: a copy that the math op of the same table issues itself (spread
+// between its instructions) instead of one issued before it.  It lies in the
+// same barrier interval either way, so the hazard rules below treat it alike.
 struct Op {
   int kind, d, guard;
+  int in_math = 0;
 };
 
 constexpr Op kPrologue[] = {{kCopyK, 0, kAlways}, {kCopyV, 0, kAlways}, {kCopyK, 1, kLtTotal}, {kWait, 0, kAlways},
                             {kSync, 0, kAlways},  {kScores, 0, kAlways}, {kSync, 0, kAlways}};
 constexpr Op kStep[] = {{kCopyK, 2, kLePipeLtTotal}, {kCopyV, 1, kAlways}, {kStepMath, 0, kAlways},
                         {kWait, 0, kAlways},        {kSync, 0, kAlways}};
+constexpr Op kStepSpread[] = {{kCopyK, 2, kLePipeLtTotal, 1}, {kCopyV, 1, kAlways, 1}, {kStepMath, 0, kAlways},
+                              {kWait, 0, kAlways},           {kSync, 0, kAlways}};
 constexpr Op kLast[] = {{kCopyV, 1, kLtTotal}, {kLastMath, 0, kAlways}, {kWait, 0, kAlways}, {kSync, 0, kAlways}};
 constexpr Op kTileStart[] = {{kCopyKV, 0, kAlways}, {kWait, 0, kAlways}, {kSync, 0, kAlways}};
 constexpr Op kTile[] = {{kCopyKV, 1, kLtTotal}, {kTileMath, 0, kAlways}, {kWait, 0, kAlways}, {kSync, 0, kAlways}};
@@ -64,6 +72,13 @@ template <const auto& T>
 struct Table {
   static constexpr int size = sizeof(T) / sizeof(T[0]);
   static constexpr Op at(int i) { return T[i]; }
+  // position of op i among the table's in_math copies, and their number
+  static constexpr int in_math_index(int i) {
+    int n = 0;
+    for (int k = 0; k < i; ++k) n += T[k].in_math;
+    return n;
+  }
+  static constexpr int in_math_count = in_math_index(size);
 };
 
 constexpr bool guard_ok(int guard, int tile, int n_pipe, int n_total) {
@@ -159,6 +174,8 @@ constexpr bool schedule_ok_all(const Op (&pro)[A], const Op (&step)[B], const Op
 
 static_assert(schedule_ok_all(kPrologue, kStep, kLast, kTileStart, kTile),
               "the K/V ring schedule reads a stage beside a write to it, or before its copy is complete");
+static_assert(schedule_ok_all(kPrologue, kStepSpread, kLast, kTileStart, kTile),
+              "the spread K/V ring schedule reads a stage beside a write to it, or before its copy is complete");
 
 }  // namespace ring
 }  // namespace attn

@@ -14,6 +14,7 @@ int main() {
     if (ok != expect) ++bad;
   };
   report("tables", schedule_ok_all(kPrologue, kStep, kLast, kTileStart, kTile), true);
+  report("tables_spread", schedule_ok_all(kPrologue, kStepSpread, kLast, kTileStart, kTile), true);
 
   // the prologue without the barrier between the scores of tile 0 and the
   // first step's copy of K2 into the same stage
@@ -44,6 +45,16 @@ int main() {
   constexpr Op step_v_late[] = {{kCopyK, 2, kLePipeLtTotal}, {kStepMath, 0, kAlways}, {kCopyV, 1, kAlways},
                                 {kWait, 0, kAlways},        {kSync, 0, kAlways}};
   report("step_copies_v_after_math", schedule_ok_all(kPrologue, step_v_late, kLast, kTileStart, kTile), true);
+  // the spread step (copies issued by its math) copying K one tile ahead, or
+  // without its wait: the copies share the interval of the math's reads
+  constexpr Op spread_k_one_ahead[] = {{kCopyK, 1, kLePipeLtTotal, 1}, {kCopyV, 1, kAlways, 1},
+                                       {kStepMath, 0, kAlways},        {kWait, 0, kAlways},
+                                       {kSync, 0, kAlways}};
+  report("spread_step_copies_k_one_ahead", schedule_ok_all(kPrologue, spread_k_one_ahead, kLast, kTileStart, kTile),
+         false);
+  constexpr Op spread_no_wait[] = {{kCopyK, 2, kLePipeLtTotal, 1}, {kCopyV, 1, kAlways, 1}, {kStepMath, 0, kAlways},
+                                   {kSync, 0, kAlways}};
+  report("spread_step_without_wait", schedule_ok_all(kPrologue, spread_no_wait, kLast, kTileStart, kTile), false);
   // the last pipelined tile without its barrier (the one-at-a-time loop then
   // refills the stage the last tile reads)
   constexpr Op last_no_sync[] = {{kCopyV, 1, kLtTotal}, {kLastMath, 0, kAlways}, {kWait, 0, kAlways}};

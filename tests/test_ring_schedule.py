@@ -20,6 +20,7 @@ def test_ring_schedule_mutations(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     got = dict(line.split() for line in r.stdout.strip().splitlines())
     assert got.pop("tables") == "1"
+    assert got.pop("tables_spread") == "1"
     assert got.pop("step_copies_v_after_math") == "1"
     assert got, "no mutation cases ran"
     assert all(v == "0" for v in got.values()), got
