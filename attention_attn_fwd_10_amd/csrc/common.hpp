@@ -69,20 +69,18 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// max of three (two) floats as one v_max3_f32 (v_max_f32).  Scores are never
-// signalling NaNs, so the quieting that fmaxf wraps around its operands
-// (a v_max x, x each) is not needed; the result is exact, so any order of
-// the operands gives the same bits.
+// max of three (two) floats as one v_maximum3_f32 (v_maximum_f32): the IEEE
+// maximum, which needs none of the quieting that fmaxf wraps around its
+// operands (a v_max x, x each).  The result is exact, so any order of the
+// operands gives the same bits.  Written with the compiler's builtin, not as
+// inline assembly: the compiler's hazard checks do not look into inline
+// assembly, and a read of a matrix-core result needs wait states after the
+// MFMA that writes it (with inline assembly reading score registers right
+// after the score MFMAs, stale registers were read).
 __device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
-__device__ __forceinline__ float max2f(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
+__device__ __forceinline__ float max2f(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 // max of the 32 scores of two 16-value score tiles (16 v_max3)
 __device__ __forceinline__ float tile_max32(const f32x16& a, const f32x16& b) {

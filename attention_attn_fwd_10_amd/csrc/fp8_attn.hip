@@ -147,13 +147,9 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// max of three floats as one v_max3_f32 (the scores are never signalling NaNs,
-// so the quieting that fmaxf adds around its operands is not needed)
-__device__ __forceinline__ float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
+// max of three floats: max3f (v_maximum3_f32, written so that the compiler
+// sees the reads of the score MFMAs' results and waits for them)
+__device__ __forceinline__ float max3(float a, float b, float c) { return max3f(a, b, c); }
 
 template <int N>
 using C = std::integral_constant<int, N>;
