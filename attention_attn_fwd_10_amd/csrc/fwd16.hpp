@@ -892,12 +892,12 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
                                 pack2<DT>(p[x - 3], p[x - 2]), pack2<DT>(p[x - 1], p[x])};
               }
             };
-            // (wide layout: the second wave of each SIMD, waves 4-7, is raised
+            // (8 waves: the second wave of each SIMD, waves 4-7, is raised
             // over region A; the hardware otherwise favours the older wave,
             // which then idles at the barrier while the younger one finishes,
-            // measured 0.7 % slower)
+            // measured 0.7 % slower in the wide layout and 3 % slower causal)
             __builtin_amdgcn_sched_barrier(0);
-            if (WIDE && wave >= 4) __builtin_amdgcn_s_setprio(1);
+            if (NW == 8 && wave >= 4) __builtin_amdgcn_s_setprio(1);
             __builtin_amdgcn_sched_barrier(0);
             u32x4 kop[NA];
 #pragma unroll
@@ -934,7 +934,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
               __builtin_amdgcn_sched_barrier(0);
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (WIDE) __builtin_amdgcn_s_setprio(0);
+            if (NW == 8) __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_sched_barrier(0);
             // keep P here: otherwise it is sunk past the rescale branch below
 #pragma unroll
