@@ -157,7 +157,7 @@ constexpr bool fwd16_layout_ok() {
 static_assert(fwd16_layout_ok<Fwd16Cfg<64, 4>>() && fwd16_layout_ok<Fwd16Cfg<64, 8>>(), "fwd16 tile layout, head dim 64");
 static_assert(fwd16_layout_ok<Fwd16Cfg<128, 4>>() && fwd16_layout_ok<Fwd16Cfg<128, 8>>(), "fwd16 tile layout, head dim 128");
 static_assert(fwd16_layout_ok<Fwd16Cfg<256, 4>>(), "fwd16 tile layout, head dim 256");
-static_assert(Fwd16Cfg<128, 8>::BR == kWideRows, "rows of a wide workgroup");
+static_assert(Fwd16Cfg<64, 8>::BR == kWideRows && Fwd16Cfg<128, 8>::BR == kWideRows, "rows of a wide workgroup");
 
 // f(integral_constant<int, I>) for I = 0 .. N-1, unrolled
 template <class F, int... I>
@@ -181,7 +181,7 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
   constexpr bool DENSE = MODE == kDense || MODE == kDenseBias || MODE == kDenseWide;
   constexpr bool BIAS = MODE == kDenseBias;
   constexpr bool WIDE = MODE == kDenseWide;
-  static_assert(!WIDE || (D == 128 && !CAUSAL), "the wide dense layout is the non-causal forward at head dim 128");
+  static_assert(!WIDE || (D <= 128 && !CAUSAL), "the wide dense layout is the non-causal forward at head dims 64 and 128");
   static_assert(!BIAS || D <= 128, "the score bias is supported up to head dim 128");
   // The two stages of the K and V rings are separate arrays: when a stage is
   // named by a compile-time constant, the compiler can tell the copies into
@@ -858,9 +858,9 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
           // 24 of the 32 exponentials per lane); region B issues the NB P V
           // MFMAs of tile j, in 16-key chunks, and the last 8 exponentials
           // after its first MFMAs (they feed the last chunk).
-          // In the wide layout the step's copies (K(j+2), V(j+1): 2 rounds
+          // In the wide layout the step's copies (K(j+2), V(j+1): D/64 rounds
           // each per wave) are spread over region A, one after each of the
-          // score MFMAs 4, 6, 8 and 10 (measured 1 % faster than issuing them
+          // score MFMAs 4, 6, 8 and 10 (at d128, measured 1 % faster than issuing them
           // first; in region B they land too late for the step's closing
           // wait, and the step ran 6 % slower).  Elsewhere they precede the
           // step: the causal 8-wave kernel spills about 190 registers with

@@ -80,8 +80,8 @@ attn_status_t attn_fwd(int dtype,
 
 /*
  * attn_fwd_ws — attn_fwd with a workspace, which lets the non-causal forward
- * at head dim 128 (4096 keys or more) split the last, partial round of its
- * grid by keys.
+ * at head dims 64 and 128 (4096 keys or more) split the last, partial round
+ * of its grid by keys.
  * (The "Fused attention kernel" page's implementation sketch keeps a running
  * row max and row sum per query, so the partial results of key ranges merge
  * exactly through their logsumexps, as for attn_fwd_splitkv.)
@@ -111,7 +111,7 @@ attn_status_t attn_fwd_ws(int dtype,
 
 /* Workspace attn_fwd_ws uses for these sizes on the current device (it
  * depends on the device's compute-unit count): 0 when the problem has no
- * split tail (causal, head dim other than 128, fewer than 4096 keys, a grid
+ * split tail (causal, head dim 256, fewer than 4096 keys, a grid
  * of whole rounds, a last round more than half full, or invalid sizes), else
  * splits * tail_items * 256 * (D + 1) * 4 bytes. */
 size_t attn_fwd_workspace_bytes(int dtype, int B, int H, int Sq, int Sk, int D, int causal);

@@ -1,7 +1,7 @@
 """GPU parity of the wide dense forward (256-row workgroups) and of its split
 tail: when the grid's last round is partial, attn_fwd_ws runs that round's
-work items as key ranges and merges them through their logsumexps (head dim
-128, 4096 keys or more).
+work items as key ranges and merges them through their logsumexps (head dims
+64 and 128, 4096 keys or more).
 
 Shapes are derived from the device's compute-unit count so that the grid has
 the intended tail: one (batch, head) plane more than whole rounds, with a
@@ -47,14 +47,15 @@ def _check_rows(o, lse, q, k, v, scale, b, h, rows, what, dtype="bf16"):
     return assert_close16(oo, o_ref[None, :, None], ll, l_ref[None, None], what, dtype=dtype)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("sk", [None, 4100])
-def test_split_tail(lib, dtype, sk):
+def test_split_tail(lib, d, dtype, sk):
     import torch
     cus = _cus()
     if cus % 8:
         pytest.skip(f"{cus} compute units: the shape below assumes a multiple of 8")
-    H, rows_per, d = 8, 256, 128
+    H, rows_per = 8, 256
     nq = cus // H + 1                # H * nq = cus + 8 work items: a tail of 8
     sq = rows_per * nq - 100         # ragged last query block
     sk = sq if sk is None else sk    # 4100 keys: 65 tiles, the last one of 4 keys
@@ -106,7 +107,7 @@ def test_split_tail_workspace_checks(lib):
 @pytest.mark.parametrize("d", [64, 128])
 def test_whole_rounds(lib, d):
     """A grid of exactly one round of 256-row work items: the wide layout
-    without a split (no workspace) at head dim 128, the 128-row layout at 64."""
+    without a split (no workspace)."""
     import torch
     cus = _cus()
     H = 8
