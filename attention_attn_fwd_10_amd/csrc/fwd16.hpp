@@ -783,6 +783,23 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
       // (contig: the pipelined tiles, whose copies are single buffer loads)
       auto run = [&](auto table, int j, auto par, auto contig, auto&& math) {
         using T = decltype(table);
+        // the in_math copies' buffer resources and guards, formed once
+        constexpr int NIM = T::in_math_count > 0 ? T::in_math_count : 1;
+        i32x4 im_rsrc[NIM];
+        bool im_ok[NIM];
+        static_for<T::size>([&](auto I) {
+          constexpr ring::Op o = T::at(decltype(I)::value);
+          if constexpr (o.in_math) {
+            constexpr int k = T::in_math_index(decltype(I)::value);
+            const int t = j + o.d;
+            im_ok[k] = ring::guard_ok(o.guard, t - j0, jm - j0, j1 - j0);
+            const int64_t row0 = tile_row0(t * BC);
+            if constexpr (o.kind == ring::kCopyK)
+              im_rsrc[k] = make_rsrc(kg + row0 * a.k_ss, (uint32_t)min(Lk - t * BC, BC) * k_rowb);
+            else
+              im_rsrc[k] = make_rsrc(vg + row0 * a.v_ss, (uint32_t)min(Lk - t * BC, BC) * v_rowb);
+          }
+        });
         // round `part % CI_W` of the table's (part / CI_W)-th in_math copy
         auto copy = [&](int part) {
           static_for<T::size>([&](auto I) {
@@ -791,11 +808,15 @@ __global__ void __launch_bounds__((64 * fwd16_waves(D, MODE, CAUSAL)), (Fwd16Cfg
               static_assert(decltype(contig)::value && (o.kind == ring::kCopyK || o.kind == ring::kCopyV),
                             "copies left to the math are the pipelined single-buffer K or V copies");
               constexpr int k = T::in_math_index(decltype(I)::value);
-              const int t = j + o.d;
-              if (part / C::CI_W != k || !ring::guard_ok(o.guard, t - j0, jm - j0, j1 - j0)) return;
+              if (part / C::CI_W != k || !im_ok[k]) return;
               const auto st = stage_of(par, std::integral_constant<int, o.d>{});
-              if constexpr (o.kind == ring::kCopyK) dma_k_round(t * BC, st, tile_row0(t * BC), part % C::CI_W);
-              else dma_v_round(t * BC, st, tile_row0(t * BC), part % C::CI_W);
+              const int ii = part % C::CI_W;
+              if constexpr (o.kind == ring::kCopyK)
+                dma16_buf(im_rsrc[k], k_boff + 2u * (uint32_t)k_key_shift(ii) * (uint32_t)a.k_ss,
+                          kbuf(st) + wave * C::KGRP + NW * ii * C::KGRP);
+              else
+                dma16_buf(im_rsrc[k], v_boff + 2u * (uint32_t)v_key_shift(ii) * (uint32_t)a.v_ss,
+                          vbuf(st) + wave * C::VGRP + NW * ii * C::VGRP);
             }
           });
         };
