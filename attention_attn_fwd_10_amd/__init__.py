@@ -8,6 +8,9 @@ The entry points mirror the C ABI in ``include/attn.h``:
   workspace for a split tail of the grid, sized by ``attn_fwd_workspace_bytes``)
 * ``fp8_quantize``   -> ``attn_fp8_quantize``   (rotation + e4m3 block quantisation)
 * ``fwd_fp8``        -> ``attn_fwd_fp8``        (e4m3 forward with per-block scales)
+* ``fp8_quantize_pow2`` / ``fwd_fp8_pow2`` -> ``attn_fp8_quantize_pow2`` / ``attn_fwd_fp8_pow2``
+  (the same with power-of-two block scales, applied inside the matrix-core
+  products; ``fp8_quantize_pow2_q`` codes Q with the softmax scale)
 * ``int8_quantize``  -> ``attn_int8_quantize``  (rotation + int8 block quantisation)
 * ``fwd_int8``       -> ``attn_fwd_int8``       (int8 scores, e4m3 V and probabilities)
 * ``fwd_varlen``     -> ``attn_fwd_varlen``     (packed sequences, optional paged KV)
@@ -25,8 +28,9 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "fwd_bias", "fp8_quantize", "fwd_fp8", "int8_quantize", "fwd_int8", "fwd_varlen", "fwd_splitkv",
-           "fwd_splitkv_noalloc", "bwd", "set_index_checks", "lib_path", "AttnError", "ATTN_BF16", "ATTN_FP16"]
+__all__ = ["fwd", "fwd_bias", "fp8_quantize", "fwd_fp8", "fp8_quantize_pow2", "fp8_quantize_pow2_q", "fwd_fp8_pow2",
+           "int8_quantize", "fwd_int8", "fwd_varlen", "fwd_splitkv", "fwd_splitkv_noalloc", "bwd",
+           "set_index_checks", "lib_path", "AttnError", "ATTN_BF16", "ATTN_FP16", "LOG2E"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libattn_fwd.so")
@@ -61,6 +65,10 @@ def _load():
     lib.attn_fp8_quantize.restype = I
     lib.attn_fwd_fp8.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, I, F, I, P]
     lib.attn_fwd_fp8.restype = I
+    lib.attn_fp8_quantize_pow2.argtypes = [P, I64P, P, P, I, I, I, I, I, P, F, P]
+    lib.attn_fp8_quantize_pow2.restype = I
+    lib.attn_fwd_fp8_pow2.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, P]
+    lib.attn_fwd_fp8_pow2.restype = I
     lib.attn_bwd.argtypes = [I, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, P]
     lib.attn_bwd.restype = I
     lib.attn_int8_quantize.argtypes = [P, I64P, P, P, I, I, I, I, I, P, P]
@@ -248,7 +256,7 @@ def fwd_bias(q, k, v, bias, softmax_scale=None, causal=False, out=None, lse=None
     return out, lse
 
 
-def _quantize(fn, code_dtype, x, block_rows, signs, out, scales, stream):
+def _quantize(fn, code_dtype, x, block_rows, signs, out, scales, stream, premul=None):
     import torch
     _require_cuda(x, signs, out, scales)
     if x.dtype != torch.bfloat16:
@@ -264,7 +272,8 @@ def _quantize(fn, code_dtype, x, block_rows, signs, out, scales, stream):
         _require(scales, "scales", _scale_shape(B, H, S, block_rows), torch.float32)
     if signs is not None and (signs.dtype != torch.int8 or signs.numel() != D):
         raise ValueError("signs must be int8 [D]")
-    _check(fn(_ptr(x), _strides(x), _ptr(out), _ptr(scales), B, H, S, D, int(block_rows), _ptr(signs),
+    extra = () if premul is None else (float(premul),)
+    _check(fn(_ptr(x), _strides(x), _ptr(out), _ptr(scales), B, H, S, D, int(block_rows), _ptr(signs), *extra,
               _stream(stream)))
     return out, scales
 
@@ -275,6 +284,24 @@ def fp8_quantize(x, block_rows=128, signs=None, out=None, scales=None, stream=No
     random-sign Hadamard rotation given by ``signs`` (int8 [D] of +-1)."""
     import torch
     return _quantize(_lib.attn_fp8_quantize, torch.uint8, x, block_rows, signs, out, scales, stream)
+
+
+LOG2E = 1.4426950408889634
+
+
+def fp8_quantize_pow2(x, block_rows=128, signs=None, premul=1.0, out=None, scales=None, stream=None):
+    """``fp8_quantize`` with power-of-two scales (the smallest power of two at
+    or above amax / 448), every value multiplied by ``premul`` first: the input
+    form of ``fwd_fp8_pow2`` (premul 1 for K and V; Q: ``fp8_quantize_pow2_q``)."""
+    import torch
+    return _quantize(_lib.attn_fp8_quantize_pow2, torch.uint8, x, block_rows, signs, out, scales, stream, premul)
+
+
+def fp8_quantize_pow2_q(q, softmax_scale=None, block_rows=128, signs=None, out=None, scales=None, stream=None):
+    """``fp8_quantize_pow2`` of a query tensor: premul = softmax_scale * log2(e)
+    (softmax_scale defaults to 1/sqrt(head_dim))."""
+    scale = 1.0 / math.sqrt(q.shape[-1]) if softmax_scale is None else float(softmax_scale)
+    return fp8_quantize_pow2(q, block_rows, signs, scale * LOG2E, out, scales, stream)
 
 
 def int8_quantize(x, block_rows=128, signs=None, out=None, scales=None, stream=None):
@@ -323,6 +350,26 @@ def fwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, block_rows=128, softmax_scale
     _check(_lib.attn_fwd_fp8(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v8), _ptr(v_scale),
                              int(block_rows), _ptr(out), _ptr(lse), B, H, Sq, Sk, D, scale, int(bool(causal)),
                              _stream(stream)))
+    return out, lse
+
+
+def fwd_fp8_pow2(q8, q_scale, k8, k_scale, v8, v_scale, block_rows=128, causal=False, out=None, lse=None,
+                 stream=None):
+    """``fwd_fp8`` on the power-of-two form (``fp8_quantize_pow2``; the Q codes
+    carry the softmax scale, so there is no softmax_scale argument).  Returns
+    (o bf16 [B, Sq, H, D], lse fp32 [B, H, Sq])."""
+    import torch
+    _require_cuda(q8, q_scale, k8, k_scale, v8, v_scale, out, lse)
+    B, Sq, H, D = q8.shape
+    Sk = k8.shape[1]
+    _check_8bit(q8, q_scale, k8, k_scale, v8, v_scale, block_rows, out, lse, torch.uint8)
+    if out is None:
+        out = torch.empty((B, Sq, H, D), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q8.device)
+    _check(_lib.attn_fwd_fp8_pow2(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v8), _ptr(v_scale),
+                                  int(block_rows), _ptr(out), _ptr(lse), B, H, Sq, Sk, D, int(bool(causal)),
+                                  _stream(stream)))
     return out, lse
 
 

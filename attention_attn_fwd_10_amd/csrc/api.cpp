@@ -23,9 +23,11 @@ namespace attn {
 template <int D, int DT, bool CAUSAL, int MODE>
 hipError_t launch_fwd16(FwdArgs a, hipStream_t s);
 hipError_t launch_fp8_quantize(const QuantArgs& a, int D, hipStream_t s);
+hipError_t launch_fp8_quantize_pow2(const QuantArgs& a, int D, hipStream_t s);
 hipError_t launch_splitkv_merge(const MergeArgs& a, int D, int dtype, hipStream_t s);
 hipError_t launch_tail_merge(const TailMergeArgs& a, int D, int dtype, hipStream_t s);
 hipError_t launch_fwd_fp8(const Fp8Args& a, int D, bool causal, hipStream_t s);
+hipError_t launch_fwd_fp8_pow2(const Fp8Args& a, int D, bool causal, hipStream_t s);
 hipError_t launch_int8_quantize(const QuantArgs& a, int D, hipStream_t s);
 hipError_t launch_fwd_int8(const Fp8Args& a, int D, bool causal, hipStream_t s);
 size_t noalloc_scratch_bytes();
@@ -583,10 +585,12 @@ typedef hipError_t (*quant_launcher_t)(const attn::QuantArgs&, int, hipStream_t)
 
 static attn_status_t quantize_8bit(const char* name, quant_launcher_t launch, const void* x,
                                    const int64_t x_strides[3], uint8_t* x8, float* scales, int B, int H, int S,
-                                   int D, int block_rows, const int8_t* signs, void* stream) {
+                                   int D, int block_rows, const int8_t* signs, float premul, void* stream) {
   attn_status_t st;
   if (B < 0 || H < 0 || S < 0) return fail(ATTN_ERR_INVALID, "negative size");
   if ((st = check_head_dim(D)) != ATTN_OK) return st;
+  if (!std::isfinite(premul) || !(premul > 0.f))
+    return fail(ATTN_ERR_INVALID, "premul must be finite and > 0 (got %g)", (double)premul);
   if (block_rows != 0 && block_rows != 128) return fail(ATTN_ERR_INVALID, "block_rows must be 128 or 0 (got %d)", block_rows);
   if ((st = check_strides("x", x_strides)) != ATTN_OK) return st;
   if (B == 0 || H == 0 || S == 0) return ok();
@@ -598,19 +602,27 @@ static attn_status_t quantize_8bit(const char* name, quant_launcher_t launch, co
   a.x_sb = x_strides[0]; a.x_ss = x_strides[1]; a.x_sh = x_strides[2];
   a.x8 = x8; a.scales = scales; a.signs = signs;
   a.B = B; a.H = H; a.S = S; a.block_rows = block_rows;
+  a.premul = premul;
   return hip_status(launch(a, D, (hipStream_t)stream), name);
 }
 
 attn_status_t attn_fp8_quantize(const void* x, const int64_t x_strides[3], uint8_t* x8, float* scales, int B, int H,
                                 int S, int D, int block_rows, const int8_t* signs, void* stream) {
   return quantize_8bit("attn_fp8_quantize launch", attn::launch_fp8_quantize, x, x_strides, x8, scales, B, H, S, D,
-                       block_rows, signs, stream);
+                       block_rows, signs, 1.f, stream);
+}
+
+attn_status_t attn_fp8_quantize_pow2(const void* x, const int64_t x_strides[3], uint8_t* x8, float* scales, int B,
+                                     int H, int S, int D, int block_rows, const int8_t* signs, float premul,
+                                     void* stream) {
+  return quantize_8bit("attn_fp8_quantize_pow2 launch", attn::launch_fp8_quantize_pow2, x, x_strides, x8, scales, B,
+                       H, S, D, block_rows, signs, premul, stream);
 }
 
 attn_status_t attn_int8_quantize(const void* x, const int64_t x_strides[3], int8_t* x8, float* scales, int B, int H,
                                  int S, int D, int block_rows, const int8_t* signs, void* stream) {
   return quantize_8bit("attn_int8_quantize launch", attn::launch_int8_quantize, x, x_strides, (uint8_t*)x8, scales,
-                       B, H, S, D, block_rows, signs, stream);
+                       B, H, S, D, block_rows, signs, 1.f, stream);
 }
 
 typedef hipError_t (*fwd8_launcher_t)(const attn::Fp8Args&, int, bool, hipStream_t);
@@ -649,6 +661,14 @@ attn_status_t attn_fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_
                            int H, int Sq, int Sk, int D, float softmax_scale, int causal, void* stream) {
   return fwd_8bit("attn_fwd_fp8 launch", attn::launch_fwd_fp8, q8, q_scale, k8, k_scale, v8, v_scale, block_rows, o,
                   lse, B, H, Sq, Sk, D, softmax_scale, causal, stream);
+}
+
+attn_status_t attn_fwd_fp8_pow2(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
+                                const uint8_t* v8, const float* v_scale, int block_rows, void* o, float* lse, int B,
+                                int H, int Sq, int Sk, int D, int causal, void* stream) {
+  // (the Q codes carry the softmax scale: 1 passes the shared checks)
+  return fwd_8bit("attn_fwd_fp8_pow2 launch", attn::launch_fwd_fp8_pow2, q8, q_scale, k8, k_scale, v8, v_scale,
+                  block_rows, o, lse, B, H, Sq, Sk, D, 1.f, causal, stream);
 }
 
 attn_status_t attn_fwd_int8(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,

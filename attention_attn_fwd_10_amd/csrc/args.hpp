@@ -104,6 +104,7 @@ struct QuantArgs {
   const int8_t* signs;
   int B, H, S;
   int block_rows;
+  float premul;              // power-of-two e4m3 form: factor applied to every value before the amax
 };
 
 }  // namespace attn

@@ -17,6 +17,14 @@
 //    V block scale is smaller gets the ratio folded into the exp2 bias of its
 //    probabilities, so block scales cost no per-element work, and the
 //    accumulator is rescaled only when a larger block scale appears;
+//  * power-of-two scales (POW2, inputs of the quantiser's power-of-two form):
+//    the Q codes carry the softmax scale times log2(e), so a tile's score
+//    scale sq * sk is a power of two that the MFMAs apply themselves through
+//    their block-scale exponent operands, and the score MFMAs start from
+//    kMu - m (every register of a lane holds its row's value): they return the
+//    exp2 argument itself, and the softmax needs no multiply-add per score.
+//    The P V MFMAs take each tile's V block scale the same way, so the
+//    accumulator holds O times the row sum in absolute units;
 //  * probabilities are quantised as p * 2^6 with the running max allowed to
 //    lag the true max by at most 2^2, so quantised values stay in (0, 256] —
 //    inside the e4m3 range (the converter does not saturate) and mostly in its
@@ -147,6 +155,13 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// mfma32_fp8 with block scales: D += 2^(ea - 127) 2^(eb - 127) A B, ea and eb
+// biased 8-bit exponents (byte 0 of the operand), here one per operand for
+// all lanes.  A power-of-two float32's exponent field is that byte.
+__device__ __forceinline__ f32x16 mfma32_fp8s(i32x8 a, i32x8 b, f32x16 c, int ea, int eb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
+}
+
 // max of three floats: max3f (v_maximum3_f32, written so that the compiler
 // sees the reads of the score MFMAs' results and waits for them)
 __device__ __forceinline__ float max3(float a, float b, float c) { return max3f(a, b, c); }
@@ -154,9 +169,10 @@ __device__ __forceinline__ float max3(float a, float b, float c) { return max3f(
 template <int N>
 using C = std::integral_constant<int, N>;
 
-template <bool CAUSAL, bool QK_I8>
+template <bool CAUSAL, bool QK_I8, bool POW2>
 __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
   using namespace fp8cfg;
+  static_assert(!(QK_I8 && POW2), "the power-of-two scale form is an e4m3 one");
   // score offset of the int8 form (see the file comment); 0 for e4m3
   constexpr float kSOff = QK_I8 ? 12582912.0f : 0.0f;
   // two-slot rings (tile j in slot j % 2) as four separate arrays, addressed
@@ -278,6 +294,7 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
   for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;
   asm volatile("" : "+v"(ones));
 
+  // ---- tiles with any positive scales -----------------------------------------
   auto compute = [&](int j, auto buf) {
     const int key0 = j * BC;
     if (!wave_active) return;
@@ -409,6 +426,117 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
     lq_run += qs[0] * inv_vratio;
   };
 
+  // ---- tiles with power-of-two scales -------------------------------------------
+  // m_e: the running (lazy) max of the row's exp2 arguments c s; minit holds
+  // kMu - m_e in all 16 registers, the score MFMAs' starting value.  Until a
+  // row's first tile m_e is 0 (l, lq and O are still zero, so the first tile's
+  // move rescales nothing that matters).
+  const int esq = (int)(__float_as_uint(sq) >> 23);  // Q block scale exponent
+  f32x16 minit;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) minit[r] = kMu;
+  float m_e = 0.f;
+  auto compute_pow2 = [&](int j, auto buf) {
+    const int key0 = j * BC;
+    if (!wave_active) return;
+    if (CAUSAL && key0 > wave_last_key) return;
+    const int blk = blocked ? key0 >> 7 : 0;
+    const int esk = (int)(__float_as_uint(ks_scale[blk]) >> 23);
+    const int esv = (int)(__float_as_uint(vs_scale[blk]) >> 23);
+    const uint8_t* ks = (decltype(buf)::value ? lds_k1 : lds_k0) + krow(l32) + kHalfStride * hh;
+    i32x8 kop[2][2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const u32x4 x0 = *(const u32x4*)(ks + krow(32 * tt) + 64 * kk);
+        const u32x4 x1 = *(const u32x4*)(ks + krow(32 * tt) + 64 * kk + kSecond);
+        kop[tt][kk] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      }
+    // x = sq sk (Q' K^T) + kMu - m_e: the exp2 argument (Q' = Q times the
+    // softmax scale times log2(e))
+    f32x16 x[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) x[tt] = mfma32_fp8s(kop[tt][0], qf[0], minit, esk, esq);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) x[tt] = mfma32_fp8s(kop[tt][1], qf[1], x[tt], esk, esq);
+    const bool need_mask = (key0 + BC > Lk) || (CAUSAL && key0 + BC - 1 > qw + diag);
+    if (need_mask) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * hh + 16 * tt + r;
+          if (key >= Lk || (CAUSAL && key > qi + diag)) x[tt][r] = -INFINITY;
+        }
+    }
+    float mx = x[0][0];
+#pragma unroll
+    for (int i = 1; i < 31; i += 2) mx = max3(mx, x[i >> 4][i & 15], x[(i + 1) >> 4][(i + 1) & 15]);
+    mx = max3(mx, x[1][15], x[1][15]);
+    const auto mxw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = max3(mx, __uint_as_float(mxw[0]), __uint_as_float(mxw[1]));
+    // the row's max moved by more than kTau (or this is its first tile): m_e
+    // becomes the tile's max, the accumulators are rescaled, and this tile's
+    // arguments and minit move with it (uniform branch, rare after the first
+    // tile).  A row with no valid key in its first tile has none at all (keys
+    // are masked from the sequence end or past the diagonal) and keeps m_e.
+    if (j == 0 || __builtin_amdgcn_ballot_w64(mx > kMu + kTau) != 0) {
+      const float m_tile = mx - kMu + m_e;
+      const float m_new = j == 0 ? (m_tile == -INFINITY ? m_e : m_tile) : max2f(m_e, m_tile);
+      const float delta = m_e - m_new;
+      const float alpha = fast_exp2(delta);
+      l_run *= alpha;
+      lq_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[tt][r] += delta;
+      const float mi = kMu - m_new;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) minit[r] = mi;
+      m_e = m_new;
+    }
+    // p = 2^x: float32 terms for the logsumexp, e4m3 codes for the MFMAs
+    float psum = 0.f;
+    uint32_t pw[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int tt = w >> 2, r0 = 4 * (w & 3);
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[e] = fast_exp2(x[tt][r0 + e]);
+        psum += p[e];
+      }
+      pw[w] = cvt_pk_fp8<true>(p[2], p[3], cvt_pk_fp8<false>(p[0], p[1], __float_as_uint(p[0])));
+    }
+    l_run += psum;
+    const i32x8 pk = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
+    // O^T += sv V^T P^T (the V block scale as the A operand's exponent)
+    const uint8_t* vs = (decltype(buf)::value ? lds_v1 : lds_v0) + vtr_off;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      u32x2 r[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) r[u] = lds_read_tr8(vs + vrow(8 * u) + 32 * dt);
+      const i32x8 vop = {(int)r[0][0], (int)r[0][1], (int)r[1][0], (int)r[1][1],
+                         (int)r[2][0], (int)r[2][1], (int)r[3][0], (int)r[3][1]};
+      oacc[dt] = mfma32_fp8s(vop, pk, oacc[dt], esv, 127);
+    }
+    // the sum of the e4m3-rounded probabilities of all 64 keys, as below
+    const f32x16 qsum = mfma32_fp8(ones, pk, zero16);
+    lq_run += qsum[0];
+  };
+  auto tile = [&](int j, auto buf) {
+    if constexpr (POW2) compute_pow2(j, buf);
+    else compute(j, buf);
+  };
+
   if (n_kv > 0) {
     dma_tile(0, C<0>{});
     wait_vmem();
@@ -416,23 +544,23 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
     // two tiles per iteration, so that every slot number is a constant
     for (int j = 0; j < n_kv; j += 2) {
       if (j + 1 < n_kv) dma_tile((j + 1) * BC, C<1>{});
-      compute(j, C<0>{});
+      tile(j, C<0>{});
       wait_vmem();
       __syncthreads();
       if (j + 1 < n_kv) {
         if (j + 2 < n_kv) dma_tile((j + 2) * BC, C<0>{});
-        compute(j + 1, C<1>{});
+        tile(j + 1, C<1>{});
         wait_vmem();
         __syncthreads();
       }
     }
   }
 
-  // epilogue: O = sv_ref * O_acc / lq', lse = ln2 * (m - kMu + log2 l')
+  // epilogue: O = sv_ref * O_acc / lq' (POW2: O_acc / lq'), lse = ln2 * (m - kMu + log2 l')
   const float l_tot = halfwave_sum(l_run);
   const float lq_tot = lq_run;  // already the full row sum
   if (qi < Lq) {
-    const float inv = lq_tot > 0.f ? sv_ref / lq_tot : 0.f;
+    const float inv = lq_tot > 0.f ? (POW2 ? 1.f : sv_ref) / lq_tot : 0.f;
     uint16_t* op = (uint16_t*)a.o + ((int64_t)b * Lq + qi) * a.H * D + (int64_t)h * D + 4 * hh;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -443,27 +571,31 @@ __global__ void __launch_bounds__(256, 3) fwd_fp8_kernel(Fp8Args a) {
                                                 pack2<kBF16>(o[4 * g + 2] * inv, o[4 * g + 3] * inv)};
       }
     if (hh == 0 && a.lse != nullptr)
-      a.lse[(int64_t)bh * Lq + qi] = l_tot > 0.f ? (m_run - kMu + __log2f(l_tot)) * kLn2 : -INFINITY;
+      a.lse[(int64_t)bh * Lq + qi] = l_tot > 0.f ? ((POW2 ? m_e : m_run) - kMu + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
-template <bool QK_I8>
+template <bool QK_I8, bool POW2>
 static hipError_t launch_8bit(const Fp8Args& a, int D, bool causal, hipStream_t s) {
   if (D != fp8cfg::D) return hipErrorNotSupported;
   const int n = a.B * a.H * a.n_qblk;
   if (causal)
-    hipLaunchKernelGGL((fwd_fp8_kernel<true, QK_I8>), dim3(n), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fwd_fp8_kernel<true, QK_I8, POW2>), dim3(n), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((fwd_fp8_kernel<false, QK_I8>), dim3(n), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fwd_fp8_kernel<false, QK_I8, POW2>), dim3(n), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_fp8(const Fp8Args& a, int D, bool causal, hipStream_t s) {
-  return launch_8bit<false>(a, D, causal, s);
+  return launch_8bit<false, false>(a, D, causal, s);
+}
+
+hipError_t launch_fwd_fp8_pow2(const Fp8Args& a, int D, bool causal, hipStream_t s) {
+  return launch_8bit<false, true>(a, D, causal, s);
 }
 
 hipError_t launch_fwd_int8(const Fp8Args& a, int D, bool causal, hipStream_t s) {
-  return launch_8bit<true>(a, D, causal, s);
+  return launch_8bit<true, false>(a, D, causal, s);
 }
 
 }  // namespace attn

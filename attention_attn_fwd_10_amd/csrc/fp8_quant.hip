@@ -4,6 +4,13 @@
 // (b, h, 128 rows) (or one per tensor for the baseline), scale = amax / 448,
 // code = e4m3fn(x / scale) with round-to-nearest-even and saturation.
 //
+// The power-of-two form (kE4M3Pow2) multiplies every value by a factor
+// `premul` first (float32; the softmax scale times log2(e) for Q, 1 for K and
+// V) and takes as scale the smallest power of two at or above amax / 448 (at
+// least 2^-126): the division is then exact, and the scale is what the matrix
+// cores' block-scale operands take (an 8-bit exponent), so the matching
+// forward applies the scales inside its MFMAs.
+//
 // The int8 form (the case study's int8 path) quantises symmetrically instead:
 // scale = amax / 127, code = x / scale rounded to nearest-even and clamped to
 // [-127, 127].
@@ -17,9 +24,10 @@
 //    a +-1 matrix, exact in bf16 operands (the signs flip sign bits of the bf16
 //    inputs; H_D's entries are generated in registers from the parity of the
 //    row and column indices) with float32 accumulation;
-//  * the quotient x / scale, which decides the code, is correctly rounded
-//    float32 without a division per element: r = 1 / scale once per block,
-//    q = x r, then two residual corrections q += fma(-q, scale, x) r (with r
+//  * amax / 448 and int8: the quotient x / scale, which decides the code, is
+//    correctly rounded float32 without a division per element: r = 1 / scale
+//    once per block, q = x r, then two residual corrections
+//    q += fma(-q, scale, x) r (with r
 //    within half an ulp of 1 / scale each residual is exact and the corrected
 //    quotient is the correctly rounded one).  Blocks whose scale is below
 //    2^-60 are first multiplied by 2^64 (exact), so no residual falls in the
@@ -37,7 +45,7 @@ __device__ __forceinline__ uint32_t int8_encode(float y) {
 }
 
 enum QuantMode { kQuantBlock = 0, kAmaxOnly = 1, kQuantGlobal = 2 };
-enum QuantFormat { kE4M3 = 0, kInt8 = 1 };
+enum QuantFormat { kE4M3 = 0, kInt8 = 1, kE4M3Pow2 = 2 };
 
 template <int FMT>
 constexpr float code_max() { return FMT == kInt8 ? 127.f : 448.f; }
@@ -85,11 +93,37 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// scale of a block (or of the tensor) from its amax
+// scale of a block (or of the tensor) from its amax: amax / 448 or amax /
+// 127 (correctly rounded); for kE4M3Pow2 the smallest power of two at or above
+// amax / 448 (the quotient rounded to float32), and at least 2^-126, the
+// smallest normal float; 1 for an all-zero block
 template <int FMT>
 __device__ __forceinline__ float scale_of(float amax) {
-  return amax > 0.f ? __fdiv_rn(amax, code_max<FMT>()) : 1.f;
+  if (!(amax > 0.f)) return 1.f;
+  const float t = __fdiv_rn(amax, code_max<FMT>());
+  if constexpr (FMT != kE4M3Pow2) {
+    return t;
+  } else {
+    uint32_t u = __float_as_uint(t);
+    if (u < 0x00800000u) return 0x1p-126f;
+    if (u & 0x007fffffu) u = (u & 0x7f800000u) + 0x00800000u;
+    return __uint_as_float(u);
+  }
 }
+
+// x / scale: correctly rounded (QuotientRN), or for the power-of-two scales
+// exact, one multiply by the exact reciprocal
+template <int FMT>
+struct Divider : QuotientRN {
+  __device__ __forceinline__ explicit Divider(float scale) : QuotientRN(scale) {}
+};
+template <>
+struct Divider<kE4M3Pow2> {
+  float r;
+  static constexpr float pre = 1.f;
+  __device__ __forceinline__ explicit Divider(float scale) : r(1.f / scale) {}
+  __device__ __forceinline__ float operator()(float x) const { return x * r; }
+};
 
 // ---------------------------------------------------------------------------
 // Without rotation: D/16 lanes per row, 16 consecutive values per lane.
@@ -125,6 +159,10 @@ __global__ void __launch_bounds__(256) quant_plain_kernel(QuantArgs a) {
         x[p][8 + 2 * e] = __uint_as_float(hi[e] << 16);
         x[p][8 + 2 * e + 1] = __uint_as_float(hi[e] & 0xffff0000u);
       }
+      if constexpr (FMT == kE4M3Pow2) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[p][e] *= a.premul;
+      }
     } else {
 #pragma unroll
       for (int e = 0; e < 16; ++e) x[p][e] = 0.f;
@@ -147,7 +185,7 @@ __global__ void __launch_bounds__(256) quant_plain_kernel(QuantArgs a) {
     scale = scale_of<FMT>(block_max(amax, red));
     if (tid == 0) a.scales[(int64_t)bh * nblk + blk] = scale;
   }
-  const QuotientRN div(scale);
+  const Divider<FMT> div(scale);
   if (div.pre != 1.f) {  // uniform: a block of tiny values
 #pragma unroll
     for (int p = 0; p < NP; ++p)
@@ -247,6 +285,7 @@ __global__ void __launch_bounds__(256) quant_rot_kernel(QuantArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       acc[jt][r] *= norm;
+      if constexpr (FMT == kE4M3Pow2) acc[jt][r] *= a.premul;
       amax = fmaxf(amax, fabsf(acc[jt][r]));
     }
 
@@ -263,7 +302,7 @@ __global__ void __launch_bounds__(256) quant_rot_kernel(QuantArgs a) {
     scale = scale_of<FMT>(block_max(amax, red));
     if (tid == 0) a.scales[(int64_t)bh * nblk + blk] = scale;
   }
-  const QuotientRN div(scale);
+  const Divider<FMT> div(scale);
   if (div.pre != 1.f) {
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt)
@@ -287,10 +326,8 @@ __global__ void __launch_bounds__(256) quant_rot_kernel(QuantArgs a) {
 
 // per-tensor mode helpers: clear the reduction cell, then turn amax into the scale
 __global__ void fp8_fill_kernel(float* p, float v) { *p = v; }
-__global__ void fp8_finalize_scale_kernel(float* p, float code_max) {
-  const float amax = *p;
-  *p = amax > 0.f ? __fdiv_rn(amax, code_max) : 1.f;
-}
+template <int FMT>
+__global__ void fp8_finalize_scale_kernel(float* p) { *p = scale_of<FMT>(*p); }
 
 template <int D, int MODE, int FMT>
 void launch_quant_pass(const QuantArgs& a, dim3 grid, hipStream_t s) {
@@ -310,7 +347,7 @@ hipError_t launch_quant_d(const QuantArgs& a, hipStream_t s) {
   }
   hipLaunchKernelGGL(fp8_fill_kernel, dim3(1), dim3(1), 0, s, a.scales, 0.f);
   launch_quant_pass<D, kAmaxOnly, FMT>(a, grid, s);
-  hipLaunchKernelGGL(fp8_finalize_scale_kernel, dim3(1), dim3(1), 0, s, a.scales, code_max<FMT>());
+  hipLaunchKernelGGL(fp8_finalize_scale_kernel<FMT>, dim3(1), dim3(1), 0, s, a.scales);
   launch_quant_pass<D, kQuantGlobal, FMT>(a, grid, s);
   return hipGetLastError();
 }
@@ -323,6 +360,9 @@ static hipError_t launch_quant(const QuantArgs& a, int D, hipStream_t s) {
 }
 
 hipError_t launch_fp8_quantize(const QuantArgs& a, int D, hipStream_t s) { return launch_quant<kE4M3>(a, D, s); }
+hipError_t launch_fp8_quantize_pow2(const QuantArgs& a, int D, hipStream_t s) {
+  return launch_quant<kE4M3Pow2>(a, D, s);
+}
 hipError_t launch_int8_quantize(const QuantArgs& a, int D, hipStream_t s) { return launch_quant<kInt8>(a, D, s); }
 
 }  // namespace attn

@@ -166,6 +166,29 @@ attn_status_t attn_fp8_quantize(const void* x, const int64_t x_strides[3],
                                 int block_rows, const int8_t* signs, void* stream);
 
 /*
+ * attn_fp8_quantize_pow2 — the 8-bit prologue with power-of-two block scales,
+ * the input form of attn_fwd_fp8_pow2.  ("Fused attention kernel" page,
+ * section "8-bit forward pass": one scale per block, whose format the section
+ * leaves open; a power of two is a shared exponent, the block-scale form the
+ * gfx950 matrix cores apply inside their products.)
+ *
+ * Arguments as for attn_fp8_quantize, plus
+ * premul: finite and > 0; every (rotated) value is multiplied by it in
+ *   float32, x'' = x' * premul, before the amax and the coding.  Pass 1 for K
+ *   and V, and softmax_scale * log2(e) for Q: attn_fwd_fp8_pow2 takes the
+ *   softmax scale from the Q codes (its scores are then base-2 exponents).
+ * Each scale is a power of two: the smallest one at or above amax / 448 (the
+ * quotient rounded to float32; amax of |x''| over the block), and at least
+ * 2^-126; 1 for an all-zero block.  Each code is e4m3fn(x'' / scale) (an
+ * exact division) rounded to nearest-even and saturated to +-448.
+ */
+attn_status_t attn_fp8_quantize_pow2(const void* x, const int64_t x_strides[3],
+                                     uint8_t* x8, float* scales,
+                                     int B, int H, int S, int D,
+                                     int block_rows, const int8_t* signs, float premul,
+                                     void* stream);
+
+/*
  * attn_fwd_fp8 — 8-bit fused forward on quantised inputs.
  * ("Fused attention kernel" page, section "8-bit forward pass": both GEMMs in
  * e4m3, V tiles transposed on chip rather than in a global pass, per-block
@@ -186,6 +209,27 @@ attn_status_t attn_fwd_fp8(const uint8_t* q8, const float* q_scale,
                            void* o, float* lse,
                            int B, int H, int Sq, int Sk, int D,
                            float softmax_scale, int causal, void* stream);
+
+/*
+ * attn_fwd_fp8_pow2 — attn_fwd_fp8 on the power-of-two form: the block scales
+ * enter the matrix-core products as their exponents, and the score products
+ * return the exp2 argument directly (no multiply-add per score).
+ *
+ * q8, k8, v8 and their scales as written by attn_fp8_quantize_pow2: q with
+ * premul = softmax_scale * log2(e), k and v with premul = 1 (the same `signs`
+ * for q and k, none for v).  There is no softmax_scale argument: the Q codes
+ * carry it.  Every scale must be a power of two in [2^-126, 2^127] (the kernel
+ * reads a scale's exponent bits only).  Other arguments, outputs (lse: natural
+ * log of the row sum of exp(softmax_scale q.k)) and errors as for
+ * attn_fwd_fp8.
+ */
+attn_status_t attn_fwd_fp8_pow2(const uint8_t* q8, const float* q_scale,
+                                const uint8_t* k8, const float* k_scale,
+                                const uint8_t* v8, const float* v_scale,
+                                int block_rows,
+                                void* o, float* lse,
+                                int B, int H, int Sq, int Sk, int D,
+                                int causal, void* stream);
 
 /*
  * attn_int8_quantize — the int8 prologue for Q or K.

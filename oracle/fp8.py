@@ -17,6 +17,15 @@ Readings where the pages are silent:
   block is amax / 448 computed in float32 (1 when amax = 0), and a value is
   coded as e4m3(x / scale) with the division in float32 — the quantised code is
   a float decision, so it is taken in the kernel's precision (float32);
+* the power-of-two form (the input form of the forward that applies block
+  scales inside its matrix-core products): the section fixes no scale format,
+  and a power of two is a shared exponent.  Its scale is the smallest power of
+  two at or above amax / 448 (that quotient rounded to float32), at least
+  2^-126 (1 when amax = 0), so x / scale is exact; Q is first multiplied by
+  the softmax scale times log2(e) (float32 products, the kernel's precision
+  for the code decision), so that the scores come out as base-2 exponents —
+  any per-block scale multiplies Q K^T exactly, so attention is unchanged
+  once that factor is divided out of the dequantised Q;
 * the rotation is M = diag(sigma) H_D / sqrt(D) with H_D the Sylvester
   Hadamard matrix, applied along the head dimension to Q and K only;
 * V is block-quantised without rotation.
@@ -167,6 +176,39 @@ def quantize(x_bshd, block_rows: int = BLOCK_ROWS):
     return codes, scales
 
 
+def scale_pow2_from_amax(amax) -> np.ndarray:
+    """Power-of-two form: the smallest power of two >= float32(amax / 448), at
+    least 2^-126; 1 for an all-zero block."""
+    a = np.asarray(amax, dtype=np.float32)
+    t = (a / np.float32(E4M3_MAX)).astype(np.float32)
+    mant, ex = np.frexp(t.astype(np.float64))          # t = mant * 2^ex, mant in [0.5, 1)
+    e = np.where(mant == 0.5, ex - 1, ex)               # t a power of two: itself
+    e = np.where(t > 0, np.maximum(e, -126), -126)      # (a quotient that underflows to 0 too)
+    return np.where(a > 0, np.exp2(e.astype(np.float64)), 1.0).astype(np.float32)
+
+
+def quantize_pow2(x_bshd, block_rows: int = BLOCK_ROWS, premul: float = 1.0):
+    """The power-of-two form of quantize: x taken to float32 and multiplied by
+    float32(premul) in float32, then scales from scale_pow2_from_amax and codes
+    e4m3(x / scale) (an exact division).  Returns (codes, scales) shaped as
+    quantize's."""
+    x = np.asarray(x_bshd, dtype=np.float32) * np.float32(premul)
+    B, S, H, D = x.shape
+    if block_rows == 0:
+        scale = scale_pow2_from_amax(np.abs(x).max() if x.size else 0.0).reshape(1)
+        return e4m3_encode(x.astype(np.float64) / float(scale[0])), scale
+    nblk = (S + block_rows - 1) // block_rows
+    scales = np.ones((B, H, nblk), dtype=np.float32)
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    for i in range(nblk):
+        lo, hi = i * block_rows, min((i + 1) * block_rows, S)
+        blk = x[:, lo:hi]
+        sc = scale_pow2_from_amax(np.abs(blk).max(axis=(1, 3)))
+        scales[:, :, i] = sc
+        codes[:, lo:hi] = e4m3_encode(blk.astype(np.float64) / sc[:, None, :, None].astype(np.float64))
+    return codes, scales
+
+
 def dequantize(codes, scales, block_rows: int = BLOCK_ROWS) -> np.ndarray:
     """codes [B, S, H, D] with their scales -> float64 values."""
     vals = e4m3_decode(codes)
@@ -190,6 +232,32 @@ def quantize_pipeline(q, k, v, signs=None, block_rows: int = BLOCK_ROWS):
     v8, vs = quantize(v, block_rows)
     return dict(q8=q8, q_scale=qs, k8=k8, k_scale=ks, v8=v8, v_scale=vs,
                 block_rows=block_rows)
+
+
+LOG2E = 1.4426950408889634
+
+
+def quantize_pipeline_pow2(q, k, v, signs=None, block_rows: int = BLOCK_ROWS, *, scale: float):
+    """quantize_pipeline in the power-of-two form: Q' multiplied by the softmax
+    scale times log2(e) before its quantisation.  The dict also holds that
+    factor as q_premul."""
+    if signs is not None:
+        q = rotate(q, signs).astype(np.float32)
+        k = rotate(k, signs).astype(np.float32)
+    pm = float(scale) * LOG2E
+    q8, qs = quantize_pow2(q, block_rows, pm)
+    k8, ks = quantize_pow2(k, block_rows)
+    v8, vs = quantize_pow2(v, block_rows)
+    return dict(q8=q8, q_scale=qs, k8=k8, k_scale=ks, v8=v8, v_scale=vs,
+                block_rows=block_rows, q_premul=pm)
+
+
+def dequantize_pipeline(qp):
+    """Float64 Q', K', V of a quantize_pipeline(_pow2) result, a Q premul
+    divided out (so that the softmax scale applies to Q' K'^T again)."""
+    br = qp["block_rows"]
+    qd = dequantize(qp["q8"], qp["q_scale"], br) / qp.get("q_premul", 1.0)
+    return qd, dequantize(qp["k8"], qp["k_scale"], br), dequantize(qp["v8"], qp["v_scale"], br)
 
 
 def emulate_fp8_attention(q, k, v, scale: float, signs=None, block_rows: int = BLOCK_ROWS,

@@ -63,6 +63,7 @@ template hipError_t launch_fwd16<64, 1, false, kDenseWide>(FwdArgs, hipStream_t)
 template hipError_t launch_fwd16<128, 0, false, kDenseWide>(FwdArgs, hipStream_t);
 template hipError_t launch_fwd16<128, 1, false, kDenseWide>(FwdArgs, hipStream_t);
 hipError_t launch_fp8_quantize(const QuantArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_fp8_quantize_pow2(const QuantArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_int8_quantize(const QuantArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_splitkv_merge(const MergeArgs&, int, int, hipStream_t) { ++g_launches; return hipSuccess; }
 }  // namespace attn
@@ -74,6 +75,7 @@ hipError_t launch_tail_merge(const TailMergeArgs& a, int, int, hipStream_t) {
   return hipSuccess;
 }
 hipError_t launch_fwd_fp8(const Fp8Args&, int, bool, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_fwd_fp8_pow2(const Fp8Args&, int, bool, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_fwd_int8(const Fp8Args&, int, bool, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_bwd(const BwdArgs&, int, int, bool, hipStream_t) { ++g_launches; return hipSuccess; }
 static float g_scratch[16];
@@ -244,6 +246,10 @@ int main() {
   expect("fp8_quant_ok", attn_fp8_quantize(p, st, q8, fbuf, 1, 4, 2, 128, 128, signs, nullptr), ATTN_OK);
   expect("fp8_quant_block_64", attn_fp8_quantize(p, st, q8, fbuf, 1, 4, 2, 128, 64, signs, nullptr), ATTN_ERR_INVALID);
   expect("fp8_quant_s_int_max", attn_fp8_quantize(p, st, q8, fbuf, 1, 4, INT_MAX, 128, 128, signs, nullptr), ATTN_OK);
+  expect("fp8_pow2_quant_ok", attn_fp8_quantize_pow2(p, st, q8, fbuf, 1, 4, 2, 128, 128, signs, 0.1275f, nullptr), ATTN_OK);
+  expect("fp8_pow2_quant_premul_0", attn_fp8_quantize_pow2(p, st, q8, fbuf, 1, 4, 2, 128, 128, signs, 0.f, nullptr), ATTN_ERR_INVALID);
+  expect("fp8_pow2_fwd_ok", attn_fwd_fp8_pow2(q8, fbuf, q8, fbuf, q8, fbuf, 128, p, lse, 1, 4, 2, 2, 128, 1, nullptr), ATTN_OK);
+  expect("fp8_pow2_fwd_d64", attn_fwd_fp8_pow2(q8, fbuf, q8, fbuf, q8, fbuf, 128, p, lse, 1, 4, 2, 2, 64, 0, nullptr), ATTN_ERR_UNSUPPORTED);
   expect("int8_quant_ok", attn_int8_quantize(p, st, (int8_t*)q8, fbuf, 1, 4, 2, 128, 0, signs, nullptr), ATTN_OK);
   expect("fp8_fwd_ok", attn_fwd_fp8(q8, fbuf, q8, fbuf, q8, fbuf, 128, p, lse, 1, 4, 2, 2, 128, sc, 1, nullptr), ATTN_OK);
   expect("fp8_fwd_d64", attn_fwd_fp8(q8, fbuf, q8, fbuf, q8, fbuf, 128, p, lse, 1, 4, 2, 2, 64, sc, 0, nullptr), ATTN_ERR_UNSUPPORTED);

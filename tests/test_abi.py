@@ -30,6 +30,8 @@ def lib():
     L.attn_fwd.argtypes = [I, P, I64P, P, I64P, P, I64P, P, I64P, P, I, I, I, I, I, F, I, P]
     L.attn_fp8_quantize.argtypes = [P, I64P, P, P, I, I, I, I, I, P, P]
     L.attn_fwd_fp8.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, I, F, I, P]
+    L.attn_fp8_quantize_pow2.argtypes = [P, I64P, P, P, I, I, I, I, I, P, F, P]
+    L.attn_fwd_fp8_pow2.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, P]
     L.attn_bwd.argtypes = [I, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, P]
     L.attn_int8_quantize.argtypes = [P, I64P, P, P, I, I, I, I, I, P, P]
     L.attn_fwd_int8.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, I, F, I, P]
@@ -58,7 +60,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("attn_fwd", "attn_fp8_quantize", "attn_fwd_fp8", "attn_fwd_varlen", "attn_fwd_splitkv",
+    for n in ("attn_fwd", "attn_fp8_quantize", "attn_fwd_fp8", "attn_fp8_quantize_pow2", "attn_fwd_fp8_pow2",
+              "attn_fwd_varlen", "attn_fwd_splitkv",
               "attn_fwd_splitkv_workspace_bytes", "attn_fwd_bias", "attn_int8_quantize", "attn_fwd_int8",
               "attn_bwd", "attn_status_string", "attn_last_error", "attn_fwd_splitkv_noalloc",
               "attn_set_index_checks", "attn_check_indices_host"):
@@ -147,6 +150,24 @@ def test_quantize_validation(lib, name):
     assert q(sc=None) == INVALID
     assert q(S=-1) == INVALID
     assert q(S=0) == OK
+
+
+def test_quantize_pow2_validation(lib):
+    q = lambda **k: lib.attn_fp8_quantize_pow2(A16, GOOD, A16, A16, 1, 1, 1, k.get("D", 128), k.get("br", 128), None,
+                                               k.get("pm", 1.0), None)
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert q(pm=bad) == INVALID
+    assert q(br=64) == INVALID
+    assert q(D=96) == UNSUPPORTED
+
+
+def test_fp8_pow2_fwd_validation(lib):
+    f = lambda **k: lib.attn_fwd_fp8_pow2(A16, A16, A16, A16, A16, A16, k.get("br", 128), A16, None, 1, 1, 1, 1,
+                                          k.get("D", 128), k.get("causal", 0), None)
+    assert f(D=64) == UNSUPPORTED
+    assert f(D=-1) == INVALID
+    assert f(br=7) == INVALID
+    assert f(causal=5) == INVALID
 
 
 @pytest.mark.parametrize("name", ["attn_fwd_fp8", "attn_fwd_int8"])

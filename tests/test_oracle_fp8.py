@@ -200,3 +200,97 @@ def test_half_ulp_of_16bit_outputs(fmt):
         nxt = (bits + 1).astype(np.uint16).view(np.float16).astype(np.float64)
     assert np.array_equal(2 * half_ulp(x, fmt), nxt - x)
     assert half_ulp(1.0, fmt) == (2.0 ** -8 if fmt == "bf16" else 2.0 ** -11)
+
+
+# ---------------------------------------------------------------------------
+# the power-of-two form
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("amax,scale", [
+    (448.0, 1.0),                  # amax / 448 = 1 exactly
+    (447.99, 1.0),
+    (449.0, 2.0),                  # just above a power of two: the next one
+    (672.0, 2.0),                  # 1.5
+    (224.0, 0.5),
+    (223.9, 0.5),
+    (448.0 * 2.0 ** -20, 2.0 ** -20),
+    (3.0e38, 2.0 ** 120),          # 6.7e35 lies in (2^119, 2^120]
+    (1e-40, 2.0 ** -126),          # quotient below the normal range: the floor
+    (2.0 ** -149, 2.0 ** -126),    # quotient that rounds to zero
+    (0.0, 1.0),                    # an all-zero block
+])
+def test_pow2_scale_values(amax, scale):
+    """Hand-derived values of the power-of-two scale rule (smallest power of
+    two at or above float32(amax / 448), at least 2^-126, 1 for amax = 0)."""
+    assert float(F.scale_pow2_from_amax(np.float32(amax))) == scale
+
+
+def test_pow2_block_quantiser_properties():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((2, 300, 3, 64)).astype(np.float32)
+    x[1, 130:256, 2] = 0.0                              # an all-zero block -> scale 1
+    codes, scales = F.quantize_pow2(x, 128)
+    assert scales.shape == (2, 3, 3)
+    for b in range(2):
+        for h in range(3):
+            for i in range(3):
+                blk = x[b, i * 128:(i + 1) * 128, h]
+                amax = np.abs(blk).max()
+                if amax == 0:
+                    assert scales[b, h, i] == 1.0
+                    assert (codes[b, i * 128:(i + 1) * 128, h] == 0).all()
+                    continue
+                sc = float(scales[b, h, i])
+                t = float(np.float32(amax) / np.float32(448))
+                # a power of two, the smallest at or above amax / 448
+                assert np.frexp(sc)[0] == 0.5
+                assert sc >= t and sc / 2 < t
+                # so the largest magnitude, in (224, 448] after the division,
+                # codes to a value in [224, 448]
+                top = np.abs(F.e4m3_decode(codes[b, i * 128:(i + 1) * 128, h])).max()
+                assert 224 <= top <= 448
+    deq = F.dequantize(codes, scales, 128)
+    # error at most half an e4m3 spacing (in scaled units): the division is exact
+    sc = np.transpose(scales, (0, 2, 1))[:, np.arange(300) // 128][..., None]
+    err = np.abs(deq - x) / sc
+    assert (err <= 0.5 * F.e4m3_ulp(x / sc)).all()
+    # per tensor: the same rule over the whole tensor
+    c0, s0 = F.quantize_pow2(x, 0)
+    t = float(np.float32(np.abs(x).max()) / np.float32(448))
+    assert s0.shape == (1,) and np.frexp(float(s0[0]))[0] == 0.5 and s0[0] >= t and s0[0] / 2 < t
+
+
+def test_pow2_premul_invariance_and_error():
+    """Multiplying by a power of two moves the scales by it and leaves the codes
+    alone (every step of the rule is exact under it); any premul codes
+    x * premul to within half an e4m3 step in scaled units."""
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((1, 260, 2, 64)).astype(np.float32)
+    c0, s0 = F.quantize_pow2(x, 128)
+    for k in (-7, 3):
+        c1, s1 = F.quantize_pow2(x, 128, premul=2.0 ** k)
+        assert np.array_equal(c1, c0)
+        assert np.array_equal(s1, s0 * np.float32(2.0 ** k))
+    pm = 0.0883883476 * 1.4426950408889634
+    c2, s2 = F.quantize_pow2(x, 128, premul=pm)
+    xp = (x * np.float32(pm)).astype(np.float64)
+    sc = np.transpose(s2, (0, 2, 1))[:, np.arange(260) // 128][..., None].astype(np.float64)
+    err = np.abs(F.dequantize(c2, s2, 128) - xp) / sc
+    assert (err <= 0.5 * F.e4m3_ulp(xp / sc)).all()
+
+
+def test_pow2_pipeline_premul_cancels():
+    """quantize_pipeline_pow2 codes Q times the softmax scale times log2(e);
+    dequantize_pipeline divides that factor out again, so the dequantised Q'
+    is Q' to within the e4m3 rounding, and the emulated attention is close to
+    that of the amax / 448 pipeline."""
+    rng = np.random.default_rng(10)
+    q, k, v = (rng.standard_normal((1, 130, 2, 128)).astype(np.float32) for _ in range(3))
+    sc = 1 / math.sqrt(128)
+    qp = F.quantize_pipeline_pow2(q, k, v, None, 128, scale=sc)
+    assert qp["q_premul"] == pytest.approx(1.4426950408889634 * sc, rel=1e-15)
+    qd, kd, vd = F.dequantize_pipeline(qp)
+    assert np.abs(qd - q).max() <= np.abs(q).max() * 2.0 ** -4
+    ref, _ = A.attention_bshd(q, k, v, sc)
+    o2, _ = A.attention_bshd(qd, kd, vd, sc)
+    o1, _ = A.attention_bshd(*F.dequantize_pipeline(F.quantize_pipeline(q, k, v, None, 128)), sc)
+    assert F.rmse(o2, ref) < 2 * F.rmse(o1, ref)
