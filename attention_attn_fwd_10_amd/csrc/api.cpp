@@ -101,7 +101,7 @@ hipError_t dispatch_causal_mode(const attn::FwdArgs& a, bool causal, int mode, h
     if (mode == kDenseBias)
       return causal ? launch_one<D, DT, true, kDenseBias>(a, s) : launch_one<D, DT, false, kDenseBias>(a, s);
   }
-  if constexpr (D <= 128) {
+  if constexpr (D == 128) {
     if (mode == kDenseWide && !causal) return launch_one<D, DT, false, kDenseWide>(a, s);
   }
   if (mode == kDense)
@@ -144,18 +144,18 @@ int device_cus() {
   return n;
 }
 
-// Schedule of the dense forward.  The non-causal forward at head dims 64 and
-// 128 with at least kWideMinKeys keys runs in 256-row workgroups (attn::kDenseWide,
+// Schedule of the dense forward.  The non-causal forward at head dim 128 with
+// at least kWideMinKeys keys runs in 256-row workgroups (attn::kDenseWide,
 // one per CU, each K/V tile copied once for 8 waves) when its grid fills
 // whole rounds of the CUs; when the last round is at most half full and a
 // workspace is at hand, the work items of that round run as key ranges
 // spread over the whole chip (at most kMaxTailSplits per item), and a merge
 // combines their partial results.  Anything else runs the 128-row workgroups
 // of attn::kDense.  (Measured: the wide layout is 4-5 % faster at head dim 128
-// from 4096 keys on and 1.4-2 % at head dim 64; below 4096 keys it is at best
-// even (d128, 2048 keys) and down to 6 % (d128) and 13 % (d64) slower at 512,
-// where the fixed cost of a work item weighs more and one workgroup per CU
-// cannot hide it behind another's key loop.)
+// from 4096 keys on; below 4096 keys it is at best even (2048 keys) and down
+// to 6 % slower at 512, where the fixed cost of a work item weighs more and
+// one workgroup per CU cannot hide it behind another's key loop.  Head dim 64
+// runs 3-4 of the 128-row workgroups per CU instead, which beat it.)
 constexpr int kMaxTailSplits = 8;
 constexpr int kWideMinKeys = 4096;
 struct DensePlan {
@@ -165,7 +165,7 @@ struct DensePlan {
 };
 DensePlan plan_dense(int B, int H, int Sq, int Sk, int D, bool causal, int cus, bool have_workspace) {
   DensePlan p;
-  if (causal || D > 128 || cus <= 0 || Sk < kWideMinKeys) return p;
+  if (causal || D != 128 || cus <= 0 || Sk < kWideMinKeys) return p;
   const int64_t nq = ((int64_t)Sq + attn::kWideRows - 1) / attn::kWideRows;
   const int64_t n = (int64_t)B * H * nq;
   if (n < cus || n > INT32_MAX - (int64_t)cus * kMaxTailSplits) return p;

@@ -17,7 +17,7 @@ constexpr int kFP16 = 1;
 
 // kDenseWide: the dense layout in workgroups of 256 query rows (8 waves, one
 // workgroup per CU, each K/V tile copied once for all of them; non-causal,
-// head dims 64 and 128); the work items of a last, partial round of the grid may run
+// head dim 128); the work items of a last, partial round of the grid may run
 // as key ranges (FwdArgs tail_start) whose partial results a merge combines.
 enum KvMode { kDense = 0, kVarlen = 1, kPaged = 2, kDenseBias = 3, kDenseWide = 4 };
 constexpr int kWideRows = 256;  // query rows per kDenseWide workgroup

@@ -4,5 +4,4 @@
 namespace attn {
 ATTN_INSTANTIATE_FWD16(64)
 ATTN_INSTANTIATE_FWD16_BIAS(64)
-ATTN_INSTANTIATE_FWD16_WIDE(64)
 }  // namespace attn

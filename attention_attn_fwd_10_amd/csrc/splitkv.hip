@@ -145,14 +145,9 @@ hipError_t launch_splitkv_merge(const MergeArgs& a, int D, int dtype, hipStream_
 hipError_t launch_tail_merge(const TailMergeArgs& a, int D, int dtype, hipStream_t s) {
   const int64_t rows = (int64_t)a.n_tail * kWideRows;
   const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-  if (D != 64 && D != 128) return hipErrorInvalidValue;  // the wide layout's head dims
-  if (dtype == kBF16) {
-    if (D == 64) hipLaunchKernelGGL((tail_merge_kernel<64, kBF16>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((tail_merge_kernel<128, kBF16>), grid, block, 0, s, a);
-  } else {
-    if (D == 64) hipLaunchKernelGGL((tail_merge_kernel<64, kFP16>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((tail_merge_kernel<128, kFP16>), grid, block, 0, s, a);
-  }
+  if (D != 128) return hipErrorInvalidValue;  // the wide layout's head dim
+  if (dtype == kBF16) hipLaunchKernelGGL((tail_merge_kernel<128, kBF16>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((tail_merge_kernel<128, kFP16>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

@@ -80,8 +80,8 @@ attn_status_t attn_fwd(int dtype,
 
 /*
  * attn_fwd_ws — attn_fwd with a workspace, which lets the non-causal forward
- * at head dims 64 and 128 (4096 keys or more) split the last, partial round
- * of its grid by keys.
+ * at head dim 128 (4096 keys or more) split the last, partial round of its
+ * grid by keys.
  * (The "Fused attention kernel" page's implementation sketch keeps a running
  * row max and row sum per query, so the partial results of key ranges merge
  * exactly through their logsumexps, as for attn_fwd_splitkv.)

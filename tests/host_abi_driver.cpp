@@ -58,8 +58,6 @@ INST(64, 0, false) INST(64, 0, true) INST(64, 1, false) INST(64, 1, true)
 INST(128, 0, false) INST(128, 0, true) INST(128, 1, false) INST(128, 1, true)
 INST(256, 0, false) INST(256, 0, true) INST(256, 1, false) INST(256, 1, true)
 #undef INST
-template hipError_t launch_fwd16<64, 0, false, kDenseWide>(FwdArgs, hipStream_t);
-template hipError_t launch_fwd16<64, 1, false, kDenseWide>(FwdArgs, hipStream_t);
 template hipError_t launch_fwd16<128, 0, false, kDenseWide>(FwdArgs, hipStream_t);
 template hipError_t launch_fwd16<128, 1, false, kDenseWide>(FwdArgs, hipStream_t);
 hipError_t launch_fp8_quantize(const QuantArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
@@ -167,7 +165,8 @@ int main() {
     n = g_launches;
     expect("fwd_d64", attn_fwd(ATTN_BF16, p, wst, p, wst, p, wst, p, wst, lse, 1, 8, 8192, 8192, 64, sc, 0, nullptr),
            ATTN_OK);
-    expect("fwd_d64_plan", g_launches - n == 1 && g_fwd_mode == attn::kDenseWide && g_fwd_d == 64, 1);
+    expect("fwd_d64_plan", g_launches - n == 1 && g_fwd_mode == attn::kDense && g_fwd_d == 64, 1);
+    expect("ws_bytes_d64", (int)attn_fwd_workspace_bytes(ATTN_BF16, 1, 8, 8448, 8448, 64, 0), 0);
     n = g_launches;
     expect("fwd_d256", attn_fwd(ATTN_BF16, p, wst, p, wst, p, wst, p, wst, lse, 1, 8, 8192, 8192, 256, sc, 0, nullptr),
            ATTN_OK);
