@@ -468,6 +468,37 @@ def splitkv_num_splits(n_work, max_seqlen_k, target=2048, min_tiles=4, max_split
     return int(max(1, min(-(-tiles // per), tiles // int(min_tiles), max_splits)))
 
 
+def decode_num_splits(n_seq_heads, max_seqlen_k, target=1024, min_tiles=2, max_splits=256):
+    """A split count for one query row per sequence at head dim 128 (the
+    streaming decode kernel, one wave per sequence, key range and head): about
+    `target` waves (n_seq_heads x splits; one per SIMD of the chip), at least
+    `min_tiles` 64-key tiles per range and no empty range.  Measured on
+    one-query decoding (d128): 4 x 32 heads x 32768 keys 8 splits 5.91 TB/s (16:
+    5.75), 16 x 32 x 8192 2 splits 5.92 (4: 5.82), 1 x 32 x 131072 32 splits
+    5.59 (64: 5.22), 64 x 8 x 4096 2 splits 5.25 (4: 4.83)."""
+    tiles = max(1, (int(max_seqlen_k) + 63) // 64)
+    want = max(1, -(-int(target) // max(1, int(n_seq_heads))))
+    splits = max(1, min(want, tiles // int(min_tiles), int(max_splits)))
+    per = -(-tiles // splits)
+    return int(-(-tiles // per))
+
+
+DECODE_MIN_WAVES = 512  # fewest (sequence, key range, head) items the library runs on the decode kernel
+
+
+def auto_num_splits(B, H, D, total_q, max_seqlen_q, max_seqlen_k, page_size=0):
+    """The split count fwd_splitkv takes when none is given: the decode rule
+    when the library runs the decode kernel (one query row per sequence, head
+    dim 128, packed or pages of at least 64 tokens, enough waves), else the
+    tiled kernel's rule."""
+    if int(max_seqlen_q) == 1 and int(D) == 128 and (int(page_size) == 0 or int(page_size) >= 64):
+        splits = decode_num_splits(int(B) * int(H), max_seqlen_k)
+        if int(B) * int(H) * splits >= DECODE_MIN_WAVES:
+            return splits
+    n_work = int(H) * (-(-int(total_q) // 128) + int(B))
+    return splitkv_num_splits(n_work, max_seqlen_k)
+
+
 def fwd_splitkv(q, cu_seqlens_q, k, v, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale=None,
                 causal=False, block_table=None, page_size=0, num_splits=None, out=None, lse=None,
                 workspace=None, stream=None):
@@ -482,8 +513,8 @@ def fwd_splitkv(q, cu_seqlens_q, k, v, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
     B, max_pages = _check_varlen(q, cu_seqlens_q, k, v, cu_seqlens_k, block_table, page_size, out, lse)
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     if num_splits is None:
-        n_work = H * (-(-int(total_q) // 128) + B)
-        num_splits = splitkv_num_splits(n_work, max_seqlen_k)
+        num_splits = auto_num_splits(B, H, D, total_q, max_seqlen_q, max_seqlen_k,
+                                     page_size if block_table is not None else 0)
     num_splits = int(num_splits)
     if out is None:
         out = torch.empty_like(q)

@@ -28,6 +28,7 @@ hipError_t launch_splitkv_merge(const MergeArgs& a, int D, int dtype, hipStream_
 hipError_t launch_tail_merge(const TailMergeArgs& a, int D, int dtype, hipStream_t s);
 hipError_t launch_fwd_fp8(const Fp8Args& a, int D, bool causal, hipStream_t s);
 hipError_t launch_fwd_fp8_pow2(const Fp8Args& a, int D, bool causal, hipStream_t s);
+hipError_t launch_decode(const FwdArgs& a, int dtype, hipStream_t s);
 hipError_t launch_int8_quantize(const QuantArgs& a, int D, hipStream_t s);
 hipError_t launch_fwd_int8(const Fp8Args& a, int D, bool causal, hipStream_t s);
 size_t noalloc_scratch_bytes();
@@ -126,6 +127,10 @@ constexpr int kBR = 128;  // query rows per workgroup of every forward kernel
 // K/V tiles are read through 32-bit buffer offsets: 64 rows of a tile must fit in 2^31 bytes
 constexpr int64_t kMaxSeqStride = int64_t(1) << 24;
 constexpr int kMaxSplits = 256;  // key splits per sequence in attn_fwd_splitkv
+// Fewest work items (waves) of the streaming decode kernel: with fewer, its
+// one tile in flight per wave leaves HBM idle and the tiled kernel is faster
+// (measured: 144 and 336 waves ran at 0.5x and 0.85x of it, 512 at 1.1x).
+constexpr int64_t kDecodeMinWaves = 512;
 
 // Compute units of the current device (0 if the query fails), looked up once
 // per device.
@@ -351,6 +356,25 @@ attn_status_t attn_fwd_bias(int dtype, const void* q, const int64_t q_strides[3]
 
 namespace {
 
+// One query row per sequence at head dim 128, packed or in pages of at least
+// 64 tokens, and at least kDecodeMinWaves (sequence, key range, head) items:
+// the streaming decode kernel takes it (a causal mask keeps every key of a
+// one-row sequence, so it needs no mask).
+bool use_decode(const attn::FwdArgs& a, int D, int mode, int n_split) {
+  return a.Sq == 1 && D == 128 && (mode == attn::kVarlen || (mode == attn::kPaged && a.page_shift >= 6)) &&
+         (int64_t)a.B * a.H * n_split >= kDecodeMinWaves;
+}
+
+// The whole-sequence (one key range) forward of a packed or paged batch.
+hipError_t dispatch_varlen(attn::FwdArgs a, int D, int dtype, bool causal, int mode, hipStream_t s) {
+  if (use_decode(a, D, mode, 1)) {
+    a.n_split = 1;
+    a.split_tiles = (int)(((int64_t)a.Sk + 63) / 64);
+    return attn::launch_decode(a, dtype, s);
+  }
+  return dispatch_fwd16(a, D, dtype, causal, mode, s);
+}
+
 // Validation and argument set-up shared by attn_fwd_varlen and
 // attn_fwd_splitkv.  *empty is set when there is nothing to compute.
 attn_status_t varlen_args(int dtype, const void* q, const int32_t* cu_seqlens_q, const void* k, const void* v,
@@ -482,7 +506,7 @@ attn_status_t attn_fwd_varlen(int dtype, const void* q, const int32_t* cu_seqlen
                                                     (hipStream_t)stream);
       ci != ATTN_OK)
     return ci;
-  return hip_status(dispatch_fwd16(a, D, dtype, causal != 0, mode, (hipStream_t)stream), "attn_fwd_varlen launch");
+  return hip_status(dispatch_varlen(a, D, dtype, causal != 0, mode, (hipStream_t)stream), "attn_fwd_varlen launch");
 }
 
 }  // extern "C"
@@ -501,7 +525,8 @@ attn_status_t splitkv_launch(attn::FwdArgs a, int mode, int dtype, int D, int ca
   a.split_tiles = (tiles + num_splits - 1) / num_splits;
   a.part_o = part;
   a.part_lse = a.part_o + (size_t)num_splits * total_q * H * D;
-  hipError_t e = dispatch_fwd16(a, D, dtype, causal != 0, mode, stream);
+  hipError_t e = use_decode(a, D, mode, num_splits) ? attn::launch_decode(a, dtype, stream)
+                                                     : dispatch_fwd16(a, D, dtype, causal != 0, mode, stream);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s launch: %s", name, hipGetErrorString(e));
   attn::MergeArgs m{};
   m.part_o = a.part_o; m.part_lse = a.part_lse; m.o = a.o; m.lse = a.lse;
@@ -539,7 +564,7 @@ attn_status_t attn_fwd_splitkv(int dtype, const void* q, const int32_t* cu_seqle
       ci != ATTN_OK)
     return ci;
   if (num_splits == 1)
-    return hip_status(dispatch_fwd16(a, D, dtype, causal != 0, mode, (hipStream_t)stream), "attn_fwd_splitkv launch");
+    return hip_status(dispatch_varlen(a, D, dtype, causal != 0, mode, (hipStream_t)stream), "attn_fwd_splitkv launch");
   const size_t need = attn_fwd_splitkv_workspace_bytes(total_q, H, D, num_splits);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(ATTN_ERR_INVALID, "workspace of %zu bytes needed (got %zu)", need, workspace == nullptr ? 0 : workspace_bytes);
@@ -566,7 +591,7 @@ attn_status_t attn_fwd_splitkv_noalloc(int dtype, const void* q, const int32_t* 
       ci != ATTN_OK)
     return ci;
   if (num_splits == 1)
-    return hip_status(dispatch_fwd16(a, D, dtype, causal != 0, mode, (hipStream_t)stream),
+    return hip_status(dispatch_varlen(a, D, dtype, causal != 0, mode, (hipStream_t)stream),
                       "attn_fwd_splitkv_noalloc launch");
   const size_t need = attn_fwd_splitkv_workspace_bytes(total_q, H, D, num_splits);
   if (need > attn::noalloc_scratch_bytes())

@@ -1,0 +1,197 @@
+// Decoding forward ("Fused attention kernel" page, section "Implementation
+// sketch": a row's running max and running sum over key blocks; the
+// FlashAttention-3 page's future-work note on LLM inference): one query row
+// per sequence against a long, optionally paged key cache, at head dim 128.
+//
+// With one query row the two products are matrix-vector products, so the
+// matrix cores have nothing to share and the work is bound by the bytes of K
+// and V.  What matters is how many of them are in flight: the tiled kernel
+// stages every K/V tile through a two-stage LDS ring, one tile ahead, which
+// caps the bytes in flight at about half the LDS of a CU.  Here every wave
+// owns a (sequence, key range, head) and streams its K/V tiles straight into
+// registers, a tile's V and the next tile's K in flight while it computes.
+//
+// Work items run with the head index fastest: the waves that run together
+// read the neighbouring 256-byte head slices of the same cache rows, so every
+// row is fetched from memory as a whole (head-slowest order left each row to
+// be read in 256-byte pieces at different times: 14-17 % slower).
+//
+// Per 64-key tile and wave:
+//  * K: lane j loads the 256-byte row of key j (16 x 16-byte buffer loads);
+//    its score is 64 dot2 products (bf16 or fp16 pairs, fp32 accumulation,
+//    four independent chains) against the query's 64 pairs, held in scalar
+//    registers;
+//  * the next tile's K loads are issued as soon as the scores are formed, so
+//    they are in flight during the softmax and the P V product;
+//  * online softmax across the lanes: the tile's max over the wave, the
+//    running max m (in base-2 units of scale * q.k), p = 2^(x - m), the row
+//    sum in fp32 (a per-lane share, summed over the wave at the end);
+//  * V: each of the 64 key rows is one coalesced 256-byte load, lane l taking
+//    head-dim columns 2l and 2l+1; a byte permute pairs two keys' values of
+//    one column, and a dot2 against the two keys' probabilities (rounded to
+//    the input type, as for the matrix-core product of the tiled kernel,
+//    broadcast from the lanes that computed them) accumulates the output.
+// Every buffer resource ends at the last key of the tile that belongs to the
+// range (and is empty past the range), so rows past the sequence (or past a
+// page's used slots) read as zeros and never reach the output.
+//
+// With several key ranges each (range, row, head) writes the split-key
+// path's partial result: its normalised fp32 output and natural-log
+// logsumexp (0 and -inf for an empty range), which splitkv_merge_kernel
+// combines.  With one range it writes the output in the input type and the
+// logsumexp directly.
+#include "common.hpp"
+
+namespace attn {
+
+// buffer_load_dword into a register (zero past the resource's range)
+__device__ int raw_buffer_load_b32(i32x4 rsrc, int voffset, int soffset, int aux) __asm("llvm.amdgcn.raw.buffer.load.i32");
+
+template <int DT>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  if constexpr (DT == kBF16) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+  } else {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+  }
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int s = 1; s < 32; s <<= 1) x = max2f(x, __shfl_xor(x, s));
+  return halfwave_max(x);
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int s = 1; s < 32; s <<= 1) x += __shfl_xor(x, s);
+  return halfwave_sum(x);
+}
+
+// FwdArgs of the packed or paged varlen forward: every sequence with at most
+// one query row, head dim 128, paged caches with pages of at least 64 tokens
+// (a 64-key tile never straddles a page); n_split >= 1 key ranges of
+// split_tiles tiles (part_o / part_lse when n_split > 1).
+template <int DT>
+__global__ void __launch_bounds__(256) decode_kernel(FwdArgs a) {
+  constexpr int D = 128, BC = 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+  if (item >= (int64_t)a.B * a.H * a.n_split) return;  // (no barriers below)
+  const int h = (int)(item % a.H);
+  const int64_t bs = item / a.H;
+  const int split = (int)(bs % a.n_split), b = (int)(bs / a.n_split);
+  const int row = a.cu_q[b];
+  if (a.cu_q[b + 1] - row <= 0) return;
+  const int kseq = a.cu_k[b], Lk = a.cu_k[b + 1] - kseq;
+  const int kbeg = split * a.split_tiles * BC;
+  const int kend = a.n_split == 1 ? Lk : min(Lk, kbeg + a.split_tiles * BC);
+
+  // the query's 64 pairs, in scalar registers (read through the constant
+  // address space: a uniform address the kernel never writes)
+  typedef const __attribute__((address_space(4))) uint32_t cu32;
+  cu32* qp = (cu32*)((const uint16_t*)a.q + ((int64_t)row * a.H + h) * D);
+  uint32_t qw[D / 2];
+#pragma unroll
+  for (int i = 0; i < D / 2; ++i) qw[i] = qp[i];
+
+  const uint32_t row_bytes = (uint32_t)a.H * D * 2;  // <= 2^25 (H * D <= 2^24, checked by the caller)
+  const bool paged = a.block_table != nullptr;
+  // element offset of key k0's (b, h) slice: a tile never straddles a page
+  auto tile_off = [&](int k0) -> int64_t {
+    int64_t base_row;
+    if (paged) {
+      const int page = a.block_table[(int64_t)b * a.max_pages + (k0 >> a.page_shift)];
+      base_row = ((int64_t)page << a.page_shift) + (k0 & ((1 << a.page_shift) - 1));
+    } else {
+      base_row = (int64_t)kseq + k0;
+    }
+    return (base_row * a.H + h) * D;
+  };
+  auto tile_bytes = [&](int k0) -> uint32_t { return (uint32_t)(min(BC, kend - k0) - 1) * row_bytes + D * 2; };
+  float m = -INFINITY;       // running max (uniform over the wave)
+  float l_lane = 0.f;        // this lane's share of the row sum
+  float o0 = 0.f, o1 = 0.f;  // head-dim columns 2 lane and 2 lane + 1
+  uint32_t kw[D / 2];  // K row of key `lane` of the current tile
+  if (kbeg < kend) {
+    const i32x4 krs = make_rsrc((const uint16_t*)a.k + tile_off(kbeg), tile_bytes(kbeg));
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+      const i32x4 x = raw_buffer_load_v4(krs, (int)(lane * row_bytes + 16 * c), 0, 0);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) kw[4 * c + w] = (uint32_t)x[w];
+    }
+  }
+  for (int k0 = kbeg; k0 < kend; k0 += BC) {
+    const int nvalid = min(BC, kend - k0);
+    const i32x4 vrs = make_rsrc((const uint16_t*)a.v + tile_off(k0), tile_bytes(k0));
+    uint32_t vw[BC];  // V column pair `lane` of every key of the tile
+#pragma unroll
+    for (int j = 0; j < BC; ++j) vw[j] = (uint32_t)raw_buffer_load_b32(vrs, (int)(j * row_bytes + 4 * lane), 0, 0);
+    // score of key `lane`
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < D / 2; ++i) acc[i & 3] = dot2<DT>(kw[i], qw[i], acc[i & 3]);
+    const float x = lane < nvalid ? ((acc[0] + acc[1]) + (acc[2] + acc[3])) * a.scale_log2 : -INFINITY;
+    // the next tile's K, into the registers the scores have just released
+    // (kept after the scores, and before the softmax, by the fences)
+    __builtin_amdgcn_sched_barrier(0);
+    const int k1 = k0 + BC;
+    int64_t off1 = 0;
+    uint32_t nb1 = 0;  // past the range: an empty resource, the loads return zeros
+    if (k1 < kend) {
+      off1 = tile_off(k1);
+      nb1 = tile_bytes(k1);
+    }
+    {
+      const i32x4 krs = make_rsrc((const uint16_t*)a.k + off1, nb1);
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) {
+        const i32x4 y = raw_buffer_load_v4(krs, (int)(lane * row_bytes + 16 * c), 0, 0);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) kw[4 * c + w] = (uint32_t)y[w];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const float m_new = max2f(m, wave_max(x));
+    const float m_safe = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_safe);
+    const float p = fast_exp2(x - m_safe);
+    l_lane = fmaf(l_lane, alpha, p);
+    m = m_new;
+    o0 *= alpha;
+    o1 *= alpha;
+    // probabilities of keys 2i, 2i+1 as one 16-bit pair, from lane 2i
+    const uint32_t pp = pack2<DT>(p, __shfl_xor(p, 1));
+#pragma unroll
+    for (int i = 0; i < BC / 2; ++i) {
+      const uint32_t pi = (uint32_t)__builtin_amdgcn_readlane((int)pp, 2 * i);
+      const uint32_t lo = __builtin_amdgcn_perm(vw[2 * i + 1], vw[2 * i], 0x05040100u);  // column 2 lane
+      const uint32_t hi = __builtin_amdgcn_perm(vw[2 * i + 1], vw[2 * i], 0x07060302u);  // column 2 lane + 1
+      o0 = dot2<DT>(lo, pi, o0);
+      o1 = dot2<DT>(hi, pi, o1);
+    }
+  }
+  const float l = wave_sum(l_lane);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float lse = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+  if (a.n_split == 1) {
+    uint16_t* o = (uint16_t*)a.o + (int64_t)row * a.o_ss + (int64_t)h * a.o_sh;
+    *(uint32_t*)(o + 2 * lane) = pack2<DT>(o0 * inv, o1 * inv);
+    if (lane == 0 && a.lse != nullptr) a.lse[(int64_t)h * a.total_q + row] = lse;
+  } else {
+    const int64_t prow = (int64_t)split * a.total_q + row;
+    *(f32x2*)(a.part_o + (prow * a.H + h) * D + 2 * lane) = f32x2{o0 * inv, o1 * inv};
+    if (lane == 0) a.part_lse[(int64_t)split * a.H * a.total_q + (int64_t)h * a.total_q + row] = lse;
+  }
+}
+
+hipError_t launch_decode(const FwdArgs& a, int dtype, hipStream_t s) {
+  const int64_t items = (int64_t)a.B * a.H * a.n_split;
+  const dim3 grid((unsigned)((items + 3) / 4)), block(256);
+  if (dtype == kBF16) hipLaunchKernelGGL(decode_kernel<kBF16>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(decode_kernel<kFP16>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace attn

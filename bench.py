@@ -376,8 +376,7 @@ def bench_decode(A, W, args):
     tab = torch.from_numpy(table).cuda()
     o = torch.empty_like(q)
     lse = torch.empty((H, B * Lq), dtype=torch.float32, device="cuda")
-    n_work = H * (-(-(B * Lq) // 128) + B)
-    splits = A.splitkv_num_splits(n_work, Lk)
+    splits = A.auto_num_splits(B, H, D, B * Lq, Lq, Lk, page)
     ws = torch.empty(A._lib.attn_fwd_splitkv_workspace_bytes(B * Lq, H, D, splits) // 4 + 4, dtype=torch.float32,
                      device="cuda")
     kv_bytes = 2 * B * Lk * H * D * 2

@@ -65,6 +65,15 @@ hipError_t launch_fp8_quantize_pow2(const QuantArgs&, int, hipStream_t) { ++g_la
 hipError_t launch_int8_quantize(const QuantArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_splitkv_merge(const MergeArgs&, int, int, hipStream_t) { ++g_launches; return hipSuccess; }
 }  // namespace attn
+static int g_decode = 0;
+namespace attn {
+hipError_t launch_decode(const FwdArgs& a, int, hipStream_t) {
+  ++g_launches;
+  ++g_decode;
+  g_fwd = a;
+  return hipSuccess;
+}
+}  // namespace attn
 static attn::TailMergeArgs g_tail;
 namespace attn {
 hipError_t launch_tail_merge(const TailMergeArgs& a, int, int, hipStream_t) {
@@ -233,6 +242,35 @@ int main() {
   expect("splitkv_ws_bytes", ws == size_t(4) * 5 * 4 * 129 * 4, 1);
   std::vector<float> work(ws / 4 + 4);
   expect("splitkv_ok", attn_fwd_splitkv(ATTN_BF16, p, cu, p, p, cu, nullptr, 0, 0, p, lse, 2, 4, 128, 5, 3, 3, sc, 0, 4, work.data(), ws, nullptr), ATTN_OK);
+  // one query row per sequence at head dim 128 with at least 512 (sequence,
+  // key range, head) items: the decode kernel (packed, or pages of >= 64
+  // tokens), then the merge; otherwise the tiled kernel
+  const size_t ws1 = attn_fwd_splitkv_workspace_bytes(2, 64, 128, 4);
+  std::vector<float> work1(ws1 / 4 + 4);
+  int d0 = g_decode;
+  n = g_launches;
+  expect("decode_ok", attn_fwd_splitkv(ATTN_BF16, p, cu, p, p, cu, nullptr, 0, 0, p, lse, 2, 64, 128, 2, 1, 3, sc, 1, 4, work1.data(), ws1, nullptr), ATTN_OK);
+  expect("decode_plan", g_decode - d0 == 1 && g_launches - n == 2 && g_fwd.n_split == 4 && g_fwd.split_tiles == 1, 1);
+  d0 = g_decode;
+  expect("decode_few_items", attn_fwd_splitkv(ATTN_BF16, p, cu, p, p, cu, nullptr, 0, 0, p, lse, 2, 4, 128, 2, 1, 3, sc, 1, 4, work1.data(), ws1, nullptr), ATTN_OK);
+  expect("decode_few_items_plan", g_decode - d0 == 0 && g_fwd_mode == attn::kVarlen, 1);
+  expect("decode_paged64", attn_fwd_splitkv(ATTN_BF16, p, cu, p, p, cu, table, 1, 64, p, lse, 2, 64, 128, 2, 1, 3, sc, 0, 4, work1.data(), ws1, nullptr), ATTN_OK);
+  expect("decode_paged64_plan", g_decode - d0, 1);
+  d0 = g_decode;
+  expect("decode_paged16", attn_fwd_splitkv(ATTN_BF16, p, cu, p, p, cu, table, 2, 16, p, lse, 2, 64, 128, 2, 1, 3, sc, 0, 4, work1.data(), ws1, nullptr), ATTN_OK);
+  expect("decode_paged16_plan", g_decode - d0 == 0 && g_fwd_mode == attn::kPaged, 1);
+  expect("decode_d64", attn_fwd_splitkv(ATTN_BF16, p, cu, p, p, cu, nullptr, 0, 0, p, lse, 2, 64, 64, 2, 1, 3, sc, 0, 4, work1.data(), ws1, nullptr), ATTN_OK);
+  expect("decode_d64_plan", g_decode - d0 == 0 && g_fwd_mode == attn::kVarlen, 1);
+  // one key range: the decode kernel writes the output itself (no merge)
+  n = g_launches;
+  expect("decode_whole_varlen", attn_fwd_varlen(ATTN_BF16, p, cu, p, p, cu, nullptr, 0, 0, p, lse, 2, 256, 128, 2, 1, 3, sc, 1, nullptr), ATTN_OK);
+  expect("decode_whole_varlen_plan", g_decode - d0 == 1 && g_launches - n == 1 && g_fwd.n_split == 1, 1);
+  d0 = g_decode;
+  expect("decode_whole_splitkv1", attn_fwd_splitkv(ATTN_BF16, p, cu, p, p, cu, nullptr, 0, 0, p, lse, 2, 256, 128, 2, 1, 3, sc, 0, 1, nullptr, 0, nullptr), ATTN_OK);
+  expect("decode_whole_splitkv1_plan", g_decode - d0 == 1 && g_fwd.n_split == 1, 1);
+  d0 = g_decode;
+  expect("decode_whole_few", attn_fwd_varlen(ATTN_BF16, p, cu, p, p, cu, nullptr, 0, 0, p, lse, 2, 64, 128, 2, 1, 3, sc, 0, nullptr), ATTN_OK);
+  expect("decode_whole_few_plan", g_decode - d0 == 0 && g_fwd_mode == attn::kVarlen, 1);
   expect("splitkv_small_ws", attn_fwd_splitkv(ATTN_BF16, p, cu, p, p, cu, nullptr, 0, 0, p, lse, 2, 4, 128, 5, 3, 3, sc, 0, 4, work.data(), ws - 4, nullptr), ATTN_ERR_INVALID);
   expect("splitkv_splits_0", attn_fwd_splitkv(ATTN_BF16, p, cu, p, p, cu, nullptr, 0, 0, p, lse, 2, 4, 128, 5, 3, 3, sc, 0, 0, work.data(), ws, nullptr), ATTN_ERR_INVALID);
   expect("splitkv_sk_int_max", attn_fwd_splitkv(ATTN_BF16, p, cu, p, p, cu, nullptr, 0, 0, p, lse, 2, 4, 128, 5, 3, INT_MAX, sc, 0, 4, work.data(), ws, nullptr), ATTN_OK);

@@ -273,6 +273,37 @@ def test_bwd_validation(lib):
     assert f(Sq=0, Sk=0) == OK
 
 
+def test_decode_num_splits():
+    import random
+    import attention_attn_fwd_10_amd as A
+    assert A.decode_num_splits(128, 32768) == 8       # 4 sequences x 32 heads: 1024 waves
+    assert A.decode_num_splits(512, 8192) == 2
+    assert A.decode_num_splits(32, 131072) == 32
+    assert A.decode_num_splits(48, 5000) == 20        # 79 tiles: ranges of 4 tiles, none empty
+    assert A.decode_num_splits(4096, 1000) == 1       # enough waves without splitting
+    assert A.decode_num_splits(1, 64) == 1
+    rng = random.Random(5)
+    for _ in range(500):
+        nbh, lk = rng.randint(1, 5000), rng.randint(0, 300000)
+        s = A.decode_num_splits(nbh, lk)
+        tiles = max(1, (lk + 63) // 64)
+        per = -(-tiles // s)
+        assert 1 <= s <= 256 and (s - 1) * per < tiles   # every range holds keys
+        assert s == 1 or per >= 2
+
+
+def test_auto_num_splits():
+    import attention_attn_fwd_10_amd as A
+    # decode kernel's rule where the library takes it, the tiled rule elsewhere
+    assert A.auto_num_splits(4, 32, 128, 4, 1, 32768, 64) == 8
+    assert A.auto_num_splits(4, 32, 128, 4, 1, 32768, 0) == 8
+    assert A.auto_num_splits(4, 32, 128, 4, 1, 32768, 16) == A.splitkv_num_splits(32 * 5, 32768)
+    assert A.auto_num_splits(4, 32, 64, 4, 1, 32768, 0) == A.splitkv_num_splits(32 * 5, 32768)
+    assert A.auto_num_splits(4, 32, 128, 8, 2, 32768, 0) == A.splitkv_num_splits(32 * 5, 32768)
+    # too few waves for the decode kernel even split: the tiled rule
+    assert A.auto_num_splits(1, 8, 128, 1, 1, 1000, 0) == A.splitkv_num_splits(8 * 2, 1000)
+
+
 def test_splitkv_num_splits_bounds():
     """The split-count rule: between 1 and 16 splits, at least 4 tiles of 64 keys
     in every split the kernel forms (ceil(tiles / splits) each), and no fewer

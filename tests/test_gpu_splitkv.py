@@ -95,3 +95,69 @@ def test_matches_unsplit_kernel(lib):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(o1, to_host(o2))
     np.testing.assert_array_equal(l1, l2.cpu().numpy().astype(np.float64))
+
+
+# One query row per sequence at head dim 128 with at least 512 (sequence, key
+# range, head) items is the streaming decode kernel's case (packed caches, and
+# paged caches with pages of at least 64 tokens); fewer items take the tiled
+# kernel.
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("splits", [2, 7, 64])
+def test_one_row_decode_packed(lib, dtype, causal, splits):
+    # key counts: several tiles with a ragged tail, one key, none, one short of
+    # a tile, exactly a tile, and a sequence without a query row; 7 x 40 heads
+    lens_q, lens_k = [1, 1, 1, 1, 1, 0, 1], [1000, 1, 0, 63, 64, 50, 4097]
+    q, k, v, cu_q, cu_k = _pack(lens_q, lens_k, 40, 128, seed=950)
+    if dtype == "fp16":
+        q, k, v = (W.f16_round(x).astype(np.float32) for x in (q, k, v))
+    o, lse = _run(lib, q, k, v, cu_q, cu_k, lens_q, lens_k, causal, splits, dtype=dtype)
+    o_ref, lse_ref = _reference(q, k, v, cu_q, cu_k, lens_q, lens_k, causal)
+    assert_close16(o, o_ref, lse, lse_ref, f"one-row decode {dtype} causal={causal} splits={splits}", dtype=dtype)
+
+
+@pytest.mark.parametrize("page", [64, 256, 16])
+def test_one_row_decode_paged_poisoned(lib, page):
+    # pages at shuffled physical slots, NaN in every slot no sequence owns
+    # (16-token pages take the tiled kernel, row by row through the table)
+    lens_q, lens_k = [1, 1, 1, 1], [5000, 130, 64, 2500]
+    q, k, v, cu_q, cu_k = _pack(lens_q, lens_k, 16, 128, seed=960 + page)
+    kp, vp, table = _paginate(k, v, cu_k, lens_k, page, seed=961)
+    o, lse = _run(lib, q, kp, vp, cu_q, cu_k, lens_q, lens_k, True, 9, table=table, page=page)
+    o_ref, lse_ref = _reference(q, k, v, cu_q, cu_k, lens_q, lens_k, True)
+    assert_close16(o, o_ref, lse, lse_ref, f"one-row paged decode page={page}")
+
+
+def test_one_row_decode_large_scores(lib):
+    # scores far from zero: the running max moves across tiles and splits
+    lens_q, lens_k = [1, 1], [3000, 777]
+    q, k, v, cu_q, cu_k = _pack(lens_q, lens_k, 64, 128, seed=970)
+    q = W.normal_bf16(np.random.default_rng(971), q.shape) * 8.0
+    o, lse = _run(lib, q, k, v, cu_q, cu_k, lens_q, lens_k, False, 5)
+    o_ref, lse_ref = _reference(q, k, v, cu_q, cu_k, lens_q, lens_k, False)
+    assert_close16(o, o_ref, lse, lse_ref, "one-row decode, large scores")
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_one_row_whole_sequence(lib, paged):
+    # one key range (attn_fwd_varlen, and attn_fwd_splitkv with one split): the
+    # decode kernel writes the output and the logsumexp itself; 8 x 64 heads
+    import torch
+    lens_q, lens_k = [1, 1, 1, 0, 1, 1, 1, 1], [2049, 0, 1, 70, 64, 700, 65, 128]
+    q, k, v, cu_q, cu_k = _pack(lens_q, lens_k, 64, 128, seed=980)
+    table = None
+    kk, vv = k, v
+    if paged:
+        kk, vv, table = _paginate(k, v, cu_k, lens_k, 128, seed=981)
+    tq, tk, tv = to_dev(q), to_dev(kk), to_dev(vv)
+    tab = None if table is None else _t32(table)
+    o1, l1 = lib.fwd_varlen(tq, _t32(cu_q), tk, tv, _t32(cu_k), 1, max(lens_k), causal=True, block_table=tab,
+                            page_size=128 if paged else 0)
+    o2, l2 = lib.fwd_splitkv(tq, _t32(cu_q), tk, tv, _t32(cu_k), 1, max(lens_k), causal=True, block_table=tab,
+                             page_size=128 if paged else 0, num_splits=1)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = _reference(q, k, v, cu_q, cu_k, lens_q, lens_k, True)
+    assert_close16(to_host(o1), o_ref, l1.cpu().numpy().astype(np.float64), lse_ref, f"one-row whole paged={paged}")
+    np.testing.assert_array_equal(to_host(o1), to_host(o2))
+    np.testing.assert_array_equal(l1.cpu().numpy(), l2.cpu().numpy())
