@@ -28,7 +28,7 @@ hipError_t launch_splitkv_merge(const MergeArgs& a, int D, int dtype, hipStream_
 hipError_t launch_tail_merge(const TailMergeArgs& a, int D, int dtype, hipStream_t s);
 hipError_t launch_fwd_fp8(const Fp8Args& a, int D, bool causal, hipStream_t s);
 hipError_t launch_fwd_fp8_pow2(const Fp8Args& a, int D, bool causal, hipStream_t s);
-hipError_t launch_decode(const FwdArgs& a, int dtype, hipStream_t s);
+hipError_t launch_decode(const FwdArgs& a, int D, int dtype, hipStream_t s);
 hipError_t launch_int8_quantize(const QuantArgs& a, int D, hipStream_t s);
 hipError_t launch_fwd_int8(const Fp8Args& a, int D, bool causal, hipStream_t s);
 size_t noalloc_scratch_bytes();
@@ -356,12 +356,12 @@ attn_status_t attn_fwd_bias(int dtype, const void* q, const int64_t q_strides[3]
 
 namespace {
 
-// One query row per sequence at head dim 128, packed or in pages of at least
-// 64 tokens, and at least kDecodeMinWaves (sequence, key range, head) items:
+// One query row per sequence at head dim 64 or 128, packed or in pages of at
+// least 64 tokens, and at least kDecodeMinWaves (sequence, key range, head) items:
 // the streaming decode kernel takes it (a causal mask keeps every key of a
 // one-row sequence, so it needs no mask).
 bool use_decode(const attn::FwdArgs& a, int D, int mode, int n_split) {
-  return a.Sq == 1 && D == 128 && (mode == attn::kVarlen || (mode == attn::kPaged && a.page_shift >= 6)) &&
+  return a.Sq == 1 && (D == 64 || D == 128) && (mode == attn::kVarlen || (mode == attn::kPaged && a.page_shift >= 6)) &&
          (int64_t)a.B * a.H * n_split >= kDecodeMinWaves;
 }
 
@@ -370,7 +370,7 @@ hipError_t dispatch_varlen(attn::FwdArgs a, int D, int dtype, bool causal, int m
   if (use_decode(a, D, mode, 1)) {
     a.n_split = 1;
     a.split_tiles = (int)(((int64_t)a.Sk + 63) / 64);
-    return attn::launch_decode(a, dtype, s);
+    return attn::launch_decode(a, D, dtype, s);
   }
   return dispatch_fwd16(a, D, dtype, causal, mode, s);
 }
@@ -525,7 +525,7 @@ attn_status_t splitkv_launch(attn::FwdArgs a, int mode, int dtype, int D, int ca
   a.split_tiles = (tiles + num_splits - 1) / num_splits;
   a.part_o = part;
   a.part_lse = a.part_o + (size_t)num_splits * total_q * H * D;
-  hipError_t e = use_decode(a, D, mode, num_splits) ? attn::launch_decode(a, dtype, stream)
+  hipError_t e = use_decode(a, D, mode, num_splits) ? attn::launch_decode(a, D, dtype, stream)
                                                      : dispatch_fwd16(a, D, dtype, causal != 0, mode, stream);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s launch: %s", name, hipGetErrorString(e));
   attn::MergeArgs m{};

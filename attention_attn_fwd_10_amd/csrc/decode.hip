@@ -1,7 +1,8 @@
 // Decoding forward ("Fused attention kernel" page, section "Implementation
 // sketch": a row's running max and running sum over key blocks; the
 // FlashAttention-3 page's future-work note on LLM inference): one query row
-// per sequence against a long, optionally paged key cache, at head dim 128.
+// per sequence against a long, optionally paged key cache, at head dim 64 or
+// 128.
 //
 // With one query row the two products are matrix-vector products, so the
 // matrix cores have nothing to share and the work is bound by the bytes of K
@@ -17,17 +18,19 @@
 // be read in 256-byte pieces at different times: 14-17 % slower).
 //
 // Per 64-key tile and wave:
-//  * K: lane j loads the 256-byte row of key j (16 x 16-byte buffer loads);
-//    its score is 64 dot2 products (bf16 or fp16 pairs, fp32 accumulation,
-//    four independent chains) against the query's 64 pairs, held in scalar
+//  * K: lane j loads the 2D-byte row of key j (D/8 16-byte buffer loads);
+//    its score is D/2 dot2 products (bf16 or fp16 pairs, fp32 accumulation,
+//    four independent chains) against the query's D/2 pairs, held in scalar
 //    registers;
 //  * the next tile's K loads are issued as soon as the scores are formed, so
 //    they are in flight during the softmax and the P V product;
 //  * online softmax across the lanes: the tile's max over the wave, the
 //    running max m (in base-2 units of scale * q.k), p = 2^(x - m), the row
 //    sum in fp32 (a per-lane share, summed over the wave at the end);
-//  * V: each of the 64 key rows is one coalesced 256-byte load, lane l taking
-//    head-dim columns 2l and 2l+1; a byte permute pairs two keys' values of
+//  * V: each of the 64 key rows is one coalesced 2D-byte load, lane l taking
+//    head-dim columns 2l and 2l+1 (at D = 64 lanes 32..63 repeat the addresses
+//    of lanes 0..31, which adds no memory traffic, and their results are
+//    dropped); a byte permute pairs two keys' values of
 //    one column, and a dot2 against the two keys' probabilities (rounded to
 //    the input type, as for the matrix-core product of the tiled kernel,
 //    broadcast from the lanes that computed them) accumulates the output.
@@ -68,12 +71,14 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // FwdArgs of the packed or paged varlen forward: every sequence with at most
-// one query row, head dim 128, paged caches with pages of at least 64 tokens
+// one query row, head dim D, paged caches with pages of at least 64 tokens
 // (a 64-key tile never straddles a page); n_split >= 1 key ranges of
 // split_tiles tiles (part_o / part_lse when n_split > 1).
-template <int DT>
+template <int DT, int D>
 __global__ void __launch_bounds__(256) decode_kernel(FwdArgs a) {
-  constexpr int D = 128, BC = 64;
+  static_assert(D == 64 || D == 128, "head dims of the decode kernel");
+  constexpr int BC = 64;
+  constexpr int NCOL = D / 2;  // lanes that own a head-dim column pair
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t item = (int64_t)blockIdx.x * 4 + wave;
@@ -111,7 +116,8 @@ __global__ void __launch_bounds__(256) decode_kernel(FwdArgs a) {
   auto tile_bytes = [&](int k0) -> uint32_t { return (uint32_t)(min(BC, kend - k0) - 1) * row_bytes + D * 2; };
   float m = -INFINITY;       // running max (uniform over the wave)
   float l_lane = 0.f;        // this lane's share of the row sum
-  float o0 = 0.f, o1 = 0.f;  // head-dim columns 2 lane and 2 lane + 1
+  float o0 = 0.f, o1 = 0.f;  // head-dim columns 2 col and 2 col + 1
+  const int col = lane % NCOL;
   uint32_t kw[D / 2];  // K row of key `lane` of the current tile
   if (kbeg < kend) {
     const i32x4 krs = make_rsrc((const uint16_t*)a.k + tile_off(kbeg), tile_bytes(kbeg));
@@ -127,7 +133,7 @@ __global__ void __launch_bounds__(256) decode_kernel(FwdArgs a) {
     const i32x4 vrs = make_rsrc((const uint16_t*)a.v + tile_off(k0), tile_bytes(k0));
     uint32_t vw[BC];  // V column pair `lane` of every key of the tile
 #pragma unroll
-    for (int j = 0; j < BC; ++j) vw[j] = (uint32_t)raw_buffer_load_b32(vrs, (int)(j * row_bytes + 4 * lane), 0, 0);
+    for (int j = 0; j < BC; ++j) vw[j] = (uint32_t)raw_buffer_load_b32(vrs, (int)(j * row_bytes + 4 * col), 0, 0);
     // score of key `lane`
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -166,8 +172,8 @@ __global__ void __launch_bounds__(256) decode_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < BC / 2; ++i) {
       const uint32_t pi = (uint32_t)__builtin_amdgcn_readlane((int)pp, 2 * i);
-      const uint32_t lo = __builtin_amdgcn_perm(vw[2 * i + 1], vw[2 * i], 0x05040100u);  // column 2 lane
-      const uint32_t hi = __builtin_amdgcn_perm(vw[2 * i + 1], vw[2 * i], 0x07060302u);  // column 2 lane + 1
+      const uint32_t lo = __builtin_amdgcn_perm(vw[2 * i + 1], vw[2 * i], 0x05040100u);  // column 2 col
+      const uint32_t hi = __builtin_amdgcn_perm(vw[2 * i + 1], vw[2 * i], 0x07060302u);  // column 2 col + 1
       o0 = dot2<DT>(lo, pi, o0);
       o1 = dot2<DT>(hi, pi, o1);
     }
@@ -177,20 +183,27 @@ __global__ void __launch_bounds__(256) decode_kernel(FwdArgs a) {
   const float lse = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
   if (a.n_split == 1) {
     uint16_t* o = (uint16_t*)a.o + (int64_t)row * a.o_ss + (int64_t)h * a.o_sh;
-    *(uint32_t*)(o + 2 * lane) = pack2<DT>(o0 * inv, o1 * inv);
+    if (lane < NCOL) *(uint32_t*)(o + 2 * lane) = pack2<DT>(o0 * inv, o1 * inv);
     if (lane == 0 && a.lse != nullptr) a.lse[(int64_t)h * a.total_q + row] = lse;
   } else {
     const int64_t prow = (int64_t)split * a.total_q + row;
-    *(f32x2*)(a.part_o + (prow * a.H + h) * D + 2 * lane) = f32x2{o0 * inv, o1 * inv};
+    if (lane < NCOL) *(f32x2*)(a.part_o + (prow * a.H + h) * D + 2 * lane) = f32x2{o0 * inv, o1 * inv};
     if (lane == 0) a.part_lse[(int64_t)split * a.H * a.total_q + (int64_t)h * a.total_q + row] = lse;
   }
 }
 
-hipError_t launch_decode(const FwdArgs& a, int dtype, hipStream_t s) {
+hipError_t launch_decode(const FwdArgs& a, int D, int dtype, hipStream_t s) {
   const int64_t items = (int64_t)a.B * a.H * a.n_split;
   const dim3 grid((unsigned)((items + 3) / 4)), block(256);
-  if (dtype == kBF16) hipLaunchKernelGGL(decode_kernel<kBF16>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(decode_kernel<kFP16>, grid, block, 0, s, a);
+  if (D == 64) {
+    if (dtype == kBF16) hipLaunchKernelGGL((decode_kernel<kBF16, 64>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<kFP16, 64>), grid, block, 0, s, a);
+  } else if (D == 128) {
+    if (dtype == kBF16) hipLaunchKernelGGL((decode_kernel<kBF16, 128>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<kFP16, 128>), grid, block, 0, s, a);
+  } else {
+    return hipErrorNotSupported;
+  }
   return hipGetLastError();
 }
 

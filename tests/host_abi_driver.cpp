@@ -67,7 +67,7 @@ hipError_t launch_splitkv_merge(const MergeArgs&, int, int, hipStream_t) { ++g_l
 }  // namespace attn
 static int g_decode = 0;
 namespace attn {
-hipError_t launch_decode(const FwdArgs& a, int, hipStream_t) {
+hipError_t launch_decode(const FwdArgs& a, int, int, hipStream_t) {
   ++g_launches;
   ++g_decode;
   g_fwd = a;
@@ -246,7 +246,7 @@ int main() {
   // key range, head) items: the decode kernel (packed, or pages of >= 64
   // tokens), then the merge; otherwise the tiled kernel
   const size_t ws1 = attn_fwd_splitkv_workspace_bytes(2, 64, 128, 4);
-  std::vector<float> work1(ws1 / 4 + 4);
+  std::vector<float> work1(attn_fwd_splitkv_workspace_bytes(2, 64, 256, 4) / 4 + 4);  // (d256 is the largest)
   int d0 = g_decode;
   n = g_launches;
   expect("decode_ok", attn_fwd_splitkv(ATTN_BF16, p, cu, p, p, cu, nullptr, 0, 0, p, lse, 2, 64, 128, 2, 1, 3, sc, 1, 4, work1.data(), ws1, nullptr), ATTN_OK);
@@ -260,7 +260,10 @@ int main() {
   expect("decode_paged16", attn_fwd_splitkv(ATTN_BF16, p, cu, p, p, cu, table, 2, 16, p, lse, 2, 64, 128, 2, 1, 3, sc, 0, 4, work1.data(), ws1, nullptr), ATTN_OK);
   expect("decode_paged16_plan", g_decode - d0 == 0 && g_fwd_mode == attn::kPaged, 1);
   expect("decode_d64", attn_fwd_splitkv(ATTN_BF16, p, cu, p, p, cu, nullptr, 0, 0, p, lse, 2, 64, 64, 2, 1, 3, sc, 0, 4, work1.data(), ws1, nullptr), ATTN_OK);
-  expect("decode_d64_plan", g_decode - d0 == 0 && g_fwd_mode == attn::kVarlen, 1);
+  expect("decode_d64_plan", g_decode - d0, 1);
+  d0 = g_decode;
+  expect("decode_d256", attn_fwd_splitkv(ATTN_BF16, p, cu, p, p, cu, nullptr, 0, 0, p, lse, 2, 64, 256, 2, 1, 3, sc, 0, 4, work1.data(), attn_fwd_splitkv_workspace_bytes(2, 64, 256, 4), nullptr), ATTN_OK);
+  expect("decode_d256_plan", g_decode - d0 == 0 && g_fwd_mode == attn::kVarlen, 1);
   // one key range: the decode kernel writes the output itself (no merge)
   n = g_launches;
   expect("decode_whole_varlen", attn_fwd_varlen(ATTN_BF16, p, cu, p, p, cu, nullptr, 0, 0, p, lse, 2, 256, 128, 2, 1, 3, sc, 1, nullptr), ATTN_OK);

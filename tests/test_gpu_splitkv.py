@@ -97,36 +97,38 @@ def test_matches_unsplit_kernel(lib):
     np.testing.assert_array_equal(l1, l2.cpu().numpy().astype(np.float64))
 
 
-# One query row per sequence at head dim 128 with at least 512 (sequence, key
-# range, head) items is the streaming decode kernel's case (packed caches, and
+# One query row per sequence at head dim 64 or 128 with at least 512 (sequence,
+# key range, head) items is the streaming decode kernel's case (packed caches, and
 # paged caches with pages of at least 64 tokens); fewer items take the tiled
 # kernel.
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("splits", [2, 7, 64])
-def test_one_row_decode_packed(lib, dtype, causal, splits):
+def test_one_row_decode_packed(lib, d, dtype, causal, splits):
     # key counts: several tiles with a ragged tail, one key, none, one short of
     # a tile, exactly a tile, and a sequence without a query row; 7 x 40 heads
     lens_q, lens_k = [1, 1, 1, 1, 1, 0, 1], [1000, 1, 0, 63, 64, 50, 4097]
-    q, k, v, cu_q, cu_k = _pack(lens_q, lens_k, 40, 128, seed=950)
+    q, k, v, cu_q, cu_k = _pack(lens_q, lens_k, 40, d, seed=950 + d)
     if dtype == "fp16":
         q, k, v = (W.f16_round(x).astype(np.float32) for x in (q, k, v))
     o, lse = _run(lib, q, k, v, cu_q, cu_k, lens_q, lens_k, causal, splits, dtype=dtype)
     o_ref, lse_ref = _reference(q, k, v, cu_q, cu_k, lens_q, lens_k, causal)
-    assert_close16(o, o_ref, lse, lse_ref, f"one-row decode {dtype} causal={causal} splits={splits}", dtype=dtype)
+    assert_close16(o, o_ref, lse, lse_ref, f"one-row decode d{d} {dtype} causal={causal} splits={splits}", dtype=dtype)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("page", [64, 256, 16])
-def test_one_row_decode_paged_poisoned(lib, page):
+def test_one_row_decode_paged_poisoned(lib, d, page):
     # pages at shuffled physical slots, NaN in every slot no sequence owns
     # (16-token pages take the tiled kernel, row by row through the table)
     lens_q, lens_k = [1, 1, 1, 1], [5000, 130, 64, 2500]
-    q, k, v, cu_q, cu_k = _pack(lens_q, lens_k, 16, 128, seed=960 + page)
+    q, k, v, cu_q, cu_k = _pack(lens_q, lens_k, 16, d, seed=960 + page + d)
     kp, vp, table = _paginate(k, v, cu_k, lens_k, page, seed=961)
     o, lse = _run(lib, q, kp, vp, cu_q, cu_k, lens_q, lens_k, True, 9, table=table, page=page)
     o_ref, lse_ref = _reference(q, k, v, cu_q, cu_k, lens_q, lens_k, True)
-    assert_close16(o, o_ref, lse, lse_ref, f"one-row paged decode page={page}")
+    assert_close16(o, o_ref, lse, lse_ref, f"one-row paged decode d{d} page={page}")
 
 
 def test_one_row_decode_large_scores(lib):
@@ -139,13 +141,14 @@ def test_one_row_decode_large_scores(lib):
     assert_close16(o, o_ref, lse, lse_ref, "one-row decode, large scores")
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("paged", [False, True])
-def test_one_row_whole_sequence(lib, paged):
+def test_one_row_whole_sequence(lib, d, paged):
     # one key range (attn_fwd_varlen, and attn_fwd_splitkv with one split): the
     # decode kernel writes the output and the logsumexp itself; 8 x 64 heads
     import torch
     lens_q, lens_k = [1, 1, 1, 0, 1, 1, 1, 1], [2049, 0, 1, 70, 64, 700, 65, 128]
-    q, k, v, cu_q, cu_k = _pack(lens_q, lens_k, 64, 128, seed=980)
+    q, k, v, cu_q, cu_k = _pack(lens_q, lens_k, 64, d, seed=980 + d)
     table = None
     kk, vv = k, v
     if paged:
