@@ -469,7 +469,7 @@ def splitkv_num_splits(n_work, max_seqlen_k, target=2048, min_tiles=4, max_split
 
 
 def decode_num_splits(n_seq_heads, max_seqlen_k, target=1024, min_tiles=2, max_splits=256):
-    """A split count for one query row per sequence at head dim 64 or 128 (the
+    """A split count for one query row per sequence (the
     streaming decode kernel, one wave per sequence, key range and head): about
     `target` waves (n_seq_heads x splits; one per SIMD of the chip), at least
     `min_tiles` 64-key tiles per range and no empty range.  Measured on
@@ -488,10 +488,10 @@ DECODE_MIN_WAVES = 512  # fewest (sequence, key range, head) items the library r
 
 def auto_num_splits(B, H, D, total_q, max_seqlen_q, max_seqlen_k, page_size=0):
     """The split count fwd_splitkv takes when none is given: the decode rule
-    when the library runs the decode kernel (one query row per sequence, head
-    dim 64 or 128, packed or pages of at least 64 tokens, enough waves), else the
+    when the library runs the decode kernel (one query row per sequence,
+    packed or pages of at least 64 tokens, enough waves), else the
     tiled kernel's rule."""
-    if int(max_seqlen_q) == 1 and int(D) in (64, 128) and (int(page_size) == 0 or int(page_size) >= 64):
+    if int(max_seqlen_q) == 1 and int(D) in (64, 128, 256) and (int(page_size) == 0 or int(page_size) >= 64):
         splits = decode_num_splits(int(B) * int(H), max_seqlen_k)
         if int(B) * int(H) * splits >= DECODE_MIN_WAVES:
             return splits

@@ -1,8 +1,8 @@
 // Decoding forward ("Fused attention kernel" page, section "Implementation
 // sketch": a row's running max and running sum over key blocks; the
 // FlashAttention-3 page's future-work note on LLM inference): one query row
-// per sequence against a long, optionally paged key cache, at head dim 64 or
-// 128.
+// per sequence against a long, optionally paged key cache, at head dim 64,
+// 128 or 256 (its own kernel below: two lanes per key).
 //
 // With one query row the two products are matrix-vector products, so the
 // matrix cores have nothing to share and the work is bound by the bytes of K
@@ -47,8 +47,10 @@
 
 namespace attn {
 
-// buffer_load_dword into a register (zero past the resource's range)
+// buffer_load_dword / _dwordx2 into registers (zeros past the resource's range)
 __device__ int raw_buffer_load_b32(i32x4 rsrc, int voffset, int soffset, int aux) __asm("llvm.amdgcn.raw.buffer.load.i32");
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+__device__ i32x2 raw_buffer_load_v2(i32x4 rsrc, int voffset, int soffset, int aux) __asm("llvm.amdgcn.raw.buffer.load.v2i32");
 
 template <int DT>
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -192,6 +194,130 @@ __global__ void __launch_bounds__(256) decode_kernel(FwdArgs a) {
   }
 }
 
+// Head dim 256: a key's 512-byte row is split between lanes j and j + 32
+// (head-dim half `half` = lane / 32 each), so a tile holds 32 keys and a
+// score is the sum of the two halves' dot products (one half-wave swap; both
+// lanes then hold the same score).  The query's half sits in vector registers
+// (its 128 pairs would not fit the scalar ones).  V: each 512-byte key row is
+// one coalesced load of 8 bytes per lane, lane l holding columns 4l .. 4l+3.
+// Otherwise as decode_kernel: head index fastest, the next tile's K in flight
+// during the softmax and P V, the same outputs.
+template <int DT>
+__global__ void __launch_bounds__(256) decode_kernel_d256(FwdArgs a) {
+  constexpr int D = 256, BC = 32, HP = D / 4;  // HP: query / K pairs per lane half
+  const int lane = threadIdx.x & 63, key_l = lane & 31, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+  if (item >= (int64_t)a.B * a.H * a.n_split) return;  // (no barriers below)
+  const int h = (int)(item % a.H);
+  const int64_t bs = item / a.H;
+  const int split = (int)(bs % a.n_split), b = (int)(bs / a.n_split);
+  const int row = a.cu_q[b];
+  if (a.cu_q[b + 1] - row <= 0) return;
+  const int kseq = a.cu_k[b], Lk = a.cu_k[b + 1] - kseq;
+  const int kbeg = split * a.split_tiles * 64;  // (ranges are counted in 64-key tiles)
+  const int kend = a.n_split == 1 ? Lk : min(Lk, kbeg + a.split_tiles * 64);
+
+  uint32_t qv[HP];  // query pairs 64 half .. 64 half + 63
+  {
+    const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + ((int64_t)row * a.H + h) * D + (D / 2) * half);
+#pragma unroll
+    for (int c = 0; c < HP / 4; ++c) {
+      const u32x4 x = qp[c];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) qv[4 * c + w] = x[w];
+    }
+  }
+  const uint32_t row_bytes = (uint32_t)a.H * D * 2;  // <= 2^25 (H * D <= 2^24, checked by the caller)
+  const bool paged = a.block_table != nullptr;
+  auto tile_off = [&](int k0) -> int64_t {  // a tile never straddles a page (>= 64 tokens)
+    int64_t base_row;
+    if (paged) {
+      const int page = a.block_table[(int64_t)b * a.max_pages + (k0 >> a.page_shift)];
+      base_row = ((int64_t)page << a.page_shift) + (k0 & ((1 << a.page_shift) - 1));
+    } else {
+      base_row = (int64_t)kseq + k0;
+    }
+    return (base_row * a.H + h) * D;
+  };
+  auto tile_bytes = [&](int k0) -> uint32_t { return (uint32_t)(min(BC, kend - k0) - 1) * row_bytes + D * 2; };
+  const uint32_t k_lane = (uint32_t)key_l * row_bytes + (D / 2) * 2 * half;  // this lane's K half-row
+  float m = -INFINITY;
+  float l_lane = 0.f;  // (lanes of the lower half only: each key counted once)
+  float o[4] = {0.f, 0.f, 0.f, 0.f};  // head-dim columns 4 lane .. 4 lane + 3
+  uint32_t kw[HP];
+  if (kbeg < kend) {
+    const i32x4 krs = make_rsrc((const uint16_t*)a.k + tile_off(kbeg), tile_bytes(kbeg));
+#pragma unroll
+    for (int c = 0; c < HP / 4; ++c) {
+      const i32x4 x = raw_buffer_load_v4(krs, (int)(k_lane + 16 * c), 0, 0);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) kw[4 * c + w] = (uint32_t)x[w];
+    }
+  }
+  for (int k0 = kbeg; k0 < kend; k0 += BC) {
+    const int nvalid = min(BC, kend - k0);
+    const i32x4 vrs = make_rsrc((const uint16_t*)a.v + tile_off(k0), tile_bytes(k0));
+    i32x2 vw[BC];
+#pragma unroll
+    for (int j = 0; j < BC; ++j) vw[j] = raw_buffer_load_v2(vrs, (int)(j * row_bytes + 8 * lane), 0, 0);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < HP; ++i) acc[i & 3] = dot2<DT>(kw[i], qv[i], acc[i & 3]);
+    const float part = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    const float x = key_l < nvalid ? halfwave_sum(part) * a.scale_log2 : -INFINITY;
+    __builtin_amdgcn_sched_barrier(0);
+    const int k1 = k0 + BC;
+    int64_t off1 = 0;
+    uint32_t nb1 = 0;  // past the range: an empty resource, the loads return zeros
+    if (k1 < kend) {
+      off1 = tile_off(k1);
+      nb1 = tile_bytes(k1);
+    }
+    {
+      const i32x4 krs = make_rsrc((const uint16_t*)a.k + off1, nb1);
+#pragma unroll
+      for (int c = 0; c < HP / 4; ++c) {
+        const i32x4 y = raw_buffer_load_v4(krs, (int)(k_lane + 16 * c), 0, 0);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) kw[4 * c + w] = (uint32_t)y[w];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const float m_new = max2f(m, wave_max(x));
+    const float m_safe = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_safe);
+    const float p = fast_exp2(x - m_safe);
+    l_lane = fmaf(l_lane, alpha, half == 0 ? p : 0.f);
+    m = m_new;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] *= alpha;
+    const uint32_t pp = pack2<DT>(p, __shfl_xor(p, 1));  // keys 2i, 2i+1 at lane 2i
+#pragma unroll
+    for (int i = 0; i < BC / 2; ++i) {
+      const uint32_t pi = (uint32_t)__builtin_amdgcn_readlane((int)pp, 2 * i);
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const uint32_t a0 = (uint32_t)vw[2 * i][w], a1 = (uint32_t)vw[2 * i + 1][w];
+        o[2 * w] = dot2<DT>(__builtin_amdgcn_perm(a1, a0, 0x05040100u), pi, o[2 * w]);
+        o[2 * w + 1] = dot2<DT>(__builtin_amdgcn_perm(a1, a0, 0x07060302u), pi, o[2 * w + 1]);
+      }
+    }
+  }
+  const float l = wave_sum(l_lane);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float lse = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+  if (a.n_split == 1) {
+    uint16_t* op = (uint16_t*)a.o + (int64_t)row * a.o_ss + (int64_t)h * a.o_sh;
+    *(u32x2*)(op + 4 * lane) = u32x2{pack2<DT>(o[0] * inv, o[1] * inv), pack2<DT>(o[2] * inv, o[3] * inv)};
+    if (lane == 0 && a.lse != nullptr) a.lse[(int64_t)h * a.total_q + row] = lse;
+  } else {
+    const int64_t prow = (int64_t)split * a.total_q + row;
+    *(f32x4*)(a.part_o + (prow * a.H + h) * D + 4 * lane) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+    if (lane == 0) a.part_lse[(int64_t)split * a.H * a.total_q + (int64_t)h * a.total_q + row] = lse;
+  }
+}
+
 hipError_t launch_decode(const FwdArgs& a, int D, int dtype, hipStream_t s) {
   const int64_t items = (int64_t)a.B * a.H * a.n_split;
   const dim3 grid((unsigned)((items + 3) / 4)), block(256);
@@ -201,6 +327,9 @@ hipError_t launch_decode(const FwdArgs& a, int D, int dtype, hipStream_t s) {
   } else if (D == 128) {
     if (dtype == kBF16) hipLaunchKernelGGL((decode_kernel<kBF16, 128>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((decode_kernel<kFP16, 128>), grid, block, 0, s, a);
+  } else if (D == 256) {
+    if (dtype == kBF16) hipLaunchKernelGGL(decode_kernel_d256<kBF16>, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(decode_kernel_d256<kFP16>, grid, block, 0, s, a);
   } else {
     return hipErrorNotSupported;
   }

@@ -263,7 +263,8 @@ int main() {
   expect("decode_d64_plan", g_decode - d0, 1);
   d0 = g_decode;
   expect("decode_d256", attn_fwd_splitkv(ATTN_BF16, p, cu, p, p, cu, nullptr, 0, 0, p, lse, 2, 64, 256, 2, 1, 3, sc, 0, 4, work1.data(), attn_fwd_splitkv_workspace_bytes(2, 64, 256, 4), nullptr), ATTN_OK);
-  expect("decode_d256_plan", g_decode - d0 == 0 && g_fwd_mode == attn::kVarlen, 1);
+  expect("decode_d256_plan", g_decode - d0, 1);
+  d0 = g_decode;
   // one key range: the decode kernel writes the output itself (no merge)
   n = g_launches;
   expect("decode_whole_varlen", attn_fwd_varlen(ATTN_BF16, p, cu, p, p, cu, nullptr, 0, 0, p, lse, 2, 256, 128, 2, 1, 3, sc, 1, nullptr), ATTN_OK);

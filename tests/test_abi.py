@@ -299,7 +299,7 @@ def test_auto_num_splits():
     assert A.auto_num_splits(4, 32, 128, 4, 1, 32768, 0) == 8
     assert A.auto_num_splits(4, 32, 128, 4, 1, 32768, 16) == A.splitkv_num_splits(32 * 5, 32768)
     assert A.auto_num_splits(4, 32, 64, 4, 1, 32768, 0) == 8
-    assert A.auto_num_splits(4, 32, 256, 4, 1, 32768, 0) == A.splitkv_num_splits(32 * 5, 32768)
+    assert A.auto_num_splits(4, 32, 256, 4, 1, 32768, 0) == 8
     assert A.auto_num_splits(4, 32, 128, 8, 2, 32768, 0) == A.splitkv_num_splits(32 * 5, 32768)
     # too few waves for the decode kernel even split: the tiled rule
     assert A.auto_num_splits(1, 8, 128, 1, 1, 1000, 0) == A.splitkv_num_splits(8 * 2, 1000)

@@ -97,12 +97,12 @@ def test_matches_unsplit_kernel(lib):
     np.testing.assert_array_equal(l1, l2.cpu().numpy().astype(np.float64))
 
 
-# One query row per sequence at head dim 64 or 128 with at least 512 (sequence,
-# key range, head) items is the streaming decode kernel's case (packed caches, and
+# One query row per sequence with at least 512 (sequence, key range, head)
+# items is the streaming decode kernel's case (packed caches, and
 # paged caches with pages of at least 64 tokens); fewer items take the tiled
 # kernel.
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("splits", [2, 7, 64])
@@ -118,7 +118,7 @@ def test_one_row_decode_packed(lib, d, dtype, causal, splits):
     assert_close16(o, o_ref, lse, lse_ref, f"one-row decode d{d} {dtype} causal={causal} splits={splits}", dtype=dtype)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("page", [64, 256, 16])
 def test_one_row_decode_paged_poisoned(lib, d, page):
     # pages at shuffled physical slots, NaN in every slot no sequence owns
@@ -141,7 +141,7 @@ def test_one_row_decode_large_scores(lib):
     assert_close16(o, o_ref, lse, lse_ref, "one-row decode, large scores")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("paged", [False, True])
 def test_one_row_whole_sequence(lib, d, paged):
     # one key range (attn_fwd_varlen, and attn_fwd_splitkv with one split): the
