@@ -72,6 +72,43 @@ __device__ __forceinline__ float wave_sum(float x) {
   return halfwave_sum(x);
 }
 
+// A wave's work item: (sequence b, key range `split`, head h), head index
+// fastest, and what both decode kernels derive from it.
+struct DecodeItem {
+  int b, h, split, row;  // row: the sequence's query row in the packed q / o
+  int kseq, kbeg, kend;  // first key row of a packed cache; key range [kbeg, kend)
+};
+// False when the item is past the grid or its sequence has no query row.
+// Ranges are split_tiles 64-key tiles long; one range takes every key.
+__device__ __forceinline__ bool decode_item(const FwdArgs& a, DecodeItem& it) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+  if (item >= (int64_t)a.B * a.H * a.n_split) return false;
+  it.h = (int)(item % a.H);
+  const int64_t bs = item / a.H;
+  it.split = (int)(bs % a.n_split);
+  it.b = (int)(bs / a.n_split);
+  it.row = a.cu_q[it.b];
+  if (a.cu_q[it.b + 1] - it.row <= 0) return false;
+  it.kseq = a.cu_k[it.b];
+  const int Lk = a.cu_k[it.b + 1] - it.kseq;
+  it.kbeg = it.split * a.split_tiles * 64;
+  it.kend = a.n_split == 1 ? Lk : min(Lk, it.kbeg + a.split_tiles * 64);
+  return true;
+}
+// Element offset of key k0's (b, h) slice of a [rows, H, D] cache (paged:
+// through the block table; a tile starting at k0 never straddles a page).
+__device__ __forceinline__ int64_t decode_tile_off(const FwdArgs& a, const DecodeItem& it, int D, int k0) {
+  int64_t base_row;
+  if (a.block_table != nullptr) {
+    const int page = a.block_table[(int64_t)it.b * a.max_pages + (k0 >> a.page_shift)];
+    base_row = ((int64_t)page << a.page_shift) + (k0 & ((1 << a.page_shift) - 1));
+  } else {
+    base_row = (int64_t)it.kseq + k0;
+  }
+  return (base_row * a.H + it.h) * D;
+}
+
 // FwdArgs of the packed or paged varlen forward: every sequence with at most
 // one query row, head dim D, paged caches with pages of at least 64 tokens
 // (a 64-key tile never straddles a page); n_split >= 1 key ranges of
@@ -82,19 +119,11 @@ __global__ void __launch_bounds__(256) decode_kernel(FwdArgs a) {
   constexpr int BC = 64;
   constexpr int NCOL = D / 2;  // lanes that own a head-dim column pair
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t item = (int64_t)blockIdx.x * 4 + wave;
-  if (item >= (int64_t)a.B * a.H * a.n_split) return;  // (no barriers below)
-  const int h = (int)(item % a.H);
-  const int64_t bs = item / a.H;
-  const int split = (int)(bs % a.n_split), b = (int)(bs / a.n_split);
-  const int row = a.cu_q[b];
-  if (a.cu_q[b + 1] - row <= 0) return;
-  const int kseq = a.cu_k[b], Lk = a.cu_k[b + 1] - kseq;
-  const int kbeg = split * a.split_tiles * BC;
-  const int kend = a.n_split == 1 ? Lk : min(Lk, kbeg + a.split_tiles * BC);
+  DecodeItem it;
+  if (!decode_item(a, it)) return;  // (no barriers below)
+  const int h = it.h, split = it.split, row = it.row, kbeg = it.kbeg, kend = it.kend;
 
-  // the query's 64 pairs, in scalar registers (read through the constant
+  // the query's D/2 pairs, in scalar registers (read through the constant
   // address space: a uniform address the kernel never writes)
   typedef const __attribute__((address_space(4))) uint32_t cu32;
   cu32* qp = (cu32*)((const uint16_t*)a.q + ((int64_t)row * a.H + h) * D);
@@ -103,18 +132,7 @@ __global__ void __launch_bounds__(256) decode_kernel(FwdArgs a) {
   for (int i = 0; i < D / 2; ++i) qw[i] = qp[i];
 
   const uint32_t row_bytes = (uint32_t)a.H * D * 2;  // <= 2^25 (H * D <= 2^24, checked by the caller)
-  const bool paged = a.block_table != nullptr;
-  // element offset of key k0's (b, h) slice: a tile never straddles a page
-  auto tile_off = [&](int k0) -> int64_t {
-    int64_t base_row;
-    if (paged) {
-      const int page = a.block_table[(int64_t)b * a.max_pages + (k0 >> a.page_shift)];
-      base_row = ((int64_t)page << a.page_shift) + (k0 & ((1 << a.page_shift) - 1));
-    } else {
-      base_row = (int64_t)kseq + k0;
-    }
-    return (base_row * a.H + h) * D;
-  };
+  auto tile_off = [&](int k0) { return decode_tile_off(a, it, D, k0); };
   auto tile_bytes = [&](int k0) -> uint32_t { return (uint32_t)(min(BC, kend - k0) - 1) * row_bytes + D * 2; };
   float m = -INFINITY;       // running max (uniform over the wave)
   float l_lane = 0.f;        // this lane's share of the row sum
@@ -206,17 +224,9 @@ template <int DT>
 __global__ void __launch_bounds__(256) decode_kernel_d256(FwdArgs a) {
   constexpr int D = 256, BC = 32, HP = D / 4;  // HP: query / K pairs per lane half
   const int lane = threadIdx.x & 63, key_l = lane & 31, half = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t item = (int64_t)blockIdx.x * 4 + wave;
-  if (item >= (int64_t)a.B * a.H * a.n_split) return;  // (no barriers below)
-  const int h = (int)(item % a.H);
-  const int64_t bs = item / a.H;
-  const int split = (int)(bs % a.n_split), b = (int)(bs / a.n_split);
-  const int row = a.cu_q[b];
-  if (a.cu_q[b + 1] - row <= 0) return;
-  const int kseq = a.cu_k[b], Lk = a.cu_k[b + 1] - kseq;
-  const int kbeg = split * a.split_tiles * 64;  // (ranges are counted in 64-key tiles)
-  const int kend = a.n_split == 1 ? Lk : min(Lk, kbeg + a.split_tiles * 64);
+  DecodeItem it;
+  if (!decode_item(a, it)) return;  // (no barriers below)
+  const int h = it.h, split = it.split, row = it.row, kbeg = it.kbeg, kend = it.kend;
 
   uint32_t qv[HP];  // query pairs 64 half .. 64 half + 63
   {
@@ -229,17 +239,7 @@ __global__ void __launch_bounds__(256) decode_kernel_d256(FwdArgs a) {
     }
   }
   const uint32_t row_bytes = (uint32_t)a.H * D * 2;  // <= 2^25 (H * D <= 2^24, checked by the caller)
-  const bool paged = a.block_table != nullptr;
-  auto tile_off = [&](int k0) -> int64_t {  // a tile never straddles a page (>= 64 tokens)
-    int64_t base_row;
-    if (paged) {
-      const int page = a.block_table[(int64_t)b * a.max_pages + (k0 >> a.page_shift)];
-      base_row = ((int64_t)page << a.page_shift) + (k0 & ((1 << a.page_shift) - 1));
-    } else {
-      base_row = (int64_t)kseq + k0;
-    }
-    return (base_row * a.H + h) * D;
-  };
+  auto tile_off = [&](int k0) { return decode_tile_off(a, it, D, k0); };
   auto tile_bytes = [&](int k0) -> uint32_t { return (uint32_t)(min(BC, kend - k0) - 1) * row_bytes + D * 2; };
   const uint32_t k_lane = (uint32_t)key_l * row_bytes + (D / 2) * 2 * half;  // this lane's K half-row
   float m = -INFINITY;
