@@ -431,7 +431,7 @@ def bench_points(A, W, args):
     the d128 seq-8k headline point of the 16384-token sweep (batch 2, 16
     heads, non-causal), the seq-512 d128 points in GB/s (HBM-bound), the
     varlen + paged workload (packed and with 64-token pages), and the 8-bit
-    kernel under a causal mask."""
+    kernel under a causal mask and on the seq-512 shape."""
     import torch
     steps = max(5, args.steps // 3)
     out = {}
@@ -455,6 +455,7 @@ def bench_points(A, W, args):
         del q, k, v, o
     out["varlen_paged"] = bench_varlen(A, W, steps)
     out["fp8_causal"] = bench_fp8_causal(A, W, steps)
+    out["fp8_s512"] = bench_fp8_short(A, W, pts["sweep_s512_d128_full"], steps)
     return out
 
 
@@ -548,6 +549,36 @@ def bench_fp8_causal(A, W, steps):
     print(f"[bench] fp8 causal: {ms:.3f} ms {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
     return {"workload": w.name + "_causal", "ms": round(ms, 4), "tflops": round(tf, 1),
             "pct_of_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2)}
+
+
+def bench_fp8_short(A, W, w, steps):
+    """The 8-bit kernel (block-128 scales, rotated Q and K) on a short-sequence
+    shape of the sweep, non-causal and causal, inputs drawn like the 8-bit
+    workload's (0.1 % outliers); beside it the 16-bit kernel on the same
+    shape is in the sweep point of that name."""
+    import torch
+    qs, _ = w.shapes()
+    qh, kh, vh = W.qkv_outlier(w.seed, qs)
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in (qh, kh, vh))
+    signs = torch.from_numpy(W.random_signs(4, w.head_dim)).cuda()
+    q8, qsc = A.fp8_quantize(q, 128, signs)
+    k8, ksc = A.fp8_quantize(k, 128, signs)
+    v8, vsc = A.fp8_quantize(v, 128, None)
+    del q, k, v
+    o = torch.empty((w.batch, w.seq_q, w.heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.batch, w.heads, w.seq_q), dtype=torch.float32, device="cuda")
+    res = {"batch": w.batch, "heads": w.heads, "seq": w.seq_q, "head_dim": w.head_dim}
+    for causal in (False, True):
+        ms = time_launches(lambda: A.fwd_fp8(q8, qsc, k8, ksc, v8, vsc, 128, w.scale, causal, out=o, lse=lse),
+                           steps, 10)
+        tf = w.flops / (2 if causal else 1) / (ms * 1e-3) / 1e12
+        key = "_causal" if causal else ""
+        res["ms" + key] = round(ms, 4)
+        res["tflops" + key] = round(tf, 1)
+        res["pct_of_peak" + key] = round(100 * tf / PEAK_FP8_TFLOPS, 2)
+        print(f"[bench] fp8 seq {w.seq_q}{' causal' if causal else ''}: {ms:.4f} ms {tf:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
+    return res
 
 
 def measured_ceilings(result):
