@@ -110,13 +110,21 @@ __device__ __forceinline__ int64_t decode_tile_off(const FwdArgs& a, const Decod
 }
 
 // FwdArgs of the packed or paged varlen forward: every sequence with at most
-// one query row, head dim D, paged caches with pages of at least 64 tokens
-// (a 64-key tile never straddles a page); n_split >= 1 key ranges of
-// split_tiles tiles (part_o / part_lse when n_split > 1).
-template <int DT, int D>
+// one query row, head dim D; n_split >= 1 key ranges of split_tiles tiles
+// (part_o / part_lse when n_split > 1).  PS = 0: a packed cache or pages of at
+// least 64 tokens (a 64-key tile lies in one page: buffer loads whose resource
+// ends at the range's last key).  PS = 4 or 5: pages of 2^PS tokens; a tile
+// spans 64 >> PS pages, whose table entries it reads once (as scalars), and
+// every K and V row is addressed through its page.  Keys of the last tile past
+// the range then read the range's last row again (their scores are masked),
+// and the prefetch past the range reads the current tile again (from L2), so
+// no address leaves the range's pages.
+template <int DT, int D, int PS>
 __global__ void __launch_bounds__(256) decode_kernel(FwdArgs a) {
   static_assert(D == 64 || D == 128, "head dims of the decode kernel");
+  static_assert(PS == 0 || PS == 4 || PS == 5, "small pages of 16 or 32 tokens");
   constexpr int BC = 64;
+  constexpr int NPG = PS > 0 ? BC >> PS : 1;  // pages per tile
   constexpr int NCOL = D / 2;  // lanes that own a head-dim column pair
   const int lane = threadIdx.x & 63;
   DecodeItem it;
@@ -138,8 +146,36 @@ __global__ void __launch_bounds__(256) decode_kernel(FwdArgs a) {
   float l_lane = 0.f;        // this lane's share of the row sum
   float o0 = 0.f, o1 = 0.f;  // head-dim columns 2 col and 2 col + 1
   const int col = lane % NCOL;
+  // small pages: the first cache row of each page of the tile at k0 (entries
+  // clamped to the range's last page), and the element offset of a row slice
+  typedef const __attribute__((address_space(4))) int32_t cint32;
+  auto tile_pages = [&](int k0, int64_t (&pg)[NPG]) {
+    const int nvalid = min(BC, kend - k0);
+    cint32* tab = (cint32*)a.block_table + (int64_t)it.b * a.max_pages + (k0 >> PS);
+#pragma unroll
+    for (int g = 0; g < NPG; ++g) pg[g] = (int64_t)tab[min(g, (nvalid - 1) >> PS)] << PS;
+  };
+  auto row_slice = [&](int64_t cache_row) { return (cache_row * a.H + h) * D; };
   uint32_t kw[D / 2];  // K row of key `lane` of the current tile
-  if (kbeg < kend) {
+  // K rows of the tile at k0 (< kend) into kw
+  auto load_k_small = [&](int k0) {
+    int64_t pg[NPG];
+    tile_pages(k0, pg);
+    const int jj = min(lane, kend - k0 - 1);  // (keys past the range: the last row again)
+    int64_t base = pg[0];
+#pragma unroll
+    for (int g = 1; g < NPG; ++g) base = (jj >> PS) == g ? pg[g] : base;
+    const u32x4* kp = (const u32x4*)((const uint16_t*)a.k + row_slice(base + (jj & ((1 << PS) - 1))));
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+      const u32x4 x = kp[c];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) kw[4 * c + w] = x[w];
+    }
+  };
+  if constexpr (PS > 0) {
+    if (kbeg < kend) load_k_small(kbeg);
+  } else if (kbeg < kend) {
     const i32x4 krs = make_rsrc((const uint16_t*)a.k + tile_off(kbeg), tile_bytes(kbeg));
 #pragma unroll
     for (int c = 0; c < D / 8; ++c) {
@@ -150,10 +186,21 @@ __global__ void __launch_bounds__(256) decode_kernel(FwdArgs a) {
   }
   for (int k0 = kbeg; k0 < kend; k0 += BC) {
     const int nvalid = min(BC, kend - k0);
-    const i32x4 vrs = make_rsrc((const uint16_t*)a.v + tile_off(k0), tile_bytes(k0));
     uint32_t vw[BC];  // V column pair `lane` of every key of the tile
+    if constexpr (PS > 0) {
+      int64_t pg[NPG];
+      tile_pages(k0, pg);
 #pragma unroll
-    for (int j = 0; j < BC; ++j) vw[j] = (uint32_t)raw_buffer_load_b32(vrs, (int)(j * row_bytes + 4 * col), 0, 0);
+      for (int j = 0; j < BC; ++j) {
+        const int jj = min(j, nvalid - 1);  // (uniform)
+        const uint32_t* vp = (const uint32_t*)((const uint16_t*)a.v + row_slice(pg[jj >> PS] + (jj & ((1 << PS) - 1))));
+        vw[j] = vp[col];
+      }
+    } else {
+      const i32x4 vrs = make_rsrc((const uint16_t*)a.v + tile_off(k0), tile_bytes(k0));
+#pragma unroll
+      for (int j = 0; j < BC; ++j) vw[j] = (uint32_t)raw_buffer_load_b32(vrs, (int)(j * row_bytes + 4 * col), 0, 0);
+    }
     // score of key `lane`
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -163,13 +210,15 @@ __global__ void __launch_bounds__(256) decode_kernel(FwdArgs a) {
     // (kept after the scores, and before the softmax, by the fences)
     __builtin_amdgcn_sched_barrier(0);
     const int k1 = k0 + BC;
-    int64_t off1 = 0;
-    uint32_t nb1 = 0;  // past the range: an empty resource, the loads return zeros
-    if (k1 < kend) {
-      off1 = tile_off(k1);
-      nb1 = tile_bytes(k1);
-    }
-    {
+    if constexpr (PS > 0) {
+      load_k_small(k1 < kend ? k1 : k0);  // (past the range: this tile again, from L2)
+    } else {
+      int64_t off1 = 0;
+      uint32_t nb1 = 0;  // past the range: an empty resource, the loads return zeros
+      if (k1 < kend) {
+        off1 = tile_off(k1);
+        nb1 = tile_bytes(k1);
+      }
       const i32x4 krs = make_rsrc((const uint16_t*)a.k + off1, nb1);
 #pragma unroll
       for (int c = 0; c < D / 8; ++c) {
@@ -321,13 +370,18 @@ __global__ void __launch_bounds__(256) decode_kernel_d256(FwdArgs a) {
 hipError_t launch_decode(const FwdArgs& a, int D, int dtype, hipStream_t s) {
   const int64_t items = (int64_t)a.B * a.H * a.n_split;
   const dim3 grid((unsigned)((items + 3) / 4)), block(256);
+  // small pages (a paged cache with pages of 16 or 32 tokens) at head dims 64 and 128
+  const int ps = a.block_table != nullptr && a.page_shift < 6 ? a.page_shift : 0;
+  if (ps != 0 && ps != 4 && ps != 5) return hipErrorNotSupported;
+  auto go = [&](auto k) { hipLaunchKernelGGL(k, grid, block, 0, s, a); };
   if (D == 64) {
-    if (dtype == kBF16) hipLaunchKernelGGL((decode_kernel<kBF16, 64>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((decode_kernel<kFP16, 64>), grid, block, 0, s, a);
+    if (dtype == kBF16) ps == 0 ? go(decode_kernel<kBF16, 64, 0>) : ps == 4 ? go(decode_kernel<kBF16, 64, 4>) : go(decode_kernel<kBF16, 64, 5>);
+    else ps == 0 ? go(decode_kernel<kFP16, 64, 0>) : ps == 4 ? go(decode_kernel<kFP16, 64, 4>) : go(decode_kernel<kFP16, 64, 5>);
   } else if (D == 128) {
-    if (dtype == kBF16) hipLaunchKernelGGL((decode_kernel<kBF16, 128>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((decode_kernel<kFP16, 128>), grid, block, 0, s, a);
+    if (dtype == kBF16) ps == 0 ? go(decode_kernel<kBF16, 128, 0>) : ps == 4 ? go(decode_kernel<kBF16, 128, 4>) : go(decode_kernel<kBF16, 128, 5>);
+    else ps == 0 ? go(decode_kernel<kFP16, 128, 0>) : ps == 4 ? go(decode_kernel<kFP16, 128, 4>) : go(decode_kernel<kFP16, 128, 5>);
   } else if (D == 256) {
+    if (ps != 0) return hipErrorNotSupported;
     if (dtype == kBF16) hipLaunchKernelGGL(decode_kernel_d256<kBF16>, grid, block, 0, s, a);
     else hipLaunchKernelGGL(decode_kernel_d256<kFP16>, grid, block, 0, s, a);
   } else {

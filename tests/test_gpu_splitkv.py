@@ -98,9 +98,9 @@ def test_matches_unsplit_kernel(lib):
 
 
 # One query row per sequence with at least 512 (sequence, key range, head)
-# items is the streaming decode kernel's case (packed caches, and
-# paged caches with pages of at least 64 tokens); fewer items take the tiled
-# kernel.
+# items is the streaming decode kernel's case (packed caches, paged caches with
+# pages of at least 64 tokens, and at head dims 64 and 128 pages of 16 or 32
+# tokens); fewer items take the tiled kernel.
 
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
@@ -119,10 +119,11 @@ def test_one_row_decode_packed(lib, d, dtype, causal, splits):
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
-@pytest.mark.parametrize("page", [64, 256, 16])
+@pytest.mark.parametrize("page", [64, 256, 16, 32])
 def test_one_row_decode_paged_poisoned(lib, d, page):
     # pages at shuffled physical slots, NaN in every slot no sequence owns
-    # (16-token pages take the tiled kernel, row by row through the table)
+    # (16- and 32-token pages: every row through the table; at head dim 256
+    # they take the tiled kernel)
     lens_q, lens_k = [1, 1, 1, 1], [5000, 130, 64, 2500]
     q, k, v, cu_q, cu_k = _pack(lens_q, lens_k, 16, d, seed=960 + page + d)
     kp, vp, table = _paginate(k, v, cu_k, lens_k, page, seed=961)
@@ -142,8 +143,8 @@ def test_one_row_decode_large_scores(lib):
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
-@pytest.mark.parametrize("paged", [False, True])
-def test_one_row_whole_sequence(lib, d, paged):
+@pytest.mark.parametrize("page", [0, 128, 16])
+def test_one_row_whole_sequence(lib, d, page):
     # one key range (attn_fwd_varlen, and attn_fwd_splitkv with one split): the
     # decode kernel writes the output and the logsumexp itself; 8 x 64 heads
     import torch
@@ -151,16 +152,16 @@ def test_one_row_whole_sequence(lib, d, paged):
     q, k, v, cu_q, cu_k = _pack(lens_q, lens_k, 64, d, seed=980 + d)
     table = None
     kk, vv = k, v
-    if paged:
-        kk, vv, table = _paginate(k, v, cu_k, lens_k, 128, seed=981)
+    if page:
+        kk, vv, table = _paginate(k, v, cu_k, lens_k, page, seed=981)
     tq, tk, tv = to_dev(q), to_dev(kk), to_dev(vv)
     tab = None if table is None else _t32(table)
     o1, l1 = lib.fwd_varlen(tq, _t32(cu_q), tk, tv, _t32(cu_k), 1, max(lens_k), causal=True, block_table=tab,
-                            page_size=128 if paged else 0)
+                            page_size=page)
     o2, l2 = lib.fwd_splitkv(tq, _t32(cu_q), tk, tv, _t32(cu_k), 1, max(lens_k), causal=True, block_table=tab,
-                             page_size=128 if paged else 0, num_splits=1)
+                             page_size=page, num_splits=1)
     torch.cuda.synchronize()
     o_ref, lse_ref = _reference(q, k, v, cu_q, cu_k, lens_q, lens_k, True)
-    assert_close16(to_host(o1), o_ref, l1.cpu().numpy().astype(np.float64), lse_ref, f"one-row whole paged={paged}")
+    assert_close16(to_host(o1), o_ref, l1.cpu().numpy().astype(np.float64), lse_ref, f"one-row whole d{d} page={page}")
     np.testing.assert_array_equal(to_host(o1), to_host(o2))
     np.testing.assert_array_equal(l1.cpu().numpy(), l2.cpu().numpy())
