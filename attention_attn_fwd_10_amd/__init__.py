@@ -488,11 +488,10 @@ DECODE_MIN_WAVES = 512  # fewest (sequence, key range, head) items the library r
 
 def auto_num_splits(B, H, D, total_q, max_seqlen_q, max_seqlen_k, page_size=0):
     """The split count fwd_splitkv takes when none is given: the decode rule
-    when the library runs the decode kernel (one query row per sequence,
-    packed, or pages of at least 64 tokens, or of 16 or 32 tokens at head dims
-    64 and 128; enough waves), else the
+    when the library runs the decode kernel (one query row per sequence, a
+    packed or paged cache, enough waves), else the
     tiled kernel's rule."""
-    if int(max_seqlen_q) == 1 and int(D) in (64, 128, 256) and (int(page_size) == 0 or int(page_size) >= 64 or int(D) <= 128):
+    if int(max_seqlen_q) == 1 and int(D) in (64, 128, 256):
         splits = decode_num_splits(int(B) * int(H), max_seqlen_k)
         if int(B) * int(H) * splits >= DECODE_MIN_WAVES:
             return splits

@@ -356,14 +356,12 @@ attn_status_t attn_fwd_bias(int dtype, const void* q, const int64_t q_strides[3]
 
 namespace {
 
-// One query row per sequence (any head dim; pages of 16 or 32 tokens at head
-// dims 64 and 128, of at least 64 at any), and at least kDecodeMinWaves
-// (sequence, key range, head) items:
+// One query row per sequence (any head dim, a packed cache or pages of any
+// size), and at least kDecodeMinWaves (sequence, key range, head) items:
 // the streaming decode kernel takes it (a causal mask keeps every key of a
 // one-row sequence, so it needs no mask).
 bool use_decode(const attn::FwdArgs& a, int D, int mode, int n_split) {
-  return a.Sq == 1 && (D == 64 || D == 128 || D == 256) &&
-         (mode == attn::kVarlen || (mode == attn::kPaged && (a.page_shift >= 6 || D <= 128))) &&
+  return a.Sq == 1 && (D == 64 || D == 128 || D == 256) && (mode == attn::kVarlen || mode == attn::kPaged) &&
          (int64_t)a.B * a.H * n_split >= kDecodeMinWaves;
 }
 

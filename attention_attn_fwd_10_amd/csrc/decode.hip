@@ -108,6 +108,18 @@ __device__ __forceinline__ int64_t decode_tile_off(const FwdArgs& a, const Decod
   }
   return (base_row * a.H + it.h) * D;
 }
+// Pages of 2^PS tokens (PS = 4 or 5): the first cache row of each of the NPG
+// pages of the tile at k0 with nvalid keys in the range; the table entries
+// are read as scalars and clamped to the range's last page, so no entry past
+// the keys the range owns is read.
+template <int PS, int NPG>
+__device__ __forceinline__ void decode_tile_pages(const FwdArgs& a, const DecodeItem& it, int k0, int nvalid,
+                                                  int64_t (&pg)[NPG]) {
+  typedef const __attribute__((address_space(4))) int32_t cint32;
+  cint32* tab = (cint32*)a.block_table + (int64_t)it.b * a.max_pages + (k0 >> PS);
+#pragma unroll
+  for (int g = 0; g < NPG; ++g) pg[g] = (int64_t)tab[min(g, (nvalid - 1) >> PS)] << PS;
+}
 
 // FwdArgs of the packed or paged varlen forward: every sequence with at most
 // one query row, head dim D; n_split >= 1 key ranges of split_tiles tiles
@@ -146,15 +158,9 @@ __global__ void __launch_bounds__(256) decode_kernel(FwdArgs a) {
   float l_lane = 0.f;        // this lane's share of the row sum
   float o0 = 0.f, o1 = 0.f;  // head-dim columns 2 col and 2 col + 1
   const int col = lane % NCOL;
-  // small pages: the first cache row of each page of the tile at k0 (entries
-  // clamped to the range's last page), and the element offset of a row slice
-  typedef const __attribute__((address_space(4))) int32_t cint32;
-  auto tile_pages = [&](int k0, int64_t (&pg)[NPG]) {
-    const int nvalid = min(BC, kend - k0);
-    cint32* tab = (cint32*)a.block_table + (int64_t)it.b * a.max_pages + (k0 >> PS);
-#pragma unroll
-    for (int g = 0; g < NPG; ++g) pg[g] = (int64_t)tab[min(g, (nvalid - 1) >> PS)] << PS;
-  };
+  // small pages: the first cache row of each page of the tile at k0, and the
+  // element offset of a row slice
+  auto tile_pages = [&](int k0, int64_t (&pg)[NPG]) { decode_tile_pages<PS>(a, it, k0, min(BC, kend - k0), pg); };
   auto row_slice = [&](int64_t cache_row) { return (cache_row * a.H + h) * D; };
   uint32_t kw[D / 2];  // K row of key `lane` of the current tile
   // K rows of the tile at k0 (< kend) into kw
@@ -268,10 +274,15 @@ __global__ void __launch_bounds__(256) decode_kernel(FwdArgs a) {
 // (its 128 pairs would not fit the scalar ones).  V: each 512-byte key row is
 // one coalesced load of 8 bytes per lane, lane l holding columns 4l .. 4l+3.
 // Otherwise as decode_kernel: head index fastest, the next tile's K in flight
-// during the softmax and P V, the same outputs.
-template <int DT>
+// during the softmax and P V, the same outputs, and the same two addressing
+// forms (PS = 0: buffer loads over a tile inside one page; PS = 4 or 5: pages
+// of 16 or 32 tokens, every row through its page, keys past the range on the
+// range's last row).
+template <int DT, int PS>
 __global__ void __launch_bounds__(256) decode_kernel_d256(FwdArgs a) {
+  static_assert(PS == 0 || PS == 4 || PS == 5, "small pages of 16 or 32 tokens");
   constexpr int D = 256, BC = 32, HP = D / 4;  // HP: query / K pairs per lane half
+  constexpr int NPG = PS > 0 ? BC >> PS : 1;   // pages per tile
   const int lane = threadIdx.x & 63, key_l = lane & 31, half = lane >> 5;
   DecodeItem it;
   if (!decode_item(a, it)) return;  // (no barriers below)
@@ -295,7 +306,27 @@ __global__ void __launch_bounds__(256) decode_kernel_d256(FwdArgs a) {
   float l_lane = 0.f;  // (lanes of the lower half only: each key counted once)
   float o[4] = {0.f, 0.f, 0.f, 0.f};  // head-dim columns 4 lane .. 4 lane + 3
   uint32_t kw[HP];
-  if (kbeg < kend) {
+  auto tile_pages = [&](int k0, int64_t (&pg)[NPG]) { decode_tile_pages<PS>(a, it, k0, min(BC, kend - k0), pg); };
+  auto row_slice = [&](int64_t cache_row) { return (cache_row * a.H + h) * D; };
+  // small pages: this lane's K half-row of the tile at k0 (< kend)
+  auto load_k_small = [&](int k0) {
+    int64_t pg[NPG];
+    tile_pages(k0, pg);
+    const int jj = min(key_l, kend - k0 - 1);  // (keys past the range: the last row again)
+    int64_t base = pg[0];
+#pragma unroll
+    for (int g = 1; g < NPG; ++g) base = (jj >> PS) == g ? pg[g] : base;
+    const u32x4* kp = (const u32x4*)((const uint16_t*)a.k + row_slice(base + (jj & ((1 << PS) - 1))) + (D / 2) * half);
+#pragma unroll
+    for (int c = 0; c < HP / 4; ++c) {
+      const u32x4 x = kp[c];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) kw[4 * c + w] = x[w];
+    }
+  };
+  if constexpr (PS > 0) {
+    if (kbeg < kend) load_k_small(kbeg);
+  } else if (kbeg < kend) {
     const i32x4 krs = make_rsrc((const uint16_t*)a.k + tile_off(kbeg), tile_bytes(kbeg));
 #pragma unroll
     for (int c = 0; c < HP / 4; ++c) {
@@ -306,10 +337,21 @@ __global__ void __launch_bounds__(256) decode_kernel_d256(FwdArgs a) {
   }
   for (int k0 = kbeg; k0 < kend; k0 += BC) {
     const int nvalid = min(BC, kend - k0);
-    const i32x4 vrs = make_rsrc((const uint16_t*)a.v + tile_off(k0), tile_bytes(k0));
     i32x2 vw[BC];
+    if constexpr (PS > 0) {
+      int64_t pg[NPG];
+      tile_pages(k0, pg);
 #pragma unroll
-    for (int j = 0; j < BC; ++j) vw[j] = raw_buffer_load_v2(vrs, (int)(j * row_bytes + 8 * lane), 0, 0);
+      for (int j = 0; j < BC; ++j) {
+        const int jj = min(j, nvalid - 1);  // (uniform)
+        const i32x2* vp = (const i32x2*)((const uint16_t*)a.v + row_slice(pg[jj >> PS] + (jj & ((1 << PS) - 1))));
+        vw[j] = vp[lane];
+      }
+    } else {
+      const i32x4 vrs = make_rsrc((const uint16_t*)a.v + tile_off(k0), tile_bytes(k0));
+#pragma unroll
+      for (int j = 0; j < BC; ++j) vw[j] = raw_buffer_load_v2(vrs, (int)(j * row_bytes + 8 * lane), 0, 0);
+    }
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < HP; ++i) acc[i & 3] = dot2<DT>(kw[i], qv[i], acc[i & 3]);
@@ -317,13 +359,15 @@ __global__ void __launch_bounds__(256) decode_kernel_d256(FwdArgs a) {
     const float x = key_l < nvalid ? halfwave_sum(part) * a.scale_log2 : -INFINITY;
     __builtin_amdgcn_sched_barrier(0);
     const int k1 = k0 + BC;
-    int64_t off1 = 0;
-    uint32_t nb1 = 0;  // past the range: an empty resource, the loads return zeros
-    if (k1 < kend) {
-      off1 = tile_off(k1);
-      nb1 = tile_bytes(k1);
-    }
-    {
+    if constexpr (PS > 0) {
+      load_k_small(k1 < kend ? k1 : k0);  // (past the range: this tile again, from L2)
+    } else {
+      int64_t off1 = 0;
+      uint32_t nb1 = 0;  // past the range: an empty resource, the loads return zeros
+      if (k1 < kend) {
+        off1 = tile_off(k1);
+        nb1 = tile_bytes(k1);
+      }
       const i32x4 krs = make_rsrc((const uint16_t*)a.k + off1, nb1);
 #pragma unroll
       for (int c = 0; c < HP / 4; ++c) {
@@ -370,7 +414,7 @@ __global__ void __launch_bounds__(256) decode_kernel_d256(FwdArgs a) {
 hipError_t launch_decode(const FwdArgs& a, int D, int dtype, hipStream_t s) {
   const int64_t items = (int64_t)a.B * a.H * a.n_split;
   const dim3 grid((unsigned)((items + 3) / 4)), block(256);
-  // small pages (a paged cache with pages of 16 or 32 tokens) at head dims 64 and 128
+  // small pages (a paged cache with pages of 16 or 32 tokens)
   const int ps = a.block_table != nullptr && a.page_shift < 6 ? a.page_shift : 0;
   if (ps != 0 && ps != 4 && ps != 5) return hipErrorNotSupported;
   auto go = [&](auto k) { hipLaunchKernelGGL(k, grid, block, 0, s, a); };
@@ -381,9 +425,8 @@ hipError_t launch_decode(const FwdArgs& a, int D, int dtype, hipStream_t s) {
     if (dtype == kBF16) ps == 0 ? go(decode_kernel<kBF16, 128, 0>) : ps == 4 ? go(decode_kernel<kBF16, 128, 4>) : go(decode_kernel<kBF16, 128, 5>);
     else ps == 0 ? go(decode_kernel<kFP16, 128, 0>) : ps == 4 ? go(decode_kernel<kFP16, 128, 4>) : go(decode_kernel<kFP16, 128, 5>);
   } else if (D == 256) {
-    if (ps != 0) return hipErrorNotSupported;
-    if (dtype == kBF16) hipLaunchKernelGGL(decode_kernel_d256<kBF16>, grid, block, 0, s, a);
-    else hipLaunchKernelGGL(decode_kernel_d256<kFP16>, grid, block, 0, s, a);
+    if (dtype == kBF16) ps == 0 ? go(decode_kernel_d256<kBF16, 0>) : ps == 4 ? go(decode_kernel_d256<kBF16, 4>) : go(decode_kernel_d256<kBF16, 5>);
+    else ps == 0 ? go(decode_kernel_d256<kFP16, 0>) : ps == 4 ? go(decode_kernel_d256<kFP16, 4>) : go(decode_kernel_d256<kFP16, 5>);
   } else {
     return hipErrorNotSupported;
   }

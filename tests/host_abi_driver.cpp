@@ -261,7 +261,8 @@ int main() {
   expect("decode_paged16_plan", g_decode - d0, 1);
   d0 = g_decode;
   expect("decode_paged16_d256", attn_fwd_splitkv(ATTN_BF16, p, cu, p, p, cu, table, 2, 16, p, lse, 2, 64, 256, 2, 1, 3, sc, 0, 4, work1.data(), attn_fwd_splitkv_workspace_bytes(2, 64, 256, 4), nullptr), ATTN_OK);
-  expect("decode_paged16_d256_plan", g_decode - d0 == 0 && g_fwd_mode == attn::kPaged, 1);
+  expect("decode_paged16_d256_plan", g_decode - d0, 1);
+  d0 = g_decode;
   expect("decode_d64", attn_fwd_splitkv(ATTN_BF16, p, cu, p, p, cu, nullptr, 0, 0, p, lse, 2, 64, 64, 2, 1, 3, sc, 0, 4, work1.data(), ws1, nullptr), ATTN_OK);
   expect("decode_d64_plan", g_decode - d0, 1);
   d0 = g_decode;

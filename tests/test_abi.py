@@ -298,7 +298,8 @@ def test_auto_num_splits():
     assert A.auto_num_splits(4, 32, 128, 4, 1, 32768, 64) == 8
     assert A.auto_num_splits(4, 32, 128, 4, 1, 32768, 0) == 8
     assert A.auto_num_splits(4, 32, 128, 4, 1, 32768, 16) == 8
-    assert A.auto_num_splits(4, 32, 256, 4, 1, 32768, 16) == A.splitkv_num_splits(32 * 5, 32768)
+    assert A.auto_num_splits(4, 32, 256, 4, 1, 32768, 16) == 8
+    assert A.auto_num_splits(4, 32, 128, 4, 1, 32768, 32) == 8
     assert A.auto_num_splits(4, 32, 64, 4, 1, 32768, 0) == 8
     assert A.auto_num_splits(4, 32, 256, 4, 1, 32768, 0) == 8
     assert A.auto_num_splits(4, 32, 128, 8, 2, 32768, 0) == A.splitkv_num_splits(32 * 5, 32768)

@@ -98,9 +98,8 @@ def test_matches_unsplit_kernel(lib):
 
 
 # One query row per sequence with at least 512 (sequence, key range, head)
-# items is the streaming decode kernel's case (packed caches, paged caches with
-# pages of at least 64 tokens, and at head dims 64 and 128 pages of 16 or 32
-# tokens); fewer items take the tiled kernel.
+# items is the streaming decode kernel's case (packed caches and paged caches
+# of any page size); fewer items take the tiled kernel.
 
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
@@ -122,8 +121,7 @@ def test_one_row_decode_packed(lib, d, dtype, causal, splits):
 @pytest.mark.parametrize("page", [64, 256, 16, 32])
 def test_one_row_decode_paged_poisoned(lib, d, page):
     # pages at shuffled physical slots, NaN in every slot no sequence owns
-    # (16- and 32-token pages: every row through the table; at head dim 256
-    # they take the tiled kernel)
+    # (16- and 32-token pages: every row through the table)
     lens_q, lens_k = [1, 1, 1, 1], [5000, 130, 64, 2500]
     q, k, v, cu_q, cu_k = _pack(lens_q, lens_k, 16, d, seed=960 + page + d)
     kp, vp, table = _paginate(k, v, cu_k, lens_k, page, seed=961)
