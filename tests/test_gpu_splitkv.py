@@ -130,6 +130,19 @@ def test_one_row_decode_paged_poisoned(lib, d, page):
     assert_close16(o, o_ref, lse, lse_ref, f"one-row paged decode d{d} page={page}")
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("page", [16, 32])
+def test_one_row_decode_small_pages_fp16(lib, d, page):
+    # fp16 through the small-page addressing, with ragged and one-key sequences
+    lens_q, lens_k = [1, 1, 1, 1], [3001, 1, 47, 1500]
+    q, k, v, cu_q, cu_k = _pack(lens_q, lens_k, 16, d, seed=990 + page + d)
+    q, k, v = (W.f16_round(x).astype(np.float32) for x in (q, k, v))
+    kp, vp, table = _paginate(k, v, cu_k, lens_k, page, seed=991)
+    o, lse = _run(lib, q, kp, vp, cu_q, cu_k, lens_q, lens_k, False, 8, table=table, page=page, dtype="fp16")
+    o_ref, lse_ref = _reference(q, k, v, cu_q, cu_k, lens_q, lens_k, False)
+    assert_close16(o, o_ref, lse, lse_ref, f"one-row fp16 decode d{d} page={page}", dtype="fp16")
+
+
 def test_one_row_decode_large_scores(lib):
     # scores far from zero: the running max moves across tiles and splits
     lens_q, lens_k = [1, 1], [3000, 777]
