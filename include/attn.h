@@ -321,6 +321,11 @@ attn_status_t attn_fwd_varlen(int dtype,
  *   a smaller workspace is an error.
  * The result is the same attention as attn_fwd_varlen up to floating-point
  * rounding (two extra fp32 roundings of the partial outputs).
+ * Decoding (max_seqlen_q == 1) with B * H * num_splits >= 512 runs a streaming
+ * kernel, one wave per (sequence, key range, head), at every head dim and page
+ * size (attn_fwd_varlen takes it too when B * H >= 512); it reads K and V near
+ * the device's streaming rate from about 1024 such items, so num_splits of
+ * about 1024 / (B * H), with ranges of at least two tiles, suits it.
  */
 attn_status_t attn_fwd_splitkv(int dtype,
                                const void* q, const int32_t* cu_seqlens_q,
